@@ -1,0 +1,202 @@
+"""Benchmark of the routed-MoE layer on one MI355X.
+
+Default workload: the decode layer (E = 512 experts, top-10, hidden 2048,
+intermediate 768, 2-bit experts + a shared expert, 1 token per step).  One
+step = one moe_layer call: router, top-k and gates, slot resolution, the
+expert FFN of the chosen experts, the shared expert and the combine.  To
+keep the weights out of the 256 MB Infinity Cache, steps cycle through
+`--layers` independent copies of the layer (48 by default, like the model's
+stack: 43.5 GB of expert weights) and through distinct tokens, so every
+step streams its experts from HBM as a real decode step does.
+
+Prints one JSON line (see the keys below).  --config c3/c4/c5 measures the
+other workloads (c3: 48-layer 4-token verify stack, step = 48 layers; c4:
+the 16-token slot-table stack; c5: prefill of 32,768 tokens through one
+layer).
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode/4-tok verify); prefill MFMA util"
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes_decode(cfg, n_experts_read, T):
+    """HBM bytes one layer must move: router weights + bias, each distinct
+    expert read once (gate, up, down planes), the shared expert, the
+    activations in and the fp32 outputs out."""
+    import synth
+    router = cfg.E * cfg.H * (2 if cfg.router_fmt == "bf16" else 4)
+    bias = cfg.E * 4 if cfg.bias != "none" else 0
+    experts = (n_experts_read + (1 if cfg.shared else 0)) * synth.expert_bytes(cfg)
+    io = T * cfg.H * 2 + T * cfg.H * 4
+    return router + bias + experts + io
+
+
+def cpu_baseline_decode(cfg, n_tokens, layers):
+    """The oracle (single-threaded fp64) on a bounded sample: n_tokens
+    decode steps, each on its own layer copy; input generation untimed."""
+    import oracle
+    import synth
+    elapsed = 0.0
+    for i in range(n_tokens):
+        layer = i % layers
+        x = synth.gen_x_rows(cfg, layer, [1000 + i])
+        W = synth.gen_router(cfg, layer)
+        bias = synth.gen_bias(cfg, layer)
+        t0 = time.perf_counter()
+        logits = oracle.router(x, W, cfg.router_fmt, bias)
+        idx, gate = oracle.topk(logits, cfg.k)
+        slot_idx, *_ = oracle.resolve(idx, gate, cfg.E, None)
+        elapsed += time.perf_counter() - t0
+        experts = {int(e): synth.gen_expert(cfg, layer, int(e)) for e in idx[0]}
+        shared = synth.gen_expert(cfg, layer, synth.SHARED_ID) if cfg.shared else None
+        t0 = time.perf_counter()
+        pair_out = np.stack([oracle.ffn(cfg.wfmt, cfg.H, cfg.I, experts[int(e)], x)[0]
+                             for e in idx[0]])
+        sh = oracle.ffn(cfg.wfmt, cfg.H, cfg.I, shared, x) if shared else None
+        oracle.combine(slot_idx, gate, pair_out, sh)
+        elapsed += time.perf_counter() - t0
+    return n_tokens / elapsed, elapsed
+
+
+def bench_decode(args, cfg_name):
+    import torch
+    import routed_expert_ffn_gemv_amd as moe
+    import synth
+    from synth import device as sdev
+
+    cfg = synth.CONFIGS[cfg_name]
+    T = cfg.T
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    L = args.layers if cfg.layers == 1 else cfg.layers
+    log(f"[bench] {cfg.name}: building {L} layer copies on the device")
+    t0 = time.time()
+    slot_of, sl, se, S = synth.slot_layout(cfg) if cfg.slots == "tiered" else (None, None, None, cfg.E)
+    global_pool = sdev.expert_pool(cfg, sl, se, dev) if cfg.slots == "tiered" else None
+    layers = []
+    ntok = max(8, (args.steps + args.warmup) // L + 1) if cfg.layers == 1 else 1
+    for l in range(L):
+        inp = sdev.layer_inputs(cfg, l, dev, x=synth.gen_x(cfg, l, T * ntok))
+        pool = global_pool if global_pool is not None else sdev.expert_pool(
+            cfg, [l] * cfg.E, list(range(cfg.E)), dev)
+        so = (torch.as_tensor(slot_of[l], device=dev) if slot_of is not None else None)
+        desc = moe.LayerDesc(cfg.E, cfg.k, cfg.H, cfg.I, inp["router_w"], cfg.router_fmt,
+                             cfg.wfmt, pool, shared=inp["shared"], router_bias=inp["bias"],
+                             slot_of_expert=so, num_slots=S)
+        layers.append((desc, inp, pool, so))
+    torch.cuda.synchronize()
+    log(f"[bench] setup {time.time() - t0:.1f}s")
+    k, H = cfg.k, cfg.H
+    ws = moe.workspace(layers[0][0], T, dev)
+    y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    gate = torch.empty((T, k), dtype=torch.float32, device=dev)
+    slot_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    miss = torch.empty((T * k * 3,), dtype=torch.int32, device=dev)
+    miss_off = torch.empty((T + 1,), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    nx = layers[0][1]["x"].shape[0] // T
+
+    def step(s):
+        """One step: one layer (c2) or the whole 48-layer stack (c3/c4)."""
+        if cfg.layers == 1:
+            desc, inp, _, _ = layers[s % L]
+            x = inp["x"][((s // L) % nx) * T:((s // L) % nx + 1) * T]
+            moe.moe_layer(desc, x, T, y, idx, gate, slot_idx, miss, miss_off, ws, stream)
+        else:
+            for desc, inp, _, _ in layers:
+                moe.moe_layer(desc, inp["x"], T, y, idx, gate, slot_idx, miss, miss_off, ws,
+                              stream)
+
+    # distinct experts read per layer call (for the algorithmic bytes)
+    uniq = []
+    for s in range(min(64, args.steps)):
+        step(s)
+        torch.cuda.synchronize()
+        sl_h = slot_idx.cpu().numpy()
+        uniq.append(len(np.unique(sl_h[sl_h >= 0])))
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for s in range(args.steps):
+        step(s)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    calls_per_step = 1 if cfg.layers == 1 else L
+    ms_call = ms / calls_per_step
+    u = float(np.mean(uniq))
+    bytes_call = algorithmic_bytes_decode(cfg, u, T)
+    gbs = bytes_call / (ms_call * 1e-3) / 1e9
+    tokens_per_s = T / (ms * 1e-3)
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "q2 weights, bf16 activations, f32 accumulation" if cfg.wfmt == "q2" else cfg.wfmt,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "E": cfg.E, "k": cfg.k, "H": cfg.H, "I": cfg.I,
+                   "T": T, "layers": L, "weights": cfg.wfmt, "shared_expert": cfg.shared,
+                   "slots": cfg.slots, "step": "one moe_layer call" if cfg.layers == 1
+                   else f"{L} moe_layer calls (one per layer)"},
+        "hbm_gbs": round(gbs, 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "moe_layer (whole call)", "bytes_per_launch": int(bytes_call),
+                     "launch_ms": round(ms_call, 5), "distinct_experts_per_layer": round(u, 2)},
+    }
+    if not args.no_cpu_baseline:
+        n = args.cpu_tokens
+        log(f"[bench] cpu baseline: oracle on {n} tokens")
+        tps, el = cpu_baseline_decode(cfg, n, L)
+        out["cpu_baseline"] = {"value": round(tps, 3), "unit": "tokens/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{n} single-token decode layers of {cfg.name} "
+                                         f"(router..combine, fp64, one thread, {el:.1f}s)"}
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--layers", type=int, default=48)
+    ap.add_argument("--cpu-tokens", type=int, default=12)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    out = bench_decode(args, args.config)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

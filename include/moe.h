@@ -1,0 +1,176 @@
+/* moe.h -- C ABI of the routed mixture-of-experts layer for MI355X (gfx950).
+ *
+ * One MoE layer of the model the Strata pages describe: per token a router
+ * GEMV over 512 experts, the 10 highest-scoring experts with softmax gate
+ * weights, a lookup of each chosen expert in a resident-expert slot table
+ * (hits are computed, misses are listed), a dequant-fused low-bit SwiGLU
+ * expert FFN and a gate-weighted combine with an always-on shared expert.
+ * Sources (page titles and sections):
+ *   [MD] ModelDock, "Strata はなぜ少ない VRAM でも速いのか" (why Strata is fast
+ *        with little VRAM): section "問題" (48 layers x 512 experts, 10 chosen
+ *        per token; the shared expert is among the weights every token uses),
+ *        section "1 トークン、三者の分担" (router on the GPU, chosen ids looked
+ *        up, resident experts run on the GPU, the GPU sums the results),
+ *        section "粗から細へ" and its placement figure (slot table of
+ *        individual resident experts, 57-109 per layer), section
+ *        "予測してから検証する" (a verify step of 1 + up to 3 draft tokens
+ *        reads each expert once), section "長いプロンプトを読む" (prefill:
+ *        thousands of tokens hit nearly every expert).
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers owned by the caller unless stated; the
+ *    library keeps none of them after the call returns.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream) and never synchronise the host.  They never allocate device
+ *    memory: scratch space is the caller's workspace `ws` of `ws_bytes`
+ *    bytes, at least moe_workspace_size() and 256-byte aligned.
+ *  - Arguments are validated on the host before any launch.  On any error
+ *    nothing is launched, nothing is written and a non-zero moe_status is
+ *    returned.  A device fault surfaces at the caller's next synchronisation.
+ *    T = 0 is a valid no-op (MOE_OK).  NaN/Inf inputs give unspecified
+ *    values (never out-of-bounds accesses).
+ *  - Row-major layouts; "K" is the contiguous (input) dimension.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID = 1,      /* bad shape, null pointer, misalignment, k > E ... */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid but not implemented (format, T too large) */
+  MOE_ERR_WORKSPACE = 3,    /* ws_bytes smaller than moe_workspace_size() */
+  MOE_ERR_DEVICE = 4        /* a HIP launch failed (hipGetLastError) */
+} moe_status;
+
+/* Weight formats.  Q2B32 / Q4B32: blocks of 32 consecutive weights along K
+ * of each row, one fp16 scale d and one fp16 min m per block, weight =
+ * d * q + m with q the unsigned 2- or 4-bit code.  The code of column c of a
+ * row sits bits*(c mod (8/bits)) bits up in byte c*bits/8 of that row (low
+ * bits first).  This is the "scale + min" low-bit block family of the
+ * quantised expert files the pages name (Q2_0 and friends); the exact 32-
+ * weight affine block is this library's definition. */
+typedef enum {
+  MOE_W_F32 = 0,   /* fp32, [rows][cols] */
+  MOE_W_BF16 = 1,  /* bf16 bits, [rows][cols] (router only) */
+  MOE_W_Q2B32 = 2, /* 2-bit codes, 3.0 bits per weight with scale and min */
+  MOE_W_Q4B32 = 3  /* 4-bit codes, 5.0 bits per weight with scale and min */
+} moe_wfmt;
+
+/* One matrix pool: `n` matrices of [rows][cols] stacked by slot.
+ *  F32:   data = float  [n][rows][cols]; scale = min = NULL.
+ *  Q2/Q4: data = codes  [n][rows*cols*bits/8] bytes (16-byte aligned);
+ *         scale, min = fp16 bits [n][rows][cols/32] (4-byte aligned). */
+typedef struct {
+  int32_t fmt;
+  const void* data;
+  const uint16_t* scale;
+  const uint16_t* min;
+} moe_mat;
+
+/* One layer.  Expert pools are indexed by SLOT: gate and up [S][I][H], down
+ * [S][H][I], all in one expert format (F32, Q2B32 or Q4B32).
+ * slot_of_expert[E] maps an expert id to its slot or -1 (not resident); NULL
+ * means every expert is resident at slot = id (then num_slots must be E).
+ * Several layers may share one pool (a global slot table).  The shared expert
+ * (sh_*) uses the same format and shapes with n = 1; sh_gate.data == NULL
+ * means the layer has none.  Router weights [E][H] are F32 or BF16;
+ * router_bias [E] fp32 may be NULL.  Limits: 1 <= k <= min(E, 32), E <= 1024,
+ * H and I multiples of 32 (of 64 for Q2B32), H <= 8192, I <= 4096,
+ * 1 <= num_slots <= 16384. */
+typedef struct {
+  int32_t E, k, H, I, num_slots;
+  int32_t router_fmt;
+  const void* router_w;
+  const float* router_bias;
+  const int32_t* slot_of_expert;
+  moe_mat gate, up, down;
+  moe_mat sh_gate, sh_up, sh_down;
+} moe_layer_desc;
+
+/* One missed (not resident) expert of one token, with its gate weight. */
+typedef struct {
+  int32_t expert;
+  int32_t token;
+  float gate;
+} moe_miss;
+
+/* Largest T accepted by moe_layer (a decode step, a 1 + 3 draft verify batch
+ * and the 16-token slot-table step all fit). */
+#define MOE_LAYER_MAX_T 16
+
+const char* moe_status_string(int32_t status);
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int32_t moe_version(void);
+
+/* Workspace bytes needed by every call below for this layer shape and T. */
+moe_status moe_workspace_size(const moe_layer_desc* desc, int32_t T, size_t* bytes);
+
+/* Router and gates ([MD] "問題", "1 トークン、三者の分担").
+ * x: bf16 bits [T][H].  logit[t][e] = sum_h x[t][h] W[e][h] + bias[e] in fp32
+ * accumulation.  topk_idx [T][k] int32: the k largest logits per token in
+ * descending order, the lower expert id first on equal logits (-0.0 equals
+ * +0.0).  topk_gate [T][k] fp32: softmax over the k selected logits. */
+moe_status moe_route(const moe_layer_desc* desc, const uint16_t* x, int32_t T,
+                     int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* Slot resolution, miss list and buckets ([MD] "1 トークン、三者の分担",
+ * placement figure of "粗から細へ").  Pair p = t*k + j.
+ *  slot_idx [T][k]: slot of each chosen expert, -1 when not resident
+ *    (topk_idx outside [0, E), or slot_of_expert outside [-1, S), count as
+ *    not resident).
+ *  miss [T*k] + miss_off [T+1]: the misses as (expert, token, gate) in
+ *    (t, j) order; token t's are miss[miss_off[t] .. miss_off[t+1]).  The
+ *    gate is copied bit for bit from topk_gate.
+ *  bucket_off [S+1], bucket_pair [T*k]: hit pairs sorted stably by slot
+ *    (i.e. by (slot, t, j)); slot s owns bucket_pair[bucket_off[s] ..
+ *    bucket_off[s+1]).  Entries past bucket_off[S] are left untouched. */
+moe_status moe_resolve_slots(const moe_layer_desc* desc, const int32_t* topk_idx,
+                             const float* topk_gate, int32_t T, int32_t* slot_idx,
+                             int32_t* bucket_off, int32_t* bucket_pair, moe_miss* miss,
+                             int32_t* miss_off, void* ws, size_t ws_bytes, void* stream);
+
+/* Expert FFN of every bucketed pair and of the shared expert ([MD]
+ * "1 トークン、三者の分担", "長いプロンプトを読む").  For a pair p = t*k + j in
+ * slot s's bucket: a = G_s x_t, u = U_s x_t, h = silu(a) * u, pair_out[p] =
+ * D_s h (fp32 [T*k][H]; rows of pairs in no bucket are left untouched).
+ * shared_out [T][H] fp32 = the same FFN with the shared expert (ignored and
+ * may be NULL when the layer has none).  Each slot's weights are read once
+ * for all of its tokens.  Small T runs dequant-fused GEMVs; large T (>= 256
+ * tokens with Q2/Q4 experts) runs an fp16-MFMA grouped GEMM whose weights
+ * are dequantised to fp16 tiles (fp32 accumulation). */
+moe_status moe_expert_ffn(const moe_layer_desc* desc, const uint16_t* x, int32_t T,
+                          const int32_t* bucket_off, const int32_t* bucket_pair,
+                          float* pair_out, float* shared_out, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* Combine ([MD] "1 トークン、三者の分担": the GPU sums the expert results).
+ * y[t] = shared_out[t] + sum over j = 0..k-1 with slot_idx[t][j] >= 0 of
+ * topk_gate[t][j] * pair_out[t*k+j], j ascending, fp32.  shared_out may be
+ * NULL (no shared expert). */
+moe_status moe_combine(const moe_layer_desc* desc, int32_t T, const int32_t* slot_idx,
+                       const float* topk_gate, const float* pair_out, const float* shared_out,
+                       float* y, void* stream);
+
+/* The whole layer for decode and verify batches (1 <= T <= MOE_LAYER_MAX_T):
+ * route, resolve, FFN of the hit experts (each read once), shared expert and
+ * combine, fused.  Outputs as above: y [T][H] fp32 (the misses are NOT in
+ * y: they are listed in miss/miss_off for another tier), topk_idx,
+ * topk_gate, slot_idx [T][k], miss [T*k], miss_off [T+1]. */
+moe_status moe_layer(const moe_layer_desc* desc, const uint16_t* x, int32_t T, float* y,
+                     int32_t* topk_idx, float* topk_gate, int32_t* slot_idx, moe_miss* miss,
+                     int32_t* miss_off, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

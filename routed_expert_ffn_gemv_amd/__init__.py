@@ -1,0 +1,205 @@
+"""Python binding of libmoe.so, the MI355X (gfx950) routed-MoE layer.
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+PyTorch provides device memory (tensors) and the stream; functions take
+torch tensors, pass their device pointers and the current HIP stream, and
+raise MoEError on a non-zero status.  The names follow include/moe.h.
+
+The library must be built (``__graft_entry__.build()`` or
+``python -m routed_expert_ffn_gemv_amd.build``); importing fails loudly when
+it is missing -- there is no fallback implementation.
+"""
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = range(5)
+MOE_W_F32, MOE_W_BF16, MOE_W_Q2B32, MOE_W_Q4B32 = range(4)
+MOE_LAYER_MAX_T = 16
+FORMATS = {"f32": MOE_W_F32, "bf16": MOE_W_BF16, "q2": MOE_W_Q2B32, "q4": MOE_W_Q4B32}
+
+# Every symbol include/moe.h declares.
+EXPORTS = ("moe_status_string", "moe_version", "moe_workspace_size", "moe_route",
+           "moe_resolve_slots", "moe_expert_ffn", "moe_combine", "moe_layer")
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+class moe_mat(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("data", ctypes.c_void_p),
+                ("scale", ctypes.c_void_p), ("min", ctypes.c_void_p)]
+
+
+class moe_layer_desc(ctypes.Structure):
+    _fields_ = [("E", ctypes.c_int32), ("k", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("I", ctypes.c_int32), ("num_slots", ctypes.c_int32),
+                ("router_fmt", ctypes.c_int32), ("router_w", ctypes.c_void_p),
+                ("router_bias", ctypes.c_void_p), ("slot_of_expert", ctypes.c_void_p),
+                ("gate", moe_mat), ("up", moe_mat), ("down", moe_mat),
+                ("sh_gate", moe_mat), ("sh_up", moe_mat), ("sh_down", moe_mat)]
+
+
+class moe_miss(ctypes.Structure):
+    _fields_ = [("expert", ctypes.c_int32), ("token", ctypes.c_int32), ("gate", ctypes.c_float)]
+
+
+def _load():
+    # libmoe.so must bind to the HIP runtime PyTorch loads (one runtime per
+    # process), so PyTorch is imported before the library is opened.
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                          "(there is no CPU fallback for the MoE layer)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    D = ctypes.POINTER(moe_layer_desc)
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_status_string.argtypes = [I32]
+    lib.moe_version.restype = I32
+    lib.moe_version.argtypes = []
+    lib.moe_workspace_size.restype = I32
+    lib.moe_workspace_size.argtypes = [D, I32, ctypes.POINTER(SZ)]
+    lib.moe_route.restype = I32
+    lib.moe_route.argtypes = [D, P, I32, P, P, P, SZ, P]
+    lib.moe_resolve_slots.restype = I32
+    lib.moe_resolve_slots.argtypes = [D, P, P, I32, P, P, P, P, P, P, SZ, P]
+    lib.moe_expert_ffn.restype = I32
+    lib.moe_expert_ffn.argtypes = [D, P, I32, P, P, P, P, P, SZ, P]
+    lib.moe_combine.restype = I32
+    lib.moe_combine.argtypes = [D, I32, P, P, P, P, P, P]
+    lib.moe_layer.restype = I32
+    lib.moe_layer.argtypes = [D, P, I32, P, P, P, P, P, P, P, SZ, P]
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status):
+    return lib.moe_status_string(int(status)).decode()
+
+
+def moe_version():
+    return lib.moe_version()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(status, what):
+    if status != MOE_OK:
+        raise MoEError(status, what)
+
+
+class LayerDesc:
+    """A moe_layer_desc built from torch tensors (kept alive here).
+
+    router_w: [E][H] fp32 or bf16-bits (int16/uint16/bfloat16) tensor;
+    pools: dict gate/up/down -> tensor (f32) or (codes, scale, min) tensors
+    stacked by slot; shared: the same dict for the shared expert or None."""
+
+    def __init__(self, E, k, H, I, router_w, router_fmt, wfmt, pools, shared=None,
+                 router_bias=None, slot_of_expert=None, num_slots=None):
+        self._keep = [router_w, router_bias, slot_of_expert, pools, shared]
+        d = moe_layer_desc()
+        d.E, d.k, d.H, d.I = E, k, H, I
+        d.num_slots = E if num_slots is None else num_slots
+        d.router_fmt = FORMATS[router_fmt] if isinstance(router_fmt, str) else router_fmt
+        d.router_w = _ptr(router_w)
+        d.router_bias = _ptr(router_bias)
+        d.slot_of_expert = _ptr(slot_of_expert)
+        fmt = FORMATS[wfmt] if isinstance(wfmt, str) else wfmt
+        for name in ("gate", "up", "down"):
+            setattr(d, name, self._mat(fmt, pools[name]))
+            if shared is not None:
+                setattr(d, "sh_" + name, self._mat(fmt, shared[name]))
+        self.desc = d
+        self.E, self.k, self.H, self.I, self.fmt = E, k, H, I, fmt
+        self.num_slots = d.num_slots
+        self.has_shared = shared is not None
+
+    @staticmethod
+    def _mat(fmt, p):
+        m = moe_mat()
+        m.fmt = fmt
+        if fmt == MOE_W_F32 or fmt == MOE_W_BF16:
+            m.data = _ptr(p)
+        else:
+            m.data, m.scale, m.min = _ptr(p[0]), _ptr(p[1]), _ptr(p[2])
+        return m
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.desc)
+
+
+def moe_workspace_size(desc, T):
+    n = ctypes.c_size_t(0)
+    _check(lib.moe_workspace_size(desc.ref, int(T), ctypes.byref(n)), "moe_workspace_size")
+    return n.value
+
+
+def workspace(desc, T, device="cuda"):
+    """A uint8 device tensor large enough for every call at this T."""
+    import torch
+    n = moe_workspace_size(desc, T)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def moe_route(desc, x, T, topk_idx, topk_gate, ws, stream=None):
+    _check(lib.moe_route(desc.ref, _ptr(x), int(T), _ptr(topk_idx), _ptr(topk_gate), _ptr(ws),
+                         ws.numel() if ws is not None else 0, _stream(stream)), "moe_route")
+
+
+def moe_resolve_slots(desc, topk_idx, topk_gate, T, slot_idx, bucket_off, bucket_pair, miss,
+                      miss_off, ws, stream=None):
+    """miss: a device tensor of T*k*3 int32 words (moe_miss records)."""
+    _check(lib.moe_resolve_slots(desc.ref, _ptr(topk_idx), _ptr(topk_gate), int(T),
+                                 _ptr(slot_idx), _ptr(bucket_off), _ptr(bucket_pair), _ptr(miss),
+                                 _ptr(miss_off), _ptr(ws), ws.numel() if ws is not None else 0,
+                                 _stream(stream)), "moe_resolve_slots")
+
+
+def moe_expert_ffn(desc, x, T, bucket_off, bucket_pair, pair_out, shared_out, ws, stream=None):
+    _check(lib.moe_expert_ffn(desc.ref, _ptr(x), int(T), _ptr(bucket_off), _ptr(bucket_pair),
+                              _ptr(pair_out), _ptr(shared_out), _ptr(ws),
+                              ws.numel() if ws is not None else 0, _stream(stream)),
+           "moe_expert_ffn")
+
+
+def moe_combine(desc, T, slot_idx, topk_gate, pair_out, shared_out, y, stream=None):
+    _check(lib.moe_combine(desc.ref, int(T), _ptr(slot_idx), _ptr(topk_gate), _ptr(pair_out),
+                           _ptr(shared_out), _ptr(y), _stream(stream)), "moe_combine")
+
+
+def moe_layer(desc, x, T, y, topk_idx, topk_gate, slot_idx, miss, miss_off, ws, stream=None):
+    _check(lib.moe_layer(desc.ref, _ptr(x), int(T), _ptr(y), _ptr(topk_idx), _ptr(topk_gate),
+                         _ptr(slot_idx), _ptr(miss), _ptr(miss_off), _ptr(ws),
+                         ws.numel() if ws is not None else 0, _stream(stream)), "moe_layer")
+
+
+def unpack_miss(miss_tensor, n):
+    """(expert, token, gate) numpy arrays of the first n moe_miss records of
+    a device or host int32 tensor [>= 3n]."""
+    import numpy as np
+    raw = miss_tensor[: 3 * n].cpu().numpy().astype(np.int32).reshape(n, 3)
+    return raw[:, 0].copy(), raw[:, 1].copy(), raw[:, 2].copy().view(np.float32)

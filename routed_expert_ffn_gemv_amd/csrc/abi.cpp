@@ -1,0 +1,297 @@
+// C ABI of the routed-MoE layer: host-side validation, workspace layout and
+// kernel dispatch.  No call allocates device memory or synchronises.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 32;
+constexpr int kMaxH = 8192;
+constexpr int kMaxI = 4096;
+constexpr int kMaxSlots = 16384;
+constexpr int64_t kMaxT = int64_t(1) << 22;
+constexpr size_t kAlign = 256;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool valid_pool(const moe_mat& m, int fmt) {
+  if (m.fmt != fmt || !m.data) return false;
+  if (fmt == MOE_W_F32) return aligned(m.data, 16);
+  return m.scale && m.min && aligned(m.data, 16) && aligned(m.scale, 4) && aligned(m.min, 4);
+}
+
+bool has_shared(const moe_layer_desc* d) { return d->sh_gate.data != nullptr; }
+
+// Checks the layer description.  Returns MOE_OK, MOE_ERR_INVALID or
+// MOE_ERR_UNSUPPORTED.
+moe_status check_desc(const moe_layer_desc* d) {
+  if (!d) return MOE_ERR_INVALID;
+  if (d->E < 1 || d->k < 1 || d->k > d->E || d->H < 32 || d->I < 32 || d->H % 32 || d->I % 32 ||
+      d->num_slots < 1)
+    return MOE_ERR_INVALID;
+  if (d->E > kMaxE || d->k > kMaxK || d->H > kMaxH || d->I > kMaxI || d->num_slots > kMaxSlots)
+    return MOE_ERR_UNSUPPORTED;
+  if (!d->slot_of_expert && d->num_slots != d->E) return MOE_ERR_INVALID;
+  if (d->router_fmt != MOE_W_F32 && d->router_fmt != MOE_W_BF16) return MOE_ERR_UNSUPPORTED;
+  if (!d->router_w || !aligned(d->router_w, 16)) return MOE_ERR_INVALID;
+  const int fmt = d->gate.fmt;
+  if (fmt != MOE_W_F32 && fmt != MOE_W_Q2B32 && fmt != MOE_W_Q4B32) return MOE_ERR_UNSUPPORTED;
+  if (fmt == MOE_W_Q2B32 && (d->H % 64 || d->I % 64)) return MOE_ERR_INVALID;
+  if (!valid_pool(d->gate, fmt) || !valid_pool(d->up, fmt) || !valid_pool(d->down, fmt))
+    return MOE_ERR_INVALID;
+  if (has_shared(d) &&
+      (!valid_pool(d->sh_gate, fmt) || !valid_pool(d->sh_up, fmt) || !valid_pool(d->sh_down, fmt)))
+    return MOE_ERR_INVALID;
+  return MOE_OK;
+}
+
+// Workspace regions (each 256-byte aligned), in this order:
+//   logits  [T][E] fp32
+//   active  slot[cap], start[cap+1], count[1]
+//   slotbuf [T*k] int32 (moe_layer's slot_idx when the caller passes none)
+//   pairbuf [T*k][H] fp32 + sharedbuf [T][H] fp32 (moe_layer only, T <= 16)
+//   bucket  off[S+1] + pair[T*k] (moe_layer only)
+//   h       [T*k + T][I] fp32 (GEMV path) -- or the grouped-GEMM workspace
+//   resolve large-path counters
+struct WsLayout {
+  size_t logits, active, slotbuf, pairbuf, sharedbuf, bucket, h, resolve, total;
+  int cap;
+};
+
+WsLayout layout(const moe_layer_desc* d, int64_t T) {
+  WsLayout w;
+  const int64_t P = T * d->k;
+  w.cap = int(P < d->num_slots ? P : d->num_slots);
+  size_t o = 0;
+  w.logits = o;
+  o += up(size_t(T) * d->E * 4);
+  w.active = o;
+  o += up(size_t(2 * w.cap + 2) * 4);
+  w.slotbuf = o;
+  o += up(size_t(P) * 4);
+  const bool layer_sized = T <= MOE_LAYER_MAX_T;
+  w.pairbuf = o;
+  o += layer_sized ? up(size_t(P) * d->H * 4) : 0;
+  w.sharedbuf = o;
+  o += layer_sized ? up(size_t(T) * d->H * 4) : 0;
+  w.bucket = o;
+  o += layer_sized ? up(size_t(d->num_slots + 1 + P) * 4) : 0;
+  w.h = o;
+  o += up(size_t(P + T) * d->I * 4);
+  w.resolve = o;
+  o += up(resolve_large_ws(int(T), d->k, d->num_slots));
+  w.total = o;
+  return w;
+}
+
+template <typename Tp>
+Tp* at(void* ws, size_t off) {
+  return reinterpret_cast<Tp*>(static_cast<uint8_t*>(ws) + off);
+}
+
+ActiveList active_at(void* ws, const WsLayout& w) {
+  ActiveList a;
+  a.slot = at<int32_t>(ws, w.active);
+  a.start = a.slot + w.cap;
+  a.count = a.start + w.cap + 1;
+  return a;
+}
+
+moe_status check_ws(const moe_layer_desc* d, int64_t T, void* ws, size_t ws_bytes) {
+  const WsLayout w = layout(d, T);
+  if (!ws || !aligned(ws, kAlign)) return MOE_ERR_INVALID;
+  if (ws_bytes < w.total) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+moe_status device_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
+
+FfnArgs ffn_args(const moe_layer_desc* d, const uint16_t* x, int T) {
+  FfnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = x;
+  a.T = T;
+  a.k = d->k;
+  a.H = d->H;
+  a.I = d->I;
+  a.fmt = d->gate.fmt;
+  a.g = make_view(d->gate, d->I, d->H);
+  a.u = make_view(d->up, d->I, d->H);
+  a.d = make_view(d->down, d->H, d->I);
+  if (has_shared(d)) {
+    a.sg = make_view(d->sh_gate, d->I, d->H);
+    a.su = make_view(d->sh_up, d->I, d->H);
+    a.sd = make_view(d->sh_down, d->H, d->I);
+  }
+  return a;
+}
+
+moe_status run_route(const moe_layer_desc* d, const uint16_t* x, int T, int32_t* idx, float* gate,
+                     void* ws, const WsLayout& w, hipStream_t st) {
+  float* logits = at<float>(ws, w.logits);
+  hipError_t e = launch_router(x, T, d->H, d->E, d->router_fmt, d->router_w, d->router_bias,
+                               logits, st);
+  if (e == hipSuccess) e = launch_topk(logits, T, d->E, d->k, idx, gate, st);
+  return device_status(e);
+}
+
+moe_status run_resolve(const moe_layer_desc* d, const int32_t* idx, const float* gate, int T,
+                       int32_t* slot_idx, int32_t* bucket_off, int32_t* bucket_pair,
+                       moe_miss* miss, int32_t* miss_off, void* ws, const WsLayout& w,
+                       hipStream_t st) {
+  const ActiveList act = active_at(ws, w);
+  hipError_t e;
+  if (int64_t(T) * d->k <= kResolveSmallMax)
+    e = launch_resolve_small(T, d->k, d->E, d->num_slots, idx, gate, d->slot_of_expert, slot_idx,
+                             bucket_off, bucket_pair, miss, miss_off, act, st);
+  else
+    e = launch_resolve_large(T, d->k, d->E, d->num_slots, idx, gate, d->slot_of_expert, slot_idx,
+                             bucket_off, bucket_pair, miss, miss_off, act,
+                             at<void>(ws, w.resolve), st);
+  return device_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int32_t s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or format";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_DEVICE: return "device launch failed";
+    default: return "unknown status";
+  }
+}
+
+int32_t moe_version(void) { return 100; }
+
+moe_status moe_workspace_size(const moe_layer_desc* desc, int32_t T, size_t* bytes) {
+  const moe_status s = check_desc(desc);
+  if (s != MOE_OK) return s;
+  if (!bytes || T < 0) return MOE_ERR_INVALID;
+  if (T > kMaxT) return MOE_ERR_UNSUPPORTED;
+  *bytes = layout(desc, T).total;
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_layer_desc* desc, const uint16_t* x, int32_t T, int32_t* topk_idx,
+                     float* topk_gate, void* ws, size_t ws_bytes, void* stream) {
+  moe_status s = check_desc(desc);
+  if (s != MOE_OK) return s;
+  if (T < 0) return MOE_ERR_INVALID;
+  if (T > kMaxT) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !aligned(x, 16) || !topk_idx || !topk_gate) return MOE_ERR_INVALID;
+  if ((s = check_ws(desc, T, ws, ws_bytes)) != MOE_OK) return s;
+  return run_route(desc, x, T, topk_idx, topk_gate, ws, layout(desc, T),
+                   static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_resolve_slots(const moe_layer_desc* desc, const int32_t* topk_idx,
+                             const float* topk_gate, int32_t T, int32_t* slot_idx,
+                             int32_t* bucket_off, int32_t* bucket_pair, moe_miss* miss,
+                             int32_t* miss_off, void* ws, size_t ws_bytes, void* stream) {
+  moe_status s = check_desc(desc);
+  if (s != MOE_OK) return s;
+  if (T < 0) return MOE_ERR_INVALID;
+  if (T > kMaxT) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!topk_idx || !topk_gate || !slot_idx || !bucket_off || !bucket_pair || !miss || !miss_off)
+    return MOE_ERR_INVALID;
+  if ((s = check_ws(desc, T, ws, ws_bytes)) != MOE_OK) return s;
+  return run_resolve(desc, topk_idx, topk_gate, T, slot_idx, bucket_off, bucket_pair, miss,
+                     miss_off, ws, layout(desc, T), static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_expert_ffn(const moe_layer_desc* desc, const uint16_t* x, int32_t T,
+                          const int32_t* bucket_off, const int32_t* bucket_pair, float* pair_out,
+                          float* shared_out, void* ws, size_t ws_bytes, void* stream) {
+  moe_status s = check_desc(desc);
+  if (s != MOE_OK) return s;
+  if (T < 0) return MOE_ERR_INVALID;
+  if (T > kMaxT) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !aligned(x, 16) || !bucket_off || !bucket_pair || !pair_out ||
+      (has_shared(desc) && !shared_out))
+    return MOE_ERR_INVALID;
+  if (!aligned(pair_out, 16) || (shared_out && !aligned(shared_out, 16))) return MOE_ERR_INVALID;
+  if ((s = check_ws(desc, T, ws, ws_bytes)) != MOE_OK) return s;
+  const WsLayout w = layout(desc, T);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  FfnArgs a = ffn_args(desc, x, T);
+  a.act = active_at(ws, w);
+  a.active_cap = w.cap;
+  a.bucket_pair = bucket_pair;
+  a.h = at<float>(ws, w.h);
+  a.h_sh = a.h + size_t(T) * desc->k * desc->I;
+  a.pair_out = pair_out;
+  a.shared_out = shared_out;
+  hipError_t e = launch_active_from_offsets(desc->num_slots, bucket_off, a.act, st);
+  if (e == hipSuccess) e = launch_ffn_gemv(a, st);
+  return device_status(e);
+}
+
+moe_status moe_combine(const moe_layer_desc* desc, int32_t T, const int32_t* slot_idx,
+                       const float* topk_gate, const float* pair_out, const float* shared_out,
+                       float* y, void* stream) {
+  moe_status s = check_desc(desc);
+  if (s != MOE_OK) return s;
+  if (T < 0) return MOE_ERR_INVALID;
+  if (T > kMaxT) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!slot_idx || !topk_gate || !pair_out || !y || !aligned(pair_out, 16) || !aligned(y, 16) ||
+      (shared_out && !aligned(shared_out, 16)))
+    return MOE_ERR_INVALID;
+  return device_status(launch_combine(T, desc->k, desc->H, slot_idx, topk_gate, pair_out,
+                                      shared_out, y, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_layer(const moe_layer_desc* desc, const uint16_t* x, int32_t T, float* y,
+                     int32_t* topk_idx, float* topk_gate, int32_t* slot_idx, moe_miss* miss,
+                     int32_t* miss_off, void* ws, size_t ws_bytes, void* stream) {
+  moe_status s = check_desc(desc);
+  if (s != MOE_OK) return s;
+  if (T < 0) return MOE_ERR_INVALID;
+  if (T > MOE_LAYER_MAX_T) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !aligned(x, 16) || !y || !aligned(y, 16) || !topk_idx || !topk_gate || !miss ||
+      !miss_off)
+    return MOE_ERR_INVALID;
+  if ((s = check_ws(desc, T, ws, ws_bytes)) != MOE_OK) return s;
+  const WsLayout w = layout(desc, T);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* sl = slot_idx ? slot_idx : at<int32_t>(ws, w.slotbuf);
+  int32_t* boff = at<int32_t>(ws, w.bucket);
+  int32_t* bpair = boff + desc->num_slots + 1;
+  float* pairbuf = at<float>(ws, w.pairbuf);
+  float* shbuf = has_shared(desc) ? at<float>(ws, w.sharedbuf) : nullptr;
+  s = run_route(desc, x, T, topk_idx, topk_gate, ws, w, st);
+  if (s == MOE_OK)
+    s = run_resolve(desc, topk_idx, topk_gate, T, sl, boff, bpair, miss, miss_off, ws, w, st);
+  if (s != MOE_OK) return s;
+  FfnArgs a = ffn_args(desc, x, T);
+  a.act = active_at(ws, w);
+  a.active_cap = w.cap;
+  a.bucket_pair = bpair;
+  a.h = at<float>(ws, w.h);
+  a.h_sh = a.h + size_t(T) * desc->k * desc->I;
+  a.pair_out = pairbuf;
+  a.shared_out = shbuf;
+  hipError_t e = launch_ffn_gemv(a, st);
+  if (e == hipSuccess)
+    e = launch_combine(T, desc->k, desc->H, sl, topk_gate, pairbuf, shbuf, y, st);
+  return device_status(e);
+}
+
+}  // extern "C"

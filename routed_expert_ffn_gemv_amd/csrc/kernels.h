@@ -1,0 +1,68 @@
+// Host-side launchers of the gfx950 kernels (one translation unit each).
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+// router
+constexpr int kRouterNT = 8;              // tokens per router block
+constexpr int kRouterLdsBytes = 64 * 1024;
+hipError_t launch_router(const uint16_t* x, int T, int H, int E, int rfmt, const void* W,
+                         const float* bias, float* logits, hipStream_t st);
+hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx, float* gate,
+                       hipStream_t st);
+// bf16 MFMA router GEMM for large T (BF16 router weights).
+hipError_t launch_router_mfma(const uint16_t* x, int T, int H, int E, const uint16_t* W,
+                              const float* bias, float* logits, hipStream_t st);
+
+// Active bucket list: slots with a non-empty bucket in ascending order,
+// where their bucket starts, and how many there are.
+struct ActiveList {
+  int32_t* slot;    // [cap]
+  int32_t* start;   // [cap + 1]; start[n] = total pairs
+  int32_t* count;   // [1]
+};
+
+// resolve
+constexpr int kResolveSmallMax = 256;     // pairs handled by one block
+constexpr int kResolveChunk = 1024;       // pairs per block in the large path
+hipError_t launch_resolve_small(int T, int k, int E, int S, const int32_t* idx,
+                                const float* gate, const int32_t* slot_of, int32_t* slot_idx,
+                                int32_t* bucket_off, int32_t* bucket_pair, moe_miss* miss,
+                                int32_t* miss_off, ActiveList act, hipStream_t st);
+size_t resolve_large_ws(int T, int k, int S);
+hipError_t launch_resolve_large(int T, int k, int E, int S, const int32_t* idx,
+                                const float* gate, const int32_t* slot_of, int32_t* slot_idx,
+                                int32_t* bucket_off, int32_t* bucket_pair, moe_miss* miss,
+                                int32_t* miss_off, ActiveList act, void* ws, hipStream_t st);
+hipError_t launch_active_from_offsets(int S, const int32_t* bucket_off, ActiveList act,
+                                      hipStream_t st);
+
+// expert FFN (decode GEMV)
+struct FfnArgs {
+  const uint16_t* x;     // bf16 [T][H]
+  int T, k, H, I, fmt;
+  MatView g, u, d;       // routed pools (by slot)
+  MatView sg, su, sd;    // shared expert (codes == nullptr: none)
+  ActiveList act;        // buckets to run
+  const int32_t* bucket_pair;
+  int active_cap;        // upper bound of act.count
+  float* h;              // fp32 [T*k][I] by pair id
+  float* h_sh;           // fp32 [T][I]
+  float* pair_out;       // fp32 [T*k][H]
+  float* shared_out;     // fp32 [T][H]
+};
+hipError_t launch_ffn_gemv(const FfnArgs& a, hipStream_t st);
+
+// expert FFN (prefill grouped GEMM, fp16 MFMA)
+size_t ffn_gemm_ws(int T, int k, int H, int I, int S);
+hipError_t launch_ffn_gemm(const FfnArgs& a, int S, const int32_t* bucket_off, void* ws,
+                           hipStream_t st);
+
+// combine
+hipError_t launch_combine(int T, int k, int H, const int32_t* slot_idx, const float* gate,
+                          const float* pair_out, const float* shared_out, float* y,
+                          hipStream_t st);
+
+}  // namespace moe

@@ -285,6 +285,7 @@ def fill_lib():
     """The GPU fill library (libsynth.so, built from fill.hip)."""
     global _LIB
     if _LIB is None:
+        import torch  # noqa: F401  (bind to PyTorch's HIP runtime first)
         path = os.path.join(_HERE, "libsynth.so")
         if not os.path.exists(path):
             raise RuntimeError("synth/libsynth.so is not built; run __graft_entry__.build()")
@@ -317,3 +318,15 @@ def fill_pool_device(cfg, matrix, slot_layers, slot_experts, codes, scale, mn,
         ctypes.c_void_p(mn.data_ptr()), ctypes.c_void_p(stream))
     if rc != 0:
         raise RuntimeError(f"synth_fill_q failed with status {rc}")
+
+
+def build():
+    """Compile libsynth.so (the GPU fill kernel) for gfx950."""
+    import subprocess
+    src = os.path.join(_HERE, "fill.hip")
+    out = os.path.join(_HERE, "libsynth.so")
+    subprocess.check_call(["/opt/rocm/bin/hipcc", "-O3", "-std=c++17", "-fPIC", "-shared",
+                           "--offload-arch=gfx950", "-mcode-object-version=5", "-Xclang", "-target-feature", "-Xclang",
+                           "-packed-fp32-ops", "-x", "hip", src, "-o", out],
+                          stderr=subprocess.DEVNULL)
+    return out

@@ -1,0 +1,104 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Routing indices, slots, miss lists and buckets must be bit-exact; floating
+outputs within 2e-3 relative error (normwise per token row).  Inputs carry a
+routing margin (every gap among a token's top-(k+1) logits >= 1e-3)."""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import (TOL, DeviceLayer, check_routing, host, rowwise_rel_err, say,
+                     small_cfg)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    # ragged shapes: partial row chunks, several units per expert, odd T
+    "q2_ragged": small_cfg(E=40, k=3, H=192, I=128, T=7, bias="zipf", seed=11),
+    "q4_ragged": small_cfg(E=24, k=5, H=96, I=160, T=13, wfmt="q4", shared=False, seed=12),
+    "f32_ragged": small_cfg(E=9, k=4, H=96, I=32, T=3, wfmt="f32", router_fmt="f32",
+                            shared=False, seed=13),
+    "q2_k_eq_E": small_cfg(E=8, k=8, H=128, I=64, T=5, seed=14),
+    "q4_T16": small_cfg(E=64, k=10, H=256, I=128, T=16, wfmt="q4", bias="zipf", seed=15),
+    "c1": synth.CONFIGS["c1"],
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("path", ["layer", "steps"])
+def test_small_layer(name, path):
+    cfg = SMALL[name]
+    say(f"[gpu] small layer {name} via {path}: E={cfg.E} k={cfg.k} H={cfg.H} I={cfg.I} T={cfg.T}")
+    x, _ = oracle.margin_x(cfg, 0)
+    L = DeviceLayer(cfg, 0, x=x)
+    o = L.run_layer() if path == "layer" else L.run_steps()
+    ref = L.oracle()
+    check_routing(o, ref, cfg.k)
+    assert rowwise_rel_err(host(o["y"]), ref["y"]) <= TOL
+    if path == "steps":
+        np.testing.assert_array_equal(host(o["bucket_off"]), ref["bucket_off"])
+        np.testing.assert_array_equal(host(o["bucket_pair"])[: len(ref["bucket_pair"])],
+                                      ref["bucket_pair"])
+        hit = ref["slot_idx"].ravel() >= 0
+        assert rowwise_rel_err(host(o["pair_out"])[hit], ref["pair_out"][hit]) <= TOL
+        if cfg.shared:
+            assert rowwise_rel_err(host(o["shared_out"]), ref["shared_out"]) <= TOL
+
+
+def test_tiered_small_with_misses():
+    """A partial slot table: misses listed bit-exactly; y holds hits only and
+    y + sum over misses of gate * FFN equals the all-resident layer."""
+    cfg = small_cfg(E=32, k=4, H=128, I=64, T=9, bias="zipf", seed=21)
+    say("[gpu] tiered small layer with misses")
+    x, _ = oracle.margin_x(cfg, 0)
+    resident = [1, 3, 4, 8, 9, 15, 16, 20, 27, 31]
+    slot_of = np.full(cfg.E, -1, np.int32)
+    slot_of[resident] = np.arange(len(resident))[::-1]      # slots not in id order
+    from synth import device as sdev
+    pool = sdev.expert_pool(cfg, [0] * len(resident), [resident[len(resident) - 1 - s]
+                                                          for s in range(len(resident))])
+    L = DeviceLayer(cfg, 0, x=x, pool=pool, slot_of=slot_of, num_slots=len(resident))
+    for path in ("layer", "steps"):
+        o = L.run_layer() if path == "layer" else L.run_steps()
+        ref = L.oracle(with_misses=True)
+        assert len(ref["miss_expert"]) > 0
+        check_routing(o, ref, cfg.k)
+        assert rowwise_rel_err(host(o["y"]), ref["y"]) <= TOL
+    # completion invariant on the GPU's partial output
+    y = host(o["y"]).astype(np.float64)
+    for e, t, g in zip(ref["miss_expert"], ref["miss_token"], ref["miss_gate"]):
+        y[t] += g * oracle.ffn(cfg.wfmt, cfg.H, cfg.I, synth.gen_expert(cfg, 0, int(e)),
+                               L.inp["x_host"][t:t + 1])[0]
+    assert rowwise_rel_err(y, ref["y_full"]) <= TOL
+
+
+def test_all_miss_table():
+    cfg = small_cfg(E=16, k=3, H=64, I=64, T=5, seed=22)
+    say("[gpu] all-miss slot table")
+    x, _ = oracle.margin_x(cfg, 0)
+    slot_of = np.full(cfg.E, -1, np.int32)
+    from synth import device as sdev
+    pool = sdev.expert_pool(cfg, [0], [0])
+    L = DeviceLayer(cfg, 0, x=x, pool=pool, slot_of=slot_of, num_slots=1)
+    o = L.run_layer()
+    ref = L.oracle()
+    check_routing(o, ref, cfg.k)
+    assert len(ref["miss_expert"]) == cfg.T * cfg.k
+    assert rowwise_rel_err(host(o["y"]), ref["y"]) <= TOL   # shared expert only
+
+
+def test_c2_decode_layer():
+    """The decode layer at full size, the launch bench.py times (moe_layer, T=1)."""
+    cfg = synth.CONFIGS["c2"]
+    say("[gpu] c2 decode layer E=512 k=10 H=2048 I=768 q2 + shared, T=1")
+    for layer in (0, 1):
+        x, _ = oracle.margin_x(cfg, layer)
+        L = DeviceLayer(cfg, layer, x=x)
+        o = L.run_layer()
+        ref = L.oracle()
+        check_routing(o, ref, cfg.k)
+        err = rowwise_rel_err(host(o["y"]), ref["y"])
+        say(f"  layer {layer}: rel err {err:.2e}")
+        assert err <= TOL
