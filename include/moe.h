@@ -162,9 +162,19 @@ moe_status moe_combine(const moe_layer_desc* desc, int32_t T, const int32_t* slo
 
 /* The whole layer for decode and verify batches (1 <= T <= MOE_LAYER_MAX_T):
  * route, resolve, FFN of the hit experts (each read once), shared expert and
- * combine, fused.  Outputs as above: y [T][H] fp32 (the misses are NOT in
- * y: they are listed in miss/miss_off for another tier), topk_idx,
- * topk_gate, slot_idx [T][k], miss [T*k], miss_off [T+1]. */
+ * combine.  Outputs as above: y [T][H] fp32 (the misses are NOT in y: they
+ * are listed in miss/miss_off for another tier), topk_idx, topk_gate
+ * [T][k], slot_idx [T][k] (may be NULL), miss [T*k], miss_off [T+1].
+ * When T*k <= 256 (and the router is BF16 for Q2/Q4 experts) this is one
+ * persistent launch whose workgroups hand over through flags kept at the
+ * start of ws, in a region no other call touches: the workspace must be
+ * zero before its first moe_layer call (allocate it zeroed once); every call
+ * leaves the flags ready for the next.  That launch sums the experts into y with
+ * device-scope float atomics, so y can differ between runs in the last bits
+ * (the gate-weighted terms are added in no fixed order).  A workspace serves one moe_layer call at a time,
+ * and the launch sizes its grid to the workgroups the device holds at once,
+ * so it must not share the GPU with a kernel that would keep some of them
+ * from running.  Other shapes run the separate steps in sequence. */
 moe_status moe_layer(const moe_layer_desc* desc, const uint16_t* x, int32_t T, float* y,
                      int32_t* topk_idx, float* topk_gate, int32_t* slot_idx, moe_miss* miss,
                      int32_t* miss_off, void* ws, size_t ws_bytes, void* stream);

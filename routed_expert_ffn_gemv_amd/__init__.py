@@ -159,10 +159,11 @@ def moe_workspace_size(desc, T):
 
 
 def workspace(desc, T, device="cuda"):
-    """A uint8 device tensor large enough for every call at this T."""
+    """A zeroed uint8 device tensor large enough for every call at this T
+    (moe_layer needs the workspace zeroed before its first use)."""
     import torch
     n = moe_workspace_size(desc, T)
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
 
 
 def moe_route(desc, x, T, topk_idx, topk_gate, ws, stream=None):

@@ -6,6 +6,7 @@
 
 #include "../../include/moe.h"
 #include "kernels.h"
+#include "layer.h"
 
 using namespace moe;
 
@@ -54,6 +55,7 @@ moe_status check_desc(const moe_layer_desc* d) {
 }
 
 // Workspace regions (each 256-byte aligned), in this order:
+//   sync    cross-workgroup flags of the fused moe_layer (layer_sync_bytes)
 //   logits  [T][E] fp32
 //   active  slot[cap], start[cap+1], count[1]
 //   slotbuf [T*k] int32 (moe_layer's slot_idx when the caller passes none)
@@ -62,7 +64,7 @@ moe_status check_desc(const moe_layer_desc* d) {
 //   h       [T*k + T][I] fp32 (GEMV path) -- or the grouped-GEMM workspace
 //   resolve large-path counters
 struct WsLayout {
-  size_t logits, active, slotbuf, pairbuf, sharedbuf, bucket, h, resolve, total;
+  size_t sync, logits, active, slotbuf, pairbuf, sharedbuf, bucket, h, resolve, total;
   int cap;
 };
 
@@ -71,6 +73,8 @@ WsLayout layout(const moe_layer_desc* d, int64_t T) {
   const int64_t P = T * d->k;
   w.cap = int(P < d->num_slots ? P : d->num_slots);
   size_t o = 0;
+  w.sync = o;
+  o += up(layer_sync_bytes(w.cap, d->I));
   w.logits = o;
   o += up(size_t(T) * d->E * 4);
   w.active = o;
@@ -271,11 +275,48 @@ moe_status moe_layer(const moe_layer_desc* desc, const uint16_t* x, int32_t T, f
   if ((s = check_ws(desc, T, ws, ws_bytes)) != MOE_OK) return s;
   const WsLayout w = layout(desc, T);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  int32_t* sl = slot_idx ? slot_idx : at<int32_t>(ws, w.slotbuf);
   int32_t* boff = at<int32_t>(ws, w.bucket);
   int32_t* bpair = boff + desc->num_slots + 1;
   float* pairbuf = at<float>(ws, w.pairbuf);
   float* shbuf = has_shared(desc) ? at<float>(ws, w.sharedbuf) : nullptr;
+  const int fmt = desc->gate.fmt;
+  if (layer_fused_ok(fmt, T, desc->k, desc->E, desc->H, desc->I) &&
+      (fmt == MOE_W_F32 || desc->router_fmt == MOE_W_BF16)) {
+    LayerArgs L;
+    memset(&L, 0, sizeof(L));
+    L.x = x;
+    L.T = T;
+    L.E = desc->E;
+    L.k = desc->k;
+    L.H = desc->H;
+    L.I = desc->I;
+    L.S = desc->num_slots;
+    L.fmt = fmt;
+    L.rfmt = desc->router_fmt;
+    L.W = desc->router_w;
+    L.bias = desc->router_bias;
+    L.slot_of = desc->slot_of_expert;
+    const FfnArgs f = ffn_args(desc, x, T);
+    L.g = f.g;
+    L.u = f.u;
+    L.d = f.d;
+    L.sg = f.sg;
+    L.su = f.su;
+    L.sd = f.sd;
+    L.has_sh = has_shared(desc) ? 1 : 0;
+    L.y = y;
+    L.idx = topk_idx;
+    L.gate = topk_gate;
+    L.slot_idx = slot_idx;
+    L.miss = miss;
+    L.miss_off = miss_off;
+    L.logits = at<float>(ws, w.logits);
+    L.h = at<float>(ws, w.h);
+    L.h_sh = L.h + size_t(T) * desc->k * desc->I;
+    L.sync = at<uint32_t>(ws, w.sync);
+    return device_status(launch_layer_fused(L, st, nullptr));
+  }
+  int32_t* sl = slot_idx ? slot_idx : at<int32_t>(ws, w.slotbuf);
   s = run_route(desc, x, T, topk_idx, topk_gate, ws, w, st);
   if (s == MOE_OK)
     s = run_resolve(desc, topk_idx, topk_gate, T, sl, boff, bpair, miss, miss_off, ws, w, st);

@@ -62,8 +62,8 @@ __global__ __launch_bounds__(256) void ffn_gateup_kernel(FfnArgs a, int units_pe
   for (int w = blockIdx.x; w < total; w += gridDim.x) {
     const Unit un = unit_of(a, w / units_per_expert, n_act);
     const int i = (w % units_per_expert) * kRowsPerUnit + wave * (64 / LPR) + lane / LPR;
-    const MatView& G = un.shared ? a.sg : a.g;
-    const MatView& U = un.shared ? a.su : a.u;
+    const MatView G = un.shared ? a.sg : a.g;
+    const MatView U = un.shared ? a.su : a.u;
     const uint8_t* gc = G.codes + un.slot * G.mat_bytes + i * row_bytes;
     const uint8_t* uc = U.codes + un.slot * U.mat_bytes + i * row_bytes;
     const uint16_t* gs = G.scale + un.slot * G.mat_blocks + int64_t(i) * sstride;
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256) void ffn_down_kernel(FfnArgs a, int units_per_
   for (int w = blockIdx.x; w < total; w += gridDim.x) {
     const Unit un = unit_of(a, w / units_per_expert, n_act);
     const int r = (w % units_per_expert) * kRowsPerUnit + wave * (64 / LPR) + lane / LPR;
-    const MatView& D = un.shared ? a.sd : a.d;
+    const MatView D = un.shared ? a.sd : a.d;
     const uint8_t* dc = D.codes + un.slot * D.mat_bytes + r * row_bytes;
     const uint16_t* ds = D.scale + un.slot * D.mat_blocks + int64_t(r) * sstride;
     const uint16_t* dm = D.mn + un.slot * D.mat_blocks + int64_t(r) * sstride;

@@ -84,19 +84,28 @@ __device__ __forceinline__ void stage_bf16(uint32_t* vec, float* sums, const uin
   }
 }
 
+// fp32 load; kCoherent reads at device scope (bypassing the per-XCD L2),
+// for data another workgroup of the same launch wrote.
+template <bool kCoherent>
+__device__ __forceinline__ float load_f32(const float* p) {
+  if (kCoherent) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return *p;
+}
+
 // Stage one fp32 row (h) as bf16 hi and lo vectors (Q formats) or as fp32.
-template <int FMT>
+template <int FMT, bool kCoherent = false>
 __device__ __forceinline__ void stage_f32(uint32_t* vhi, float* shi, uint32_t* vlo, float* slo,
                                           const float* src, int K) {
   if (FMT == MOE_W_F32) {
     float* vf = reinterpret_cast<float*>(vhi);
-    for (int c = threadIdx.x; c < K; c += blockDim.x) vf[c] = src[c];
+    for (int c = threadIdx.x; c < K; c += blockDim.x) vf[c] = load_f32<kCoherent>(src + c);
   } else {
     const int ndw = (K / Fmt<FMT>::kWPC) * Fmt<FMT>::kCS;
     for (int dw = threadIdx.x; dw < ndw; dw += blockDim.x) {
       int c;
       if (slot_low_column<FMT>(dw, &c)) {
-        const float a = src[c], b = src[c + partner_offset<FMT>()];
+        const float a = load_f32<kCoherent>(src + c);
+        const float b = load_f32<kCoherent>(src + c + partner_offset<FMT>());
         const uint32_t ah = f32_to_bf16_bits(a), bh = f32_to_bf16_bits(b);
         const uint32_t al = f32_to_bf16_bits(a - bf16_to_f32(ah));
         const uint32_t bl = f32_to_bf16_bits(b - bf16_to_f32(bh));
@@ -107,7 +116,7 @@ __device__ __forceinline__ void stage_f32(uint32_t* vhi, float* shi, uint32_t* v
     for (int b = threadIdx.x; b < K / 32; b += blockDim.x) {
       float sh = 0.f, sl = 0.f;
       for (int c = 0; c < 32; ++c) {
-        const float v = src[32 * b + c];
+        const float v = load_f32<kCoherent>(src + 32 * b + c);
         const float hi = bf16_to_f32(f32_to_bf16_bits(v));
         sh += hi;
         sl += bf16_to_f32(f32_to_bf16_bits(v - hi));

@@ -102,3 +102,65 @@ def test_c2_decode_layer():
         err = rowwise_rel_err(host(o["y"]), ref["y"])
         say(f"  layer {layer}: rel err {err:.2e}")
         assert err <= TOL
+
+
+def test_repeated_calls_share_one_workspace():
+    """Back-to-back fused calls on one workspace (counters and flag are
+    reused across calls), alternating layers and token counts."""
+    import routed_expert_ffn_gemv_amd as moe
+    cfg = small_cfg(E=64, k=6, H=256, I=128, T=16, bias="zipf", seed=31)
+    say("[gpu] repeated moe_layer calls on one workspace")
+    layers = []
+    for l in range(3):
+        x, _ = oracle.margin_x(cfg, l)
+        layers.append(DeviceLayer(cfg, l, x=x))
+    ws = moe.workspace(layers[0].desc, cfg.T)
+    refs = [L.oracle() for L in layers]
+    for rep in range(3):
+        for l, L in enumerate(layers):
+            o = L.run_layer(ws)
+            check_routing(o, refs[l], cfg.k)
+            assert rowwise_rel_err(host(o["y"]), refs[l]["y"]) <= TOL
+
+
+def test_c3_verify_stack_sampled_layers():
+    """4-token verify batch through full-size layers of the 48-layer stack
+    (Zipf-biased routing, all experts resident); moe_layer as bench.py
+    times it."""
+    cfg = synth.CONFIGS["c3"]
+    for layer in (0, 23, 47):
+        say(f"[gpu] c3 layer {layer}: E=512 k=10 T=4 q2 zipf")
+        x, _ = oracle.margin_x(cfg, layer)
+        L = DeviceLayer(cfg, layer, x=x)
+        o = L.run_layer()
+        ref = L.oracle()
+        check_routing(o, ref, cfg.k)
+        err = rowwise_rel_err(host(o["y"]), ref["y"])
+        say(f"  rel err {err:.2e}, distinct experts {len(np.unique(ref['idx']))}")
+        assert err <= TOL
+
+
+def test_c4_slot_tiering_sampled_layers():
+    """16 tokens per layer against the 4,176-expert global slot table:
+    bit-exact miss lists, hits-only y, and the completion invariant."""
+    from synth import device as sdev
+    cfg = synth.CONFIGS["c4"]
+    slot_of, sl, se, S = synth.slot_layout(cfg)
+    say(f"[gpu] c4: filling the global pool of {S} slots")
+    pool = sdev.expert_pool(cfg, sl, se)
+    for layer in (0, 31):
+        say(f"[gpu] c4 layer {layer}: T=16, resident {int((slot_of[layer] >= 0).sum())}")
+        x, _ = oracle.margin_x(cfg, layer)
+        L = DeviceLayer(cfg, layer, x=x, pool=pool, slot_of=slot_of[layer], num_slots=S)
+        o = L.run_layer()
+        ref = L.oracle(with_misses=(layer == 0))
+        check_routing(o, ref, cfg.k)
+        err = rowwise_rel_err(host(o["y"]), ref["y"])
+        hit = (ref["slot_idx"] >= 0).mean()
+        say(f"  rel err {err:.2e}, hit rate {hit:.2f}, misses {len(ref['miss_expert'])}")
+        assert err <= TOL
+        if layer == 0:
+            y = host(o["y"]).astype(np.float64)
+            for e, t, g in zip(ref["miss_expert"], ref["miss_token"], ref["miss_gate"]):
+                y[t] += g * ref["pair_out"][t * cfg.k + list(ref["idx"][t]).index(e)]
+            assert rowwise_rel_err(y, ref["y_full"]) <= TOL
