@@ -50,11 +50,11 @@ constexpr int kTMax = MOE_LAYER_MAX_T;
 constexpr int kPMax = 256;
 constexpr int kNChMax = 4;                      // 16-byte chunks per lane and weight row
 
-// Lanes per weight row: enough that a lane holds at most kNChMax chunks of a
-// 2048-wide (gate/up) or 768-wide (down) row.
+// Lanes per weight row: a lane holds at most 2 (Q2) or 4 (Q4) chunks of a
+// 2048-wide gate/up row and 3 of a 768-wide down row.
 template <int FMT>
 struct Lanes {
-  static constexpr int kGU = FMT == MOE_W_Q4B32 ? 16 : 8;   // gate/up
+  static constexpr int kGU = FMT == MOE_W_F32 ? 8 : 16;     // gate/up
   static constexpr int kD = FMT == MOE_W_Q4B32 ? 8 : 4;     // down
   static constexpr int kRowsGU = 64 / kGU;                  // rows per wave task
   static constexpr int kRowsD = kWaves * (64 / kD);         // rows per down unit
@@ -71,6 +71,14 @@ __device__ __forceinline__ void st_dev(V* p, V v) {
 __device__ __forceinline__ void fadd_dev(float* p, float v) {
   __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Marks a register as rewritten here, so work derived from it is redone at
+// this point instead of being hoisted out of the enclosing loop (emits no
+// instruction).
+__device__ __forceinline__ u32x4 fresh(u32x4 w) {
+  asm volatile("" : "+v"(w));
+  return w;
+}
+
 // Wait until this wave's memory operations have completed.
 __device__ __forceinline__ void wait_mem() { __builtin_amdgcn_s_waitcnt(0); }
 
@@ -348,86 +356,130 @@ __device__ __forceinline__ void load_row(RowRegs<FMT, NCH>& R, const uint8_t* __
   }
 }
 
-// acc[v] += this lane's part of row . vector vid(v), v < n.
-template <int FMT, int NCH, int NV>
-__device__ __forceinline__ void dot_row(const RowRegs<FMT, NCH>& R, int nch, int lane_g, int lpr,
-                                        const uint32_t* vec, int vstride, const float* sums,
-                                        int sstride, int n, const int* vid, float (&acc)[NV]) {
+// Block dot products of one 16-byte code chunk with one staged vector.
+// Q2: 64 codes = two 32-weight blocks, pairs (s, s+8) of each code dword;
+// Q4: 32 codes = one block, pairs (s, s+4).  Returns sum (128 + q) x per
+// block in p[0..1]; independent accumulators keep the dot2 chains short.
+template <int FMT>
+__device__ __forceinline__ void chunk_dot(u32x4 w, const uint32_t* xv, float* p) {
+  w = fresh(w);   // unpack per vector; keeping every unpacked pair costs more registers
+  const u32x4* x4 = reinterpret_cast<const u32x4*>(xv);
+#pragma unroll
+  for (int bb = 0; bb < (FMT == MOE_W_Q2B32 ? 2 : 1); ++bb) {
+    u32x4 xx[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xx[q] = x4[4 * bb + q];
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t pr = FMT == MOE_W_Q2B32 ? q2_pair(w[2 * bb + (q >> 1)], (q & 1) * 4 + e)
+                                                : q4_pair(w[q], e);
+        a[e] = dot2_bf16(pr, xx[q][e], a[e]);
+      }
+    p[bb] = (a[0] + a[1]) + (a[2] + a[3]);
+  }
+}
+
+// The same for two code chunks (gate and up rows) against one vector chunk.
+template <int FMT>
+__device__ __forceinline__ void chunk_dot2(u32x4 wg, u32x4 wu, const uint32_t* xv,
+                                           float* pg, float* pu) {
+  wg = fresh(wg);
+  wu = fresh(wu);
+  const u32x4* x4 = reinterpret_cast<const u32x4*>(xv);
+#pragma unroll
+  for (int bb = 0; bb < (FMT == MOE_W_Q2B32 ? 2 : 1); ++bb) {
+    u32x4 xx[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xx[q] = x4[4 * bb + q];
+    float a[4] = {0.f, 0.f, 0.f, 0.f}, c[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int s2 = (q & 1) * 4 + e;
+        const uint32_t prg = FMT == MOE_W_Q2B32 ? q2_pair(wg[2 * bb + (q >> 1)], s2)
+                                                 : q4_pair(wg[q], e);
+        const uint32_t pru = FMT == MOE_W_Q2B32 ? q2_pair(wu[2 * bb + (q >> 1)], s2)
+                                                 : q4_pair(wu[q], e);
+        a[e] = dot2_bf16(prg, xx[q][e], a[e]);
+        c[e] = dot2_bf16(pru, xx[q][e], c[e]);
+      }
+    pg[bb] = (a[0] + a[1]) + (a[2] + a[3]);
+    pu[bb] = (c[0] + c[1]) + (c[2] + c[3]);
+  }
+}
+
+// This lane's part of one row . one staged vector (at xv_base + chunk
+// offsets, block sums at sv_base), over the lane's NCH chunks.
+template <int FMT, int NCH>
+__device__ __forceinline__ float row_vec_dot(const RowRegs<FMT, NCH>& R, int nch, int lane_g,
+                                             int lpr, const uint32_t* xv_base,
+                                             const float* sv_base) {
+  float acc = 0.f;
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
     if (j >= nch) continue;
     const int c = lane_g + j * lpr;
-    const u32x4 w = R.w[j];
-    if constexpr (FMT == MOE_W_Q2B32) {
+    if constexpr (FMT == MOE_W_F32) {
+      const float4 wf = __builtin_bit_cast(float4, R.w[j]);
+      const float* xv = reinterpret_cast<const float*>(xv_base) + 4 * c;
+      acc = fmaf(wf.x, xv[0], fmaf(wf.y, xv[1], fmaf(wf.z, xv[2], fmaf(wf.w, xv[3], acc))));
+    } else if constexpr (FMT == MOE_W_Q2B32) {
+      float p[2];
+      chunk_dot<FMT>(R.w[j], xv_base + c * Fmt<FMT>::kCS, p);
       const float d0 = f16_to_f32(uint16_t(R.sc[j] & 0xFFFFu));
       const float d1 = f16_to_f32(uint16_t(R.sc[j] >> 16));
       const float m0 = f16_to_f32(uint16_t(R.mn[j] & 0xFFFFu)) - 128.f * d0;
       const float m1 = f16_to_f32(uint16_t(R.mn[j] >> 16)) - 128.f * d1;
-      uint32_t pr[32];
-#pragma unroll
-      for (int dw = 0; dw < 4; ++dw)
-#pragma unroll
-        for (int s = 0; s < 8; ++s) pr[dw * 8 + s] = q2_pair(w[dw], s);
-#pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        if (v < n) {
-          const int id = vid ? vid[v] : v;
-          const u32x4* xv = reinterpret_cast<const u32x4*>(vec + id * vstride + c * Fmt<FMT>::kCS);
-          float p0 = 0.f, p1 = 0.f;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const u32x4 xx = xv[q];
-            p0 = dot2_bf16(pr[q * 4 + 0], xx[0], p0);
-            p0 = dot2_bf16(pr[q * 4 + 1], xx[1], p0);
-            p0 = dot2_bf16(pr[q * 4 + 2], xx[2], p0);
-            p0 = dot2_bf16(pr[q * 4 + 3], xx[3], p0);
-          }
-#pragma unroll
-          for (int q = 4; q < 8; ++q) {
-            const u32x4 xx = xv[q];
-            p1 = dot2_bf16(pr[q * 4 + 0], xx[0], p1);
-            p1 = dot2_bf16(pr[q * 4 + 1], xx[1], p1);
-            p1 = dot2_bf16(pr[q * 4 + 2], xx[2], p1);
-            p1 = dot2_bf16(pr[q * 4 + 3], xx[3], p1);
-          }
-          const float* sv = sums + id * sstride + 2 * c;
-          acc[v] += d0 * p0 + m0 * sv[0] + d1 * p1 + m1 * sv[1];
-        }
-      }
-    } else if constexpr (FMT == MOE_W_Q4B32) {
+      acc += (d0 * p[0] + m0 * sv_base[2 * c]) + (d1 * p[1] + m1 * sv_base[2 * c + 1]);
+    } else {
+      float p[2];
+      chunk_dot<FMT>(R.w[j], xv_base + c * Fmt<FMT>::kCS, p);
       const float d = f16_to_f32(uint16_t(R.sc[j]));
       const float m = f16_to_f32(uint16_t(R.mn[j])) - 128.f * d;
-      uint32_t pr[16];
+      acc += d * p[0] + m * sv_base[c];
+    }
+  }
+  return acc;
+}
+
+// Gate and up rows . one vector in one pass (one set of LDS reads for both).
+template <int FMT, int NCH>
+__device__ __forceinline__ void row_pair_vec_dot(const RowRegs<FMT, NCH>& RG,
+                                                 const RowRegs<FMT, NCH>& RU, int nch, int lane_g,
+                                                 int lpr, const uint32_t* xv_base,
+                                                 const float* sv_base, float& g, float& u) {
+  if constexpr (FMT == MOE_W_F32) {
+    g = row_vec_dot<FMT, NCH>(RG, nch, lane_g, lpr, xv_base, sv_base);
+    u = row_vec_dot<FMT, NCH>(RU, nch, lane_g, lpr, xv_base, sv_base);
+  } else {
+    g = 0.f;
+    u = 0.f;
 #pragma unroll
-      for (int dw = 0; dw < 4; ++dw)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) pr[dw * 4 + s] = q4_pair(w[dw], s);
-#pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        if (v < n) {
-          const int id = vid ? vid[v] : v;
-          const u32x4* xv = reinterpret_cast<const u32x4*>(vec + id * vstride + c * Fmt<FMT>::kCS);
-          float p = 0.f;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const u32x4 xx = xv[q];
-            p = dot2_bf16(pr[q * 4 + 0], xx[0], p);
-            p = dot2_bf16(pr[q * 4 + 1], xx[1], p);
-            p = dot2_bf16(pr[q * 4 + 2], xx[2], p);
-            p = dot2_bf16(pr[q * 4 + 3], xx[3], p);
-          }
-          acc[v] += d * p + m * sums[id * sstride + c];
-        }
-      }
-    } else {
-      const float4 wf = __builtin_bit_cast(float4, w);
-      const float* vf = reinterpret_cast<const float*>(vec);
-#pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        if (v < n) {
-          const float* xv = vf + (vid ? vid[v] : v) * vstride + 4 * c;
-          acc[v] = fmaf(wf.x, xv[0], fmaf(wf.y, xv[1], fmaf(wf.z, xv[2], fmaf(wf.w, xv[3], acc[v]))));
-        }
+    for (int j = 0; j < NCH; ++j) {
+      if (j >= nch) continue;
+      const int c = lane_g + j * lpr;
+      const uint32_t* xv = xv_base + c * Fmt<FMT>::kCS;
+      float pg[2], pu[2];
+      chunk_dot2<FMT>(RG.w[j], RU.w[j], xv, pg, pu);
+      if constexpr (FMT == MOE_W_Q2B32) {
+        const float s0 = sv_base[2 * c], s1 = sv_base[2 * c + 1];
+        const float dg0 = f16_to_f32(uint16_t(RG.sc[j] & 0xFFFFu));
+        const float dg1 = f16_to_f32(uint16_t(RG.sc[j] >> 16));
+        const float du0 = f16_to_f32(uint16_t(RU.sc[j] & 0xFFFFu));
+        const float du1 = f16_to_f32(uint16_t(RU.sc[j] >> 16));
+        g += (dg0 * pg[0] + (f16_to_f32(uint16_t(RG.mn[j] & 0xFFFFu)) - 128.f * dg0) * s0) +
+             (dg1 * pg[1] + (f16_to_f32(uint16_t(RG.mn[j] >> 16)) - 128.f * dg1) * s1);
+        u += (du0 * pu[0] + (f16_to_f32(uint16_t(RU.mn[j] & 0xFFFFu)) - 128.f * du0) * s0) +
+             (du1 * pu[1] + (f16_to_f32(uint16_t(RU.mn[j] >> 16)) - 128.f * du1) * s1);
+      } else {
+        const float s0 = sv_base[c];
+        const float dg = f16_to_f32(uint16_t(RG.sc[j])), du = f16_to_f32(uint16_t(RU.sc[j]));
+        g += dg * pg[0] + (f16_to_f32(uint16_t(RG.mn[j])) - 128.f * dg) * s0;
+        u += du * pu[0] + (f16_to_f32(uint16_t(RU.mn[j])) - 128.f * du) * s0;
       }
     }
   }
@@ -438,12 +490,14 @@ __host__ __device__ __forceinline__ int chunks_of(int K) {
   return FMT == MOE_W_F32 ? K / 4 : K / Fmt<FMT>::kWPC;
 }
 
-// gate/up + SwiGLU for 8 rows (one per lane group) of one expert.
+// gate/up + SwiGLU for one row per lane group (64 / LPR rows per wave) of
+// one expert, for its n tokens; h[t] goes to out[ids(t)][i] (ids = pair ids,
+// or the tokens themselves when ids is null).
 template <int FMT>
 __device__ __forceinline__ void gateup_task(const LayerArgs& a, const MatView& G, const MatView& U,
                                             int slot, int i, int n, const int* vid,
-                                            const uint32_t* xs, const float* xsum, int vstride,
-                                            int lane_g, float (&h)[kTMax]) {
+                                            const int* ids, float* out, const uint32_t* xs,
+                                            const float* xsum, int vstride, int lane_g) {
   constexpr int kLprGU = Lanes<FMT>::kGU;
   const int K = a.H, sstride = K / 32;
   const int nch = chunks_of<FMT>(K) / kLprGU;
@@ -454,18 +508,14 @@ __device__ __forceinline__ void gateup_task(const LayerArgs& a, const MatView& G
                          G.mn + blk, nch, lane_g, kLprGU);
   load_row<FMT, kNChMax>(ru, U.codes + slot * U.mat_bytes + i * row_bytes, U.scale + blk,
                          U.mn + blk, nch, lane_g, kLprGU);
-  float ag[kTMax], au[kTMax];
-#pragma unroll
-  for (int t = 0; t < kTMax; ++t) ag[t] = au[t] = 0.f;
-  dot_row<FMT, kNChMax, kTMax>(rg, nch, lane_g, kLprGU, xs, vstride, xsum, sstride, n, vid, ag);
-  dot_row<FMT, kNChMax, kTMax>(ru, nch, lane_g, kLprGU, xs, vstride, xsum, sstride, n, vid, au);
-#pragma unroll
-  for (int t = 0; t < kTMax; ++t) {
-    if (t < n) {
-      const float g = group_sum<kLprGU>(ag[t]);
-      const float u = group_sum<kLprGU>(au[t]);
-      h[t] = silu_f32(g) * u;
-    }
+  for (int v = 0; v < n; ++v) {
+    const int id = vid ? vid[v] : v;
+    float g, u;
+    row_pair_vec_dot<FMT, kNChMax>(rg, ru, nch, lane_g, kLprGU, xs + id * vstride,
+                                   xsum + id * sstride, g, u);
+    g = group_sum<kLprGU>(g);
+    u = group_sum<kLprGU>(u);
+    if (lane_g == 0) st_dev(out + int64_t(ids ? ids[v] : v) * a.I + i, silu_f32(g) * u);
   }
 }
 
@@ -519,10 +569,10 @@ __device__ __forceinline__ void router_task(const LayerArgs& a, int task, const 
         for (int t = 0; t < kTMax; ++t) {
           if (t < a.T) {
             const uint32_t* xv = xs + t * vstride + c * Fmt<FMT>::kCS;
-            float s = acc[t];
+            float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < kG * kS; ++j) s = dot2_bf16(pr[j], xv[j], s);
-            acc[t] = s;
+            for (int j = 0; j < kG * kS; ++j) s4[j & 3] = dot2_bf16(pr[j], xv[j], s4[j & 3]);
+            acc[t] += (s4[0] + s4[1]) + (s4[2] + s4[3]);
           }
         }
       }
@@ -585,12 +635,8 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs a) {
         router_task<FMT>(a, task, xs, vstride, lane);
       } else {
         const int i = (task - n_router) * kRowsGU + lane / kLprGU;
-        float h[kTMax];
-        gateup_task<FMT>(a, a.sg, a.su, 0, i, T, nullptr, xs, xsum, vstride, lane % kLprGU, h);
-        if (lane % kLprGU == 0)
-#pragma unroll
-          for (int t = 0; t < kTMax; ++t)
-            if (t < T) st_dev(a.h_sh + t * a.I + i, h[t]);
+        gateup_task<FMT>(a, a.sg, a.su, 0, i, T, nullptr, nullptr, a.h_sh, xs, xsum, vstride,
+                         lane % kLprGU);
       }
     }
     for (int i = b * kThreads + tid; i < T * K; i += G * kThreads) st_dev(a.y + i, 0.f);
@@ -701,13 +747,8 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs a) {
       const int i = (task % tasks_per_expert) * kRowsGU + lane / kLprGU;
       const int st = L.act_start[u];
       const int n = L.act_start[u + 1] - st;
-      float h[kTMax];
-      gateup_task<FMT>(a, a.g, a.u, L.act_slot[u], i, n, L.tok + st, xs, xsum, vstride,
-                       lane % kLprGU, h);
-      if (lane % kLprGU == 0)
-#pragma unroll
-        for (int t = 0; t < kTMax; ++t)
-          if (t < n) st_dev(a.h + int64_t(L.bpair[st + t]) * a.I + i, h[t]);
+      gateup_task<FMT>(a, a.g, a.u, L.act_slot[u], i, n, L.tok + st, L.bpair + st, a.h, xs, xsum,
+                       vstride, lane % kLprGU);
       wait_mem();
       if (lane == 0) st_dev(task_flag + u * tasks_per_expert + task % tasks_per_expert, epoch);
     }
@@ -751,21 +792,17 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs a) {
       __syncthreads();
       stage_h<FMT>(srcs, n, Kd, xd, sd, pd, vs_d);
       __syncthreads();
-      float acc[2 * kTMax];
-#pragma unroll
-      for (int v = 0; v < 2 * kTMax; ++v) acc[v] = 0.f;
-      dot_row<FMT, kNChMax, 2 * kTMax>(rd, nch, lane_g, kLprD, xd, vs_d, sd, ss_d, n * kVPP,
-                                        nullptr, acc);
-#pragma unroll
-      for (int v = 0; v < kTMax; ++v) {
-        if (v < n) {
-          float o = group_sum<kLprD>(acc[kVPP * v]);
-          if (kVPP == 2) o += group_sum<kLprD>(acc[kVPP * v + 1]);
-          if (r < a.H && lane_g == 0) {
-            const int t = shared ? v : L.tok[st + v];
-            const float g = shared ? 1.f : L.gate[L.bpair[st + v]];
-            fadd_dev(a.y + int64_t(t) * a.H + r, g * o);
-          }
+      for (int v = 0; v < n; ++v) {
+        float o = row_vec_dot<FMT, kNChMax>(rd, nch, lane_g, kLprD, xd + (kVPP * v) * vs_d,
+                                            sd + (kVPP * v) * ss_d);
+        if (kVPP == 2)
+          o += row_vec_dot<FMT, kNChMax>(rd, nch, lane_g, kLprD, xd + (kVPP * v + 1) * vs_d,
+                                         sd + (kVPP * v + 1) * ss_d);
+        o = group_sum<kLprD>(o);
+        if (r < a.H && lane_g == 0) {
+          const int t = shared ? v : L.tok[st + v];
+          const float g = shared ? 1.f : L.gate[L.bpair[st + v]];
+          fadd_dev(a.y + int64_t(t) * a.H + r, g * o);
         }
       }
     }
