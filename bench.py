@@ -181,6 +181,139 @@ def bench_decode(args, cfg_name):
     return out
 
 
+def gemm_flops(cfg, n_hit, T):
+    """Algorithmic MFMA flops of the expert FFN: 2*H*I for each of gate, up
+    and down, per hit pair and per token of the shared expert (no padding)."""
+    per = 6 * cfg.H * cfg.I
+    return per * (n_hit + (T if cfg.shared else 0))
+
+
+def cpu_baseline_prefill(cfg, n_route, n_ffn):
+    """Oracle on a bounded sample of the prefill layer: routing of n_route
+    tokens and the FFN + combine of n_ffn of them; tokens/s extrapolated
+    from the per-token times (input generation untimed)."""
+    import oracle
+    import synth
+    x = synth.gen_x_rows(cfg, 0, np.arange(n_route))
+    W = synth.gen_router(cfg, 0)
+    bias = synth.gen_bias(cfg, 0)
+    t0 = time.perf_counter()
+    logits = oracle.router(x, W, cfg.router_fmt, bias)
+    idx, gate = oracle.topk(logits, cfg.k)
+    slot_idx, *_ = oracle.resolve(idx, gate, cfg.E, None)
+    oracle.bucket(slot_idx, cfg.E)
+    t_route = (time.perf_counter() - t0) / n_route
+    experts = {int(e): synth.gen_expert(cfg, 0, int(e)) for e in np.unique(idx[:n_ffn])}
+    shared = synth.gen_expert(cfg, 0, synth.SHARED_ID) if cfg.shared else None
+    t0 = time.perf_counter()
+    for t in range(n_ffn):
+        po = np.stack([oracle.ffn(cfg.wfmt, cfg.H, cfg.I, experts[int(e)], x[t:t + 1])[0]
+                       for e in idx[t]])
+        sh = oracle.ffn(cfg.wfmt, cfg.H, cfg.I, shared, x[t:t + 1]) if shared else None
+        oracle.combine(slot_idx[t:t + 1], gate[t:t + 1], po, sh)
+    t_ffn = (time.perf_counter() - t0) / n_ffn
+    return 1.0 / (t_route + t_ffn), t_route * n_route + t_ffn * n_ffn
+
+
+def bench_prefill(args, cfg_name):
+    import torch
+    import routed_expert_ffn_gemv_amd as moe
+    import synth
+    from synth import device as sdev
+    cfg = synth.CONFIGS[cfg_name]
+    T, k, H, E = cfg.T, cfg.k, cfg.H, cfg.E
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    log(f"[bench] {cfg.name}: building the layer ({T} tokens)")
+    t0 = time.time()
+    inp = sdev.layer_inputs(cfg, 0, dev)
+    pool = sdev.expert_pool(cfg, [0] * E, list(range(E)), dev)
+    desc = moe.LayerDesc(E, k, H, cfg.I, inp["router_w"], cfg.router_fmt, cfg.wfmt, pool,
+                         shared=inp["shared"], router_bias=inp["bias"])
+    ws = moe.workspace(desc, T, dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    idx = torch.empty((T, k), **i32)
+    gate = torch.empty((T, k), dtype=torch.float32, device=dev)
+    slot_idx = torch.empty((T, k), **i32)
+    boff = torch.empty((E + 1,), **i32)
+    bpair = torch.empty((T * k,), **i32)
+    miss = torch.empty((T * k * 3,), **i32)
+    moff = torch.empty((T + 1,), **i32)
+    pair_out = torch.empty((T * k, H), dtype=torch.float32, device=dev)
+    shared_out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] setup {time.time() - t0:.1f}s")
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    x = inp["x"]
+
+    def step(times=None):
+        if times is not None:
+            ev[0].record(stream)
+        moe.moe_route(desc, x, T, idx, gate, ws, stream)
+        if times is not None:
+            ev[1].record(stream)
+        moe.moe_resolve_slots(desc, idx, gate, T, slot_idx, boff, bpair, miss, moff, ws, stream)
+        if times is not None:
+            ev[2].record(stream)
+        moe.moe_expert_ffn(desc, x, T, boff, bpair, pair_out, shared_out, ws, stream)
+        if times is not None:
+            ev[3].record(stream)
+        moe.moe_combine(desc, T, slot_idx, gate, pair_out, shared_out, y, stream)
+        if times is not None:
+            ev[4].record(stream)
+            torch.cuda.synchronize()
+            times.append([ev[i].elapsed_time(ev[i + 1]) for i in range(4)])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    parts = []
+    for _ in range(3):
+        step(parts)
+    parts = np.median(np.array(parts), axis=0)
+    n_hit = int(boff[-1].item())
+    flops = gemm_flops(cfg, n_hit, T)
+    ffn_ms = float(parts[2])
+    tflops = flops / (ffn_ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "q4 weights dequantised to fp16 tiles, fp16 MFMA, fp32 accumulation",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "E": E, "k": k, "H": H, "I": cfg.I, "T": T,
+                   "weights": cfg.wfmt, "shared_expert": cfg.shared,
+                   "step": "moe_route + moe_resolve_slots + moe_expert_ffn + moe_combine"},
+        "ms_route": round(float(parts[0]), 4), "ms_resolve": round(float(parts[1]), 4),
+        "ms_expert_ffn": round(ffn_ms, 4), "ms_combine": round(float(parts[3]), 4),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "moe_expert_ffn (grouped gate/up + down GEMMs)",
+                     "flops_per_launch": int(flops)},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline: oracle on a sample")
+        tps, el = cpu_baseline_prefill(cfg, 512, 4)
+        out["cpu_baseline"] = {"value": round(tps, 3), "unit": "tokens/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"routing of 512 tokens + FFN/combine of 4 tokens of "
+                                         f"{cfg.name}, extrapolated per token (fp64, one thread, "
+                                         f"{el:.1f}s)"}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -194,7 +327,7 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
-    out = bench_decode(args, args.config)
+    out = bench_prefill(args, "c5") if args.config == "c5" else bench_decode(args, args.config)
     print(json.dumps(out), flush=True)
 
 

@@ -209,13 +209,15 @@ def layer(x, router_w, router_fmt, bias, k, fmt, pools, I, slot_of=None, shared=
             "bucket_off": boff, "bucket_pair": bpair[: int(boff[S])].copy()}
 
 
-def route_from_synth(cfg, layer_id, x, slot_of=None, num_slots=None):
+def route_from_synth(cfg, layer_id, x, slot_of=None, num_slots=None, threads=1):
     """Oracle routing of one layer of a synthetic config: logits, top-k,
-    gates, slot resolution, miss list and buckets (all in liboracle.so)."""
+    gates, slot resolution, miss list and buckets (all in liboracle.so;
+    threads > 1 splits the router rows over threads)."""
     import synth
     W = synth.gen_router(cfg, layer_id)
     bias = synth.gen_bias(cfg, layer_id)
-    logits = router(x, W, cfg.router_fmt, bias)
+    logits = (router_threads(x, W, cfg.router_fmt, bias, threads) if threads > 1
+              else router(x, W, cfg.router_fmt, bias))
     idx, gate = topk(logits, cfg.k)
     S = num_slots if num_slots is not None else cfg.E
     slot_idx, me, mt, mg, moff = resolve(idx, gate, cfg.E, slot_of)
@@ -226,15 +228,16 @@ def route_from_synth(cfg, layer_id, x, slot_of=None, num_slots=None):
 
 
 def layer_from_synth(cfg, layer_id, x, slot_of=None, num_slots=None, tokens=None,
-                     with_misses=False):
+                     with_misses=False, route=None, threads=1):
     """Oracle outputs of one layer of a synthetic config.
 
     Routing covers every token of x; the FFN and combine cover `tokens`
     (default: all).  Each expert's weights are regenerated by synth on the
     host.  with_misses also returns y_full, where missed experts are added
-    as if they were resident."""
+    as if they were resident.  route: a result of route_from_synth to reuse."""
     import synth
-    r = route_from_synth(cfg, layer_id, x, slot_of, num_slots)
+    r = dict(route) if route is not None else route_from_synth(cfg, layer_id, x, slot_of,
+                                                                num_slots, threads)
     T = x.shape[0]
     k, H, I = cfg.k, cfg.H, cfg.I
     tokens = np.arange(T) if tokens is None else np.asarray(tokens)

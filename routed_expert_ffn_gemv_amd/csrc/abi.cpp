@@ -19,6 +19,8 @@ constexpr int kMaxI = 4096;
 constexpr int kMaxSlots = 16384;
 constexpr int64_t kMaxT = int64_t(1) << 22;
 constexpr size_t kAlign = 256;
+constexpr int kRouterGemmMinT = 256;       // tokens from which the router runs on MFMA
+constexpr int64_t kFfnGemmMinPairs = 2048; // pairs from which the FFN runs as grouped GEMMs
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -61,7 +63,8 @@ moe_status check_desc(const moe_layer_desc* d) {
 //   slotbuf [T*k] int32 (moe_layer's slot_idx when the caller passes none)
 //   pairbuf [T*k][H] fp32 + sharedbuf [T][H] fp32 (moe_layer only, T <= 16)
 //   bucket  off[S+1] + pair[T*k] (moe_layer only)
-//   h       [T*k + T][I] fp32 (GEMV path) -- or the grouped-GEMM workspace
+//   h       [T*k + T][I] fp32 (GEMV path), or the grouped-GEMM tile list and
+//           fp16 h (GEMM path): the larger of the two
 //   resolve large-path counters
 struct WsLayout {
   size_t sync, logits, active, slotbuf, pairbuf, sharedbuf, bucket, h, resolve, total;
@@ -89,7 +92,9 @@ WsLayout layout(const moe_layer_desc* d, int64_t T) {
   w.bucket = o;
   o += layer_sized ? up(size_t(d->num_slots + 1 + P) * 4) : 0;
   w.h = o;
-  o += up(size_t(P + T) * d->I * 4);
+  const size_t h_gemv = size_t(P + T) * d->I * 4;
+  const size_t h_gemm = ffn_gemm_ws(int(T), d->k, d->H, d->I, d->num_slots);
+  o += up(h_gemv > h_gemm ? h_gemv : h_gemm);
   w.resolve = o;
   o += up(resolve_large_ws(int(T), d->k, d->num_slots));
   w.total = o;
@@ -141,8 +146,12 @@ FfnArgs ffn_args(const moe_layer_desc* d, const uint16_t* x, int T) {
 moe_status run_route(const moe_layer_desc* d, const uint16_t* x, int T, int32_t* idx, float* gate,
                      void* ws, const WsLayout& w, hipStream_t st) {
   float* logits = at<float>(ws, w.logits);
-  hipError_t e = launch_router(x, T, d->H, d->E, d->router_fmt, d->router_w, d->router_bias,
-                               logits, st);
+  hipError_t e;
+  if (T >= kRouterGemmMinT && d->router_fmt == MOE_W_BF16 && d->H % 64 == 0)
+    e = launch_router_mfma(x, T, d->H, d->E, static_cast<const uint16_t*>(d->router_w),
+                           d->router_bias, logits, st);
+  else
+    e = launch_router(x, T, d->H, d->E, d->router_fmt, d->router_w, d->router_bias, logits, st);
   if (e == hipSuccess) e = launch_topk(logits, T, d->E, d->k, idx, gate, st);
   return device_status(e);
 }
@@ -242,7 +251,12 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const uint16_t* x, int32_t
   a.pair_out = pair_out;
   a.shared_out = shared_out;
   hipError_t e = launch_active_from_offsets(desc->num_slots, bucket_off, a.act, st);
-  if (e == hipSuccess) e = launch_ffn_gemv(a, st);
+  if (e == hipSuccess) {
+    if (int64_t(T) * desc->k >= kFfnGemmMinPairs && ffn_gemm_ok(a.fmt, desc->H, desc->I))
+      e = launch_ffn_gemm(a, desc->num_slots, bucket_off, at<void>(ws, w.h), st);
+    else
+      e = launch_ffn_gemv(a, st);
+  }
   return device_status(e);
 }
 
