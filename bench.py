@@ -314,6 +314,19 @@ def bench_prefill(args, cfg_name):
     return out
 
 
+def copy_probe(mib):
+    """A plain copy of mib MiB: reads and writes exactly mib MiB of HBM."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -323,10 +336,15 @@ def main():
     ap.add_argument("--layers", type=int, default=48)
     ap.add_argument("--cpu-tokens", type=int, default=12)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="first run a plain device-to-device copy of MIB MiB (3 times): the "
+                         "known-size kernel that scales the HBM byte counters of a profile")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
     out = bench_prefill(args, "c5") if args.config == "c5" else bench_decode(args, args.config)
     print(json.dumps(out), flush=True)
 

@@ -57,7 +57,9 @@ moe_status check_desc(const moe_layer_desc* d) {
 }
 
 // Workspace regions (each 256-byte aligned), in this order:
-//   sync    cross-workgroup flags of the fused moe_layer (layer_sync_bytes)
+//   layer   hand-off region of the fused moe_layer (layer_region_bytes;
+//           sized from the layer shape alone, so it sits at the same place
+//           for every T)
 //   logits  [T][E] fp32
 //   active  slot[cap], start[cap+1], count[1]
 //   slotbuf [T*k] int32 (moe_layer's slot_idx when the caller passes none)
@@ -67,7 +69,7 @@ moe_status check_desc(const moe_layer_desc* d) {
 //           fp16 h (GEMM path): the larger of the two
 //   resolve large-path counters
 struct WsLayout {
-  size_t sync, logits, active, slotbuf, pairbuf, sharedbuf, bucket, h, resolve, total;
+  size_t layer, logits, active, slotbuf, pairbuf, sharedbuf, bucket, h, resolve, total;
   int cap;
 };
 
@@ -76,8 +78,8 @@ WsLayout layout(const moe_layer_desc* d, int64_t T) {
   const int64_t P = T * d->k;
   w.cap = int(P < d->num_slots ? P : d->num_slots);
   size_t o = 0;
-  w.sync = o;
-  o += up(layer_sync_bytes(w.cap, d->I));
+  w.layer = o;
+  o += up(layer_region_bytes(d->E, d->k, d->I));
   w.logits = o;
   o += up(size_t(T) * d->E * 4);
   w.active = o;
@@ -305,30 +307,29 @@ moe_status moe_layer(const moe_layer_desc* desc, const uint16_t* x, int32_t T, f
     L.H = desc->H;
     L.I = desc->I;
     L.S = desc->num_slots;
-    L.fmt = fmt;
     L.rfmt = desc->router_fmt;
+    L.has_sh = has_shared(desc) ? 1 : 0;
     L.W = desc->router_w;
     L.bias = desc->router_bias;
     L.slot_of = desc->slot_of_expert;
     const FfnArgs f = ffn_args(desc, x, T);
-    L.g = f.g;
-    L.u = f.u;
-    L.d = f.d;
-    L.sg = f.sg;
-    L.su = f.su;
-    L.sd = f.sd;
-    L.has_sh = has_shared(desc) ? 1 : 0;
+    auto planes = [](const MatView& v) { return Planes{v.codes, v.scale, v.mn}; };
+    L.g = planes(f.g);
+    L.u = planes(f.u);
+    L.d = planes(f.d);
+    L.sg = planes(f.sg);
+    L.su = planes(f.su);
+    L.sd = planes(f.sd);
+    L.mat_bytes = f.g.mat_bytes;     // the same for all six: I x H weights each
+    L.mat_blocks = f.g.mat_blocks;
     L.y = y;
     L.idx = topk_idx;
     L.gate = topk_gate;
     L.slot_idx = slot_idx;
     L.miss = miss;
     L.miss_off = miss_off;
-    L.logits = at<float>(ws, w.logits);
-    L.h = at<float>(ws, w.h);
-    L.h_sh = L.h + size_t(T) * desc->k * desc->I;
-    L.sync = at<uint32_t>(ws, w.sync);
-    return device_status(launch_layer_fused(L, st, nullptr));
+    L.region = at<uint8_t>(ws, w.layer);
+    return device_status(launch_layer_fused(L, fmt, st, nullptr));
   }
   int32_t* sl = slot_idx ? slot_idx : at<int32_t>(ws, w.slotbuf);
   s = run_route(desc, x, T, topk_idx, topk_gate, ws, w, st);

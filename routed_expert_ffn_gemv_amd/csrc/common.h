@@ -56,12 +56,24 @@ __device__ __forceinline__ uint32_t ordered_bits(float f) {
 
 __device__ __forceinline__ float silu_f32(float a) { return a / (1.0f + __expf(-a)); }
 
+// Lane v's value moved by a DPP row permutation (every source lane valid).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
 // Sum over aligned groups of G lanes (G a power of two, <= 64); every lane
-// of the group receives the group sum.
+// of the group receives the group sum.  Within a row of 16 lanes the steps
+// are DPP permutations (quads, then the other quad of the half row, then
+// the other half row); wider groups add lane shuffles.
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
+  if constexpr (G >= 2) v += dpp_f32<0xB1>(v);    // quad_perm [1,0,3,2]
+  if constexpr (G >= 4) v += dpp_f32<0x4E>(v);    // quad_perm [2,3,0,1]
+  if constexpr (G >= 8) v += dpp_f32<0x141>(v);   // row_half_mirror
+  if constexpr (G >= 16) v += dpp_f32<0x140>(v);  // row_mirror
 #pragma unroll
-  for (int m = 1; m < G; m <<= 1) v += __shfl_xor(v, m, kWave);
+  for (int m = 16; m < G; m <<= 1) v += __shfl_xor(v, m, kWave);
   return v;
 }
 

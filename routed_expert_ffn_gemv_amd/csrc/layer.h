@@ -5,27 +5,49 @@
 
 namespace moe {
 
-// Cross-workgroup bookkeeping of the fused layer, in 32-bit words at the
-// start of the workspace (a region no other call touches).  It must be zero
-// before the first call on a workspace.  Word 0 counts calls; every other
-// word is a flag that holds the number of the call that last set it, so
-// nothing has to be cleared between calls.
-constexpr int kSyncCalls = 0;
-constexpr int kSyncArrive = 1024;       // one word per workgroup (<= 1024)
-constexpr int kSyncTasks = 2048;        // one word per gate/up task
-constexpr size_t layer_sync_bytes(int max_active, int I) {
-  return size_t(kSyncTasks) * 4 + size_t(max_active) * (I / 4) * 4;
+// Hand-off region of the fused layer, at the start of the workspace, sized
+// from the layer shape only (never from T) so that every call on one
+// workspace finds it at the same place.  It must be zero before the first
+// call.  Word 0 counts calls.  Every other entry is a 64-bit word {value,
+// call number}: a workgroup publishes a value together with the number of
+// the call that made it in one store, and a reader knows the value is
+// current when the number matches -- no separate flag, no reset.
+//   [0, 256)           call counter (uint32)
+//   arrive [1024]      one tagged word per workgroup
+//   logits [16][E]     tagged router logits
+//   h      [hrows][I]  tagged SwiGLU activations: pairs first, then the
+//                      shared expert's rows (one per token)
+constexpr int kLayerMaxGrid = 1024;
+constexpr int kLayerMaxPairs = 256;
+__host__ __device__ inline int layer_h_rows(int k) {
+  const int p = MOE_LAYER_MAX_T * k;
+  return (p < kLayerMaxPairs ? p : kLayerMaxPairs) + MOE_LAYER_MAX_T;
+}
+inline size_t layer_region_bytes(int E, int k, int I) {
+  return 256 + size_t(kLayerMaxGrid) * 8 + size_t(MOE_LAYER_MAX_T) * E * 8 +
+         size_t(layer_h_rows(k)) * I * 8;
 }
 
+// Data planes of one expert matrix pool (sizes are common to all six).
+struct Planes {
+  const uint8_t* codes;    // Q formats: codes; F32: fp32 data as bytes
+  const uint16_t* scale;
+  const uint16_t* mn;
+};
+
+// Kernel arguments, kept small: every field lives in scalar registers for
+// the whole launch.
 struct LayerArgs {
   const uint16_t* x;
-  int T, E, k, H, I, S, fmt;
+  int T, E, k, H, I, S;
   int rfmt;
+  int has_sh;
   const void* W;
   const float* bias;
   const int32_t* slot_of;
-  MatView g, u, d, sg, su, sd;
-  int has_sh;
+  Planes g, u, d, sg, su, sd;
+  int64_t mat_bytes;       // bytes of one matrix's data plane
+  int64_t mat_blocks;      // 32-weight blocks of one matrix
   // outputs
   float* y;
   int32_t* idx;
@@ -33,15 +55,11 @@ struct LayerArgs {
   int32_t* slot_idx;       // may be null
   moe_miss* miss;
   int32_t* miss_off;
-  // workspace
-  float* logits;           // [T][E]
-  float* h;                // [T*k][I]
-  float* h_sh;             // [T][I]
-  uint32_t* sync;          // kSyncWords
+  uint8_t* region;         // hand-off region (layout above)
 };
 
 bool layer_fused_ok(int fmt, int T, int k, int E, int H, int I);
 size_t layer_fused_lds(int fmt, int T, int E, int H, int I);
-hipError_t launch_layer_fused(const LayerArgs& a, hipStream_t st, int* grid);
+hipError_t launch_layer_fused(const LayerArgs& a, int fmt, hipStream_t st, int* grid);
 
 }  // namespace moe

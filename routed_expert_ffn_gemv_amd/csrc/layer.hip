@@ -14,28 +14,32 @@
 //
 // A decode layer moves ~21.6 MB in a dependent chain (router -> top-k ->
 // gate/up -> down -> sum).  At ~1-2 us per HBM round trip the chain, not the
-// bandwidth, sets the time, so it runs in one launch and every step issues
-// all of its loads before it consumes any:
-//  A  stage the tokens in LDS; router rows and shared-expert gate/up rows
-//     (independent of the routing); zero y; grid barrier (each workgroup
-//     stores its arrival, every workgroup polls all arrivals);
-//  B  every workgroup reads all logits and takes the routing decisions
-//     itself (top-k, gates, slots, miss list, buckets) -- the same
-//     deterministic result everywhere, so nothing has to be broadcast;
+// bandwidth, sets the time, so it runs in one launch, every step issues all
+// of its loads before it consumes any, and each hand-off between
+// workgroups costs one round trip:
+//  A  each wave issues the loads of its first task (router rows, or
+//     shared-expert gate/up rows: neither depends on the routing) before the
+//     tokens are staged in LDS; router waves zero their share of y first.
+//     Logits and shared h are published as tagged words (below);
+//  B  every workgroup polls all logits (and one arrival word per
+//     workgroup) until they carry this call's number, then takes the
+//     routing decisions itself (top-k, gates, slots, miss list, buckets) --
+//     the same deterministic result everywhere, so nothing is broadcast;
 //     workgroup 0 writes the routing outputs;
-//  C  routed gate/up + SwiGLU, a few rows of one expert per wave task; each
-//     task raises its own flag when its rows of h are out;
-//  D  down projection units (expert, block of rows): the unit loads its
-//     weight rows, then waits for its expert's task flags, stages h, and adds
-//     gate * output into y with device-scope float atomics (the shared
-//     expert adds with weight 1).  The summation order over experts is not
-//     fixed, so y may differ from run to run in the last bits.
-// The grid never exceeds the number of workgroups the device holds at once,
-// so every workgroup a wait depends on is running.  Data one workgroup hands
-// to another goes through device-scope (sc1) loads and stores, which bypass
-// the per-XCD L2 caches; a wave waits for its own stores (s_waitcnt) before
-// the flag that publishes them, so no cache-wide write-back or invalidate
-// is needed, and flags carry the call number so none is ever reset.
+//  C  the workgroup's first down unit issues its weight loads; routed
+//     gate/up + SwiGLU, a few rows of one expert per wave task, publishes
+//     tagged h;
+//  D  down units (expert, block of rows) poll their expert's h, stage it
+//     and add gate * output into y with device-scope float atomics (the
+//     shared expert adds with weight 1).  The summation order over experts
+//     is not fixed, so y may differ from run to run in the last bits.
+// Hand-offs are 64-bit words {value, call number} written with one store:
+// a reader that sees this call's number has the value, so no flag, fence
+// or reset is needed (this is the flag-in-data idea of low-latency
+// collective protocols).  Loads and stores of them are device-scope (sc1),
+// which bypasses the per-XCD L2 caches.  The grid never exceeds the
+// workgroups the device holds at once, so every producer a poll waits for
+// is running, and no producer waits on anything.
 #include "gemv_core.h"
 #include "kernels.h"
 #include "layer.h"
@@ -47,7 +51,8 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kTMax = MOE_LAYER_MAX_T;
-constexpr int kPMax = 256;
+constexpr int kPMax = kLayerMaxPairs;
+constexpr int kEMax = 1024;
 constexpr int kNChMax = 4;                      // 16-byte chunks per lane and weight row
 
 // Lanes per weight row: a lane holds at most 2 (Q2) or 4 (Q4) chunks of a
@@ -82,26 +87,83 @@ __device__ __forceinline__ u32x4 fresh(u32x4 w) {
 // Wait until this wave's memory operations have completed.
 __device__ __forceinline__ void wait_mem() { __builtin_amdgcn_s_waitcnt(0); }
 
-// 64-bit wave maximum with DPP row operations; every lane gets the result.
-__device__ __forceinline__ uint64_t wave_max_u64_dpp(uint64_t v) {
-#define MOE_DPP_STEP(ctrl, rmask)                                                              \
-  {                                                                                            \
-    const uint32_t lo = uint32_t(v), hi = uint32_t(v >> 32);                                   \
-    const uint32_t olo = __builtin_amdgcn_update_dpp(lo, lo, ctrl, rmask, 0xF, false);         \
-    const uint32_t ohi = __builtin_amdgcn_update_dpp(hi, hi, ctrl, rmask, 0xF, false);         \
-    const uint64_t o = (uint64_t(ohi) << 32) | olo;                                            \
-    v = o > v ? o : v;                                                                         \
+// Parts of the hand-off region.
+__device__ __forceinline__ uint32_t* region_calls(const LayerArgs& a) {
+  return reinterpret_cast<uint32_t*>(a.region);
+}
+__device__ __forceinline__ uint64_t* region_arrive(const LayerArgs& a) {
+  return reinterpret_cast<uint64_t*>(a.region + 256);
+}
+__device__ __forceinline__ uint64_t* region_lg(const LayerArgs& a) {
+  return region_arrive(a) + kLayerMaxGrid;
+}
+__device__ __forceinline__ uint64_t* region_h(const LayerArgs& a) {
+  return region_lg(a) + kTMax * a.E;
+}
+__device__ __forceinline__ uint64_t* region_h_sh(const LayerArgs& a) {
+  return region_h(a) + int64_t(layer_h_rows(a.k) - kTMax) * a.I;
+}
+
+// Tagged words: value bits low, call number high.
+__device__ __forceinline__ uint64_t tag_word(float v, uint32_t epoch) {
+  return (uint64_t(epoch) << 32) | __float_as_uint(v);
+}
+__device__ __forceinline__ bool tag_ok(uint64_t w, uint32_t epoch) {
+  return uint32_t(w >> 32) == epoch;
+}
+__device__ __forceinline__ float tag_val(uint64_t w) { return __uint_as_float(uint32_t(w)); }
+
+// Wave reductions: DPP steps within quads, half rows and rows of 16 lanes
+// (fused into the max/add), then the four row results read as scalars.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_mov_dpp(int(v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = max(v, dpp_u32<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = max(v, dpp_u32<0x141>(v));   // row_half_mirror
+  v = max(v, dpp_u32<0x140>(v));   // row_mirror
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 47), r3 = __builtin_amdgcn_readlane(v, 63);
+  return max(max(r0, r1), max(r2, r3));
+}
+__device__ __forceinline__ float wave_sum_f32(float f) {
+  f += __uint_as_float(dpp_u32<0xB1>(__float_as_uint(f)));
+  f += __uint_as_float(dpp_u32<0x4E>(__float_as_uint(f)));
+  f += __uint_as_float(dpp_u32<0x141>(__float_as_uint(f)));
+  f += __uint_as_float(dpp_u32<0x140>(__float_as_uint(f)));
+  const uint32_t v = __float_as_uint(f);
+  const float r0 = __uint_as_float(__builtin_amdgcn_readlane(v, 15));
+  const float r1 = __uint_as_float(__builtin_amdgcn_readlane(v, 31));
+  const float r2 = __uint_as_float(__builtin_amdgcn_readlane(v, 47));
+  const float r3 = __uint_as_float(__builtin_amdgcn_readlane(v, 63));
+  return (r0 + r1) + (r2 + r3);
+}
+
+// One selection round over the lanes' head keys (logit bits hv, ~expert
+// lo): the largest logit, and among equal logits the lowest expert id.
+// Keys are unique, so exactly one lane owns the winner.
+struct Pick {
+  uint32_t hv, lo;
+  int owner;
+};
+__device__ __forceinline__ Pick wave_pick(uint32_t hv, uint32_t lo) {
+  Pick p;
+  p.hv = wave_max_u32(hv);
+  uint64_t own = __ballot(hv == p.hv);
+  if (__popcll(own) > 1) {   // equal logits: the lowest expert id has the largest ~id
+    const uint32_t ml = wave_max_u32(hv == p.hv ? lo : 0u);
+    own = __ballot(hv == p.hv && lo == ml);
   }
-  MOE_DPP_STEP(0xB1, 0xF)    // quad_perm [1,0,3,2]
-  MOE_DPP_STEP(0x4E, 0xF)    // quad_perm [2,3,0,1]
-  MOE_DPP_STEP(0x141, 0xF)   // row_half_mirror
-  MOE_DPP_STEP(0x140, 0xF)   // row_mirror
-  MOE_DPP_STEP(0x142, 0xA)   // row_bcast:15
-  MOE_DPP_STEP(0x143, 0xC)   // row_bcast:31
-#undef MOE_DPP_STEP
-  const uint32_t lo = __builtin_amdgcn_readlane(uint32_t(v), 63);
-  const uint32_t hi = __builtin_amdgcn_readlane(uint32_t(v >> 32), 63);
-  return (uint64_t(hi) << 32) | lo;
+  p.owner = __ffsll(static_cast<unsigned long long>(own)) - 1;
+  p.lo = __builtin_amdgcn_readlane(lo, p.owner);
+  return p;
+}
+
+// Logit of an order-preserving key.
+__device__ __forceinline__ float key_value(uint32_t ob) {
+  return __uint_as_float((ob & 0x80000000u) ? (ob & 0x7FFFFFFFu) : ~ob);
 }
 
 __device__ __forceinline__ void cas_desc(uint64_t& a, uint64_t& b) {
@@ -113,9 +175,8 @@ __device__ __forceinline__ void cas_desc(uint64_t& a, uint64_t& b) {
 // Top-k of one token's logits (LDS, E <= 64 * KPL) by one wave.  Keys are
 // (order-preserving logit bits << 32) | ~expert, unique, so the largest key
 // is the largest logit and, among equal logits, the lowest expert id.  Each
-// lane sorts its KPL keys once; each round takes the wave maximum of the
-// lane heads and the owning lane drops its head.  Lane j < k returns the
-// j-th choice.
+// lane sorts its KPL keys once; each round picks the best head (wave_pick)
+// and the owning lane drops it.  Lane j < k returns the j-th choice.
 template <int KPL>
 __device__ __forceinline__ void wave_topk(const float* l, int E, int k, int lane, int* e_out,
                                           float* v_out) {
@@ -154,17 +215,56 @@ __device__ __forceinline__ void wave_topk(const float* l, int E, int k, int lane
   int my_e = 0;
   float my_v = 0.f;
   for (int j = 0; j < k; ++j) {
-    const uint64_t m = wave_max_u64_dpp(key[0]);
-    const int e = int(~uint32_t(m));
-    const uint32_t ob = uint32_t(m >> 32);
+    const Pick pk = wave_pick(uint32_t(key[0] >> 32), uint32_t(key[0]));
     if (lane == j) {
-      my_e = e;
-      my_v = __uint_as_float((ob & 0x80000000u) ? (ob & 0x7FFFFFFFu) : ~ob);
+      my_e = int(~pk.lo);
+      my_v = key_value(pk.hv);
     }
-    if (lane == (e & 63)) {
+    if (lane == pk.owner) {
 #pragma unroll
       for (int i = 0; i < KPL - 1; ++i) key[i] = key[i + 1];
       key[KPL - 1] = 0ull;
+    }
+  }
+  *e_out = my_e;
+  *v_out = my_v;
+}
+
+// Top-k of one token over E <= 512 logits with every wave of the block:
+// wave w keeps the k best of experts [64w, 64w + 64) (one key per lane, no
+// sorting), then wave 0 picks the k best of those 8 sorted lists (two keys
+// per lane).  The same choices and order as wave_topk; k <= 16.  Lane j < k
+// of wave 0 returns the j-th choice.  Called by every thread of the block.
+constexpr int kTopkListMax = 16;
+__device__ __forceinline__ void block_topk_one(const float* l, int E, int k, int wave, int lane,
+                                               uint64_t* cand, int* e_out, float* v_out) {
+  {
+    const int e = wave * 64 + lane;
+    uint64_t key = e < E ? (uint64_t(ordered_bits(l[e])) << 32) | uint64_t(~uint32_t(e)) : 0ull;
+    for (int j = 0; j < k; ++j) {
+      const Pick pk = wave_pick(uint32_t(key >> 32), uint32_t(key));
+      if (lane == 0) cand[wave * kTopkListMax + j] = (uint64_t(pk.hv) << 32) | pk.lo;
+      if (lane == pk.owner) key = 0ull;
+    }
+  }
+  __syncthreads();
+  int my_e = 0;
+  float my_v = 0.f;
+  if (wave == 0) {
+    // lane = (list, pair of positions); each list is already descending
+    const int list = lane >> 3, pos = 2 * (lane & 7);
+    uint64_t k0 = pos < k ? cand[list * kTopkListMax + pos] : 0ull;
+    uint64_t k1 = pos + 1 < k ? cand[list * kTopkListMax + pos + 1] : 0ull;
+    for (int j = 0; j < k; ++j) {
+      const Pick pk = wave_pick(uint32_t(k0 >> 32), uint32_t(k0));
+      if (lane == j) {
+        my_e = int(~pk.lo);
+        my_v = key_value(pk.hv);
+      }
+      if (lane == pk.owner) {
+        k0 = k1;
+        k1 = 0ull;
+      }
     }
   }
   *e_out = my_e;
@@ -180,18 +280,22 @@ struct Lds {
   int tok[kPMax];        // their tokens
   int act_slot[kPMax];   // distinct hit slots, ascending
   int act_start[kPMax + 1];
+  int slot_of[kEMax];    // the slot table (when the layer has one)
+  uint64_t cand[8 * kTopkListMax];   // per-wave top-k lists of block_topk_one
+  int ptok[kPMax];       // token of each pair
   int tmp[32];
   int n_act;
-  uint32_t flag0;
+  uint32_t calls;
 };
 
 // --------------------------------------------------------------- staging
 // Tokens into the expert format's LDS layout, with 32-byte loads per
 // thread (16 columns of one token) issued before any is used.  psum holds
 // each 16-column group's sum; block sums add two groups in a fixed order.
+// The caller synchronises before reading xs or psum.
 template <int FMT>
 __device__ __forceinline__ void stage_tokens(const uint16_t* __restrict__ x, int T, int H, uint32_t* xs,
-                             float* xsum, float* psum, int vstride) {
+                                             float* psum, int vstride) {
   const int per_tok = H / 16;
   const int n_items = T * per_tok;
   constexpr int kR = 4;
@@ -249,66 +353,99 @@ __device__ __forceinline__ void stage_tokens(const uint16_t* __restrict__ x, int
       }
     }
   }
-  __syncthreads();
-  const int nb = H / 32;
+}
+
+// Block sums of the staged tokens (after a barrier that follows stage_tokens).
+__device__ __forceinline__ void token_block_sums(int T, int H, float* xsum, const float* psum) {
+  const int nb = H / 32, per_tok = H / 16;
   for (int i = threadIdx.x; i < T * nb; i += kThreads) {
     const int t = i / nb, b = i % nb;
     xsum[t * nb + b] = psum[t * per_tok + 2 * b] + psum[t * per_tok + 2 * b + 1];
   }
 }
 
-// fp32 vectors written by other workgroups (h) into hi/lo bf16 vectors of
-// the pair layout (F32 format: plain fp32), 16 columns per item, loads first.
+
+// Tagged fp32 vectors published by other workgroups (h) into hi/lo bf16
+// vectors of the pair layout (F32 format: plain fp32), 16 columns per item.
+// All loads of a batch are issued first; words that do not yet carry this
+// call's number are read again until they do (their producers never wait
+// on anything, so this ends).
 template <int FMT>
-__device__ __forceinline__ void stage_h(const float* const* srcs, int n, int K, uint32_t* xd, float* sd,
-                        float* psum, int vs) {
+__device__ __forceinline__ void stage_h(const uint64_t* const* srcs, int n, int K, uint32_t* xd,
+                                        float* sd, float* psum, int vs, uint32_t epoch) {
   const int per_vec = K / 16;
   const int n_items = n * per_vec;
   constexpr int kVPP = FMT == MOE_W_F32 ? 1 : 2;
-  for (int base = 0; base < n_items; base += kThreads) {
-    const int it = base + threadIdx.x;
-    float v[16];
-    if (it < n_items) {
-      const float* src = srcs[it / per_vec] + (it % per_vec) * 16;
+  constexpr int kIt = 2;   // items per thread and batch
+  for (int base = 0; base < n_items; base += kIt * kThreads) {
+    uint64_t wv[kIt][16];
+    const uint64_t* src[kIt];
 #pragma unroll
-      for (int c = 0; c < 16; ++c) v[c] = ld_dev(src + c);
+    for (int r = 0; r < kIt; ++r) {
+      const int it = base + r * kThreads + threadIdx.x;
+      src[r] = it < n_items ? srcs[it / per_vec] + (it % per_vec) * 16 : nullptr;
+      if (src[r]) {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) wv[r][c] = ld_dev(src[r] + c);
+      }
     }
-    if (it < n_items) {
-      const int p = it / per_vec, g16 = it % per_vec;
-      if constexpr (FMT == MOE_W_F32) {
-        float* xf = reinterpret_cast<float*>(xd) + p * vs + g16 * 16;
+    for (;;) {
+      bool ok = true;
 #pragma unroll
-        for (int c = 0; c < 16; ++c) xf[c] = v[c];
-      } else {
-        uint32_t hi[16], lo[16];
-        float shi = 0.f, slo = 0.f;
+      for (int r = 0; r < kIt; ++r)
 #pragma unroll
-        for (int c = 0; c < 16; ++c) {
-          hi[c] = f32_to_bf16_bits(v[c]);
-          const float hf = bf16_to_f32(hi[c]);
-          lo[c] = f32_to_bf16_bits(v[c] - hf);
-          shi += hf;
-          slo += bf16_to_f32(lo[c]);
-        }
-        psum[(kVPP * p) * per_vec + g16] = shi;
-        psum[(kVPP * p + 1) * per_vec + g16] = slo;
-        uint32_t* dh = xd + (kVPP * p) * vs;
-        uint32_t* dl = xd + (kVPP * p + 1) * vs;
-        if constexpr (FMT == MOE_W_Q2B32) {
-          const int off = (g16 >> 2) * Fmt<FMT>::kCS + (g16 & 3) * 8;
+        for (int c = 0; c < 16; ++c) ok = ok && (!src[r] || tag_ok(wv[r][c], epoch));
+      if (ok) break;
+      __builtin_amdgcn_s_sleep(1);
 #pragma unroll
-          for (int s = 0; s < 8; ++s) {
-            dh[off + s] = hi[s] | (hi[s + 8] << 16);
-            dl[off + s] = lo[s] | (lo[s + 8] << 16);
-          }
+      for (int r = 0; r < kIt; ++r)
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+          if (src[r] && !tag_ok(wv[r][c], epoch)) wv[r][c] = ld_dev(src[r] + c);
+    }
+#pragma unroll
+    for (int r = 0; r < kIt; ++r) {
+      const int it = base + r * kThreads + threadIdx.x;
+      float v[16];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) v[c] = tag_val(wv[r][c]);
+      if (it < n_items) {
+        const int p = it / per_vec, g16 = it % per_vec;
+        if constexpr (FMT == MOE_W_F32) {
+          float* xf = reinterpret_cast<float*>(xd) + p * vs + g16 * 16;
+#pragma unroll
+          for (int c = 0; c < 16; ++c) xf[c] = v[c];
         } else {
+          uint32_t hi[16], lo[16];
+          float shi = 0.f, slo = 0.f;
 #pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int off = (g16 >> 1) * Fmt<FMT>::kCS + ((g16 & 1) * 2 + q) * 4;
+          for (int c = 0; c < 16; ++c) {
+            hi[c] = f32_to_bf16_bits(v[c]);
+            const float hf = bf16_to_f32(hi[c]);
+            lo[c] = f32_to_bf16_bits(v[c] - hf);
+            shi += hf;
+            slo += bf16_to_f32(lo[c]);
+          }
+          psum[(kVPP * p) * per_vec + g16] = shi;
+          psum[(kVPP * p + 1) * per_vec + g16] = slo;
+          uint32_t* dh = xd + (kVPP * p) * vs;
+          uint32_t* dl = xd + (kVPP * p + 1) * vs;
+          if constexpr (FMT == MOE_W_Q2B32) {
+            const int off = (g16 >> 2) * Fmt<FMT>::kCS + (g16 & 3) * 8;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              dh[off + s] = hi[8 * q + s] | (hi[8 * q + s + 4] << 16);
-              dl[off + s] = lo[8 * q + s] | (lo[8 * q + s + 4] << 16);
+            for (int s = 0; s < 8; ++s) {
+              dh[off + s] = hi[s] | (hi[s + 8] << 16);
+              dl[off + s] = lo[s] | (lo[s + 8] << 16);
+            }
+          } else {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const int off = (g16 >> 1) * Fmt<FMT>::kCS + ((g16 & 1) * 2 + q) * 4;
+#pragma unroll
+              for (int s = 0; s < 4; ++s) {
+                dh[off + s] = hi[8 * q + s] | (hi[8 * q + s + 4] << 16);
+                dl[off + s] = lo[8 * q + s] | (lo[8 * q + s + 4] << 16);
+              }
             }
           }
         }
@@ -490,24 +627,34 @@ __host__ __device__ __forceinline__ int chunks_of(int K) {
   return FMT == MOE_W_F32 ? K / 4 : K / Fmt<FMT>::kWPC;
 }
 
-// gate/up + SwiGLU for one row per lane group (64 / LPR rows per wave) of
-// one expert, for its n tokens; h[t] goes to out[ids(t)][i] (ids = pair ids,
-// or the tokens themselves when ids is null).
+// gate/up rows i of one expert: this lane's chunks (loads only).
 template <int FMT>
-__device__ __forceinline__ void gateup_task(const LayerArgs& a, const MatView& G, const MatView& U,
-                                            int slot, int i, int n, const int* vid,
-                                            const int* ids, float* out, const uint32_t* xs,
-                                            const float* xsum, int vstride, int lane_g) {
+__device__ __forceinline__ void gateup_load(RowRegs<FMT, kNChMax>& rg, RowRegs<FMT, kNChMax>& ru,
+                                            const LayerArgs& a, const Planes& G, const Planes& U,
+                                            int slot, int i, int lane_g) {
   constexpr int kLprGU = Lanes<FMT>::kGU;
   const int K = a.H, sstride = K / 32;
   const int nch = chunks_of<FMT>(K) / kLprGU;
   const int64_t row_bytes = int64_t(K) * fmt_bits(FMT) / 8;
-  const int64_t blk = int64_t(slot) * G.mat_blocks + int64_t(i) * sstride;
-  RowRegs<FMT, kNChMax> rg, ru;
-  load_row<FMT, kNChMax>(rg, G.codes + slot * G.mat_bytes + i * row_bytes, G.scale + blk,
-                         G.mn + blk, nch, lane_g, kLprGU);
-  load_row<FMT, kNChMax>(ru, U.codes + slot * U.mat_bytes + i * row_bytes, U.scale + blk,
-                         U.mn + blk, nch, lane_g, kLprGU);
+  const int64_t blk = int64_t(slot) * a.mat_blocks + int64_t(i) * sstride;
+  const int64_t off = slot * a.mat_bytes + i * row_bytes;
+  load_row<FMT, kNChMax>(rg, G.codes + off, G.scale + blk, G.mn + blk, nch, lane_g, kLprGU);
+  load_row<FMT, kNChMax>(ru, U.codes + off, U.scale + blk, U.mn + blk, nch, lane_g, kLprGU);
+}
+
+// SwiGLU of row i for the expert's n tokens (vid: their staged vectors);
+// h of token v is published at out[ids(v)][i] (ids = pair ids, or the
+// tokens themselves when ids is null).
+template <int FMT>
+__device__ __forceinline__ void gateup_compute(const RowRegs<FMT, kNChMax>& rg,
+                                               const RowRegs<FMT, kNChMax>& ru, const LayerArgs& a,
+                                               int i, int n, const int* vid, const int* ids,
+                                               uint64_t* out, const uint32_t* xs,
+                                               const float* xsum, int vstride, int lane_g,
+                                               uint32_t epoch) {
+  constexpr int kLprGU = Lanes<FMT>::kGU;
+  const int K = a.H, sstride = K / 32;
+  const int nch = chunks_of<FMT>(K) / kLprGU;
   for (int v = 0; v < n; ++v) {
     const int id = vid ? vid[v] : v;
     float g, u;
@@ -515,13 +662,15 @@ __device__ __forceinline__ void gateup_task(const LayerArgs& a, const MatView& G
                                    xsum + id * sstride, g, u);
     g = group_sum<kLprGU>(g);
     u = group_sum<kLprGU>(u);
-    if (lane_g == 0) st_dev(out + int64_t(ids ? ids[v] : v) * a.I + i, silu_f32(g) * u);
+    if (lane_g == 0)
+      st_dev(out + int64_t(ids ? ids[v] : v) * a.I + i, tag_word(silu_f32(g) * u, epoch));
   }
 }
 
-// One router wave task: 64 / LPR rows of W (E x H) against the T tokens.
-// Quantised formats keep the tokens in the expert pair layout, so W's
-// natural bf16 pairs are regrouped with v_perm.
+// Router wave tasks: 64 / LPR rows of W (E x H) against the T tokens.
+// Quantised expert formats keep the tokens in the expert pair layout, so
+// W's natural bf16 pairs are regrouped with v_perm; their router is bf16
+// with one 16-byte-aligned chunk of kWPC columns per lane (LPR = chunks).
 template <int FMT>
 __host__ __device__ __forceinline__ int router_lpr(int H) {
   if (FMT == MOE_W_F32) return 64;
@@ -530,8 +679,41 @@ __host__ __device__ __forceinline__ int router_lpr(int H) {
 }
 
 template <int FMT>
-__device__ __forceinline__ void router_task(const LayerArgs& a, int task, const uint32_t* xs, int vstride,
-                            int lane) {
+struct RouterRegs {
+  static constexpr int kQ = FMT == MOE_W_F32 ? 1 : Fmt<FMT>::kWPC / 8;   // 16-byte loads
+  u32x4 w[kQ];
+  float bias;
+};
+
+// Issues the task's loads: zeroes its share of y (every router task has
+// one; they cover y), then loads this lane's router chunk and bias.
+template <int FMT>
+__device__ __forceinline__ void router_load(RouterRegs<FMT>& R, const LayerArgs& a, int task,
+                                            int n_router, int lane) {
+  const int TH = a.T * a.H, per = (TH + n_router - 1) / n_router;
+  const int y0 = task * per, y1 = min(y0 + per, TH);
+  for (int i = y0 + lane; i < y1; i += 64) st_dev(a.y + i, 0.f);
+  const int lpr = router_lpr<FMT>(a.H);
+  const int e = task * (64 / lpr) + lane / lpr;
+  if constexpr (FMT != MOE_W_F32) {
+    if (e < a.E) {
+      const u32x4* row = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.W) +
+                                                        int64_t(e) * a.H);
+      const int c = lane % lpr;
+#pragma unroll
+      for (int q = 0; q < RouterRegs<FMT>::kQ; ++q) R.w[q] = row[c * RouterRegs<FMT>::kQ + q];
+    }
+  }
+  R.bias = (e < a.E && a.bias) ? a.bias[e] : 0.f;
+}
+
+// Logits of the task's rows for every token, published as tagged words
+// once this wave's zeroes of y have landed (a workgroup adds into y only
+// after it has seen every logit).
+template <int FMT>
+__device__ __forceinline__ void router_compute(const RouterRegs<FMT>& R, const LayerArgs& a,
+                                               int task, const uint32_t* xs, int vstride,
+                                               int lane, uint32_t epoch) {
   const int lpr = router_lpr<FMT>(a.H);
   const int e = task * (64 / lpr) + lane / lpr;
   const int lane_g = lane % lpr;
@@ -540,40 +722,33 @@ __device__ __forceinline__ void router_task(const LayerArgs& a, int task, const 
   for (int t = 0; t < kTMax; ++t) acc[t] = 0.f;
   if (e < a.E) {
     if constexpr (FMT == MOE_W_Q2B32 || FMT == MOE_W_Q4B32) {
-      constexpr int kWPC = Fmt<FMT>::kWPC;
-      const int chunks = a.H / kWPC;
-      const u32x4* row = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.W) +
-                                                        int64_t(e) * a.H);
-      constexpr int kQ = kWPC / 8;          // 16-byte loads of W per chunk
-      for (int c = lane_g; c < chunks; c += lpr) {
-        uint32_t w[kQ * 4];
+      constexpr int kQ = RouterRegs<FMT>::kQ;
+      uint32_t w[kQ * 4];
 #pragma unroll
-        for (int q = 0; q < kQ; ++q) {
-          const u32x4 v = row[c * kQ + q];
-          w[q * 4 + 0] = v[0];
-          w[q * 4 + 1] = v[1];
-          w[q * 4 + 2] = v[2];
-          w[q * 4 + 3] = v[3];
+      for (int q = 0; q < kQ; ++q) {
+        w[q * 4 + 0] = R.w[q][0];
+        w[q * 4 + 1] = R.w[q][1];
+        w[q * 4 + 2] = R.w[q][2];
+        w[q * 4 + 3] = R.w[q][3];
+      }
+      constexpr int kG = 4, kS = FMT == MOE_W_Q2B32 ? 8 : 4;
+      uint32_t pr[kG * kS];
+#pragma unroll
+      for (int g = 0; g < kG; ++g)
+#pragma unroll
+        for (int m = 0; m < kS / 2; ++m) {
+          const uint32_t lo_w = w[g * kS + m], hi_w = w[g * kS + kS / 2 + m];
+          pr[g * kS + 2 * m] = __builtin_amdgcn_perm(hi_w, lo_w, 0x05040100u);
+          pr[g * kS + 2 * m + 1] = __builtin_amdgcn_perm(hi_w, lo_w, 0x07060302u);
         }
-        constexpr int kG = 4, kS = FMT == MOE_W_Q2B32 ? 8 : 4;
-        uint32_t pr[kG * kS];
 #pragma unroll
-        for (int g = 0; g < kG; ++g)
+      for (int t = 0; t < kTMax; ++t) {
+        if (t < a.T) {
+          const uint32_t* xv = xs + t * vstride + lane_g * Fmt<FMT>::kCS;
+          float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int m = 0; m < kS / 2; ++m) {
-            const uint32_t lo_w = w[g * kS + m], hi_w = w[g * kS + kS / 2 + m];
-            pr[g * kS + 2 * m] = __builtin_amdgcn_perm(hi_w, lo_w, 0x05040100u);
-            pr[g * kS + 2 * m + 1] = __builtin_amdgcn_perm(hi_w, lo_w, 0x07060302u);
-          }
-#pragma unroll
-        for (int t = 0; t < kTMax; ++t) {
-          if (t < a.T) {
-            const uint32_t* xv = xs + t * vstride + c * Fmt<FMT>::kCS;
-            float s4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < kG * kS; ++j) s4[j & 3] = dot2_bf16(pr[j], xv[j], s4[j & 3]);
-            acc[t] += (s4[0] + s4[1]) + (s4[2] + s4[3]);
-          }
+          for (int j = 0; j < kG * kS; ++j) s4[j & 3] = dot2_bf16(pr[j], xv[j], s4[j & 3]);
+          acc[t] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
         }
       }
     } else {
@@ -588,224 +763,388 @@ __device__ __forceinline__ void router_task(const LayerArgs& a, int task, const 
       }
     }
   }
-  const float b = (e < a.E && a.bias) ? a.bias[e] : 0.f;
+  wait_mem();
 #pragma unroll
   for (int t = 0; t < kTMax; ++t) {
     if (t < a.T) {
       float s = acc[t];
       for (int m = 1; m < lpr; m <<= 1) s += __shfl_xor(s, m, 64);
-      if (e < a.E && lane_g == 0) st_dev(a.logits + t * a.E + e, s + b);
+      if (e < a.E && lane_g == 0) st_dev(region_lg(a) + t * a.E + e, tag_word(s + R.bias, epoch));
     }
+  }
+}
+
+// Slot of a chosen expert: -1 when it is not resident (or out of range).
+__device__ __forceinline__ int slot_of_choice(const LayerArgs& a, const Lds& L, int e) {
+  int s = (e >= 0 && e < a.E) ? (a.slot_of ? L.slot_of[e] : e) : -1;
+  return (s >= 0 && s < a.S) ? s : -1;
+}
+
+// Resolution of P <= 64 pairs by wave 0 alone, lane p = pair p: ballots give
+// the miss positions; bucket positions and distinct slots come from one
+// pass over the pairs with their slots read as scalars.
+__device__ __forceinline__ void resolve_wave(const LayerArgs& a, Lds& L, int P, int lane,
+                                             bool writer) {
+  const int p = lane;
+  const bool valid = p < P;
+  const int tok = valid ? L.ptok[p] : 0;
+  const bool first_of_token = valid && (p == 0 || L.ptok[p - 1] != tok);
+  const int s = valid ? slot_of_choice(a, L, L.idx[p]) : -1;
+  const bool hit = s >= 0;
+  const uint64_t miss_mask = __ballot(valid && !hit);
+  const int mpos = __builtin_amdgcn_mbcnt_hi(uint32_t(miss_mask >> 32),
+                                             __builtin_amdgcn_mbcnt_lo(uint32_t(miss_mask), 0u));
+  const int n_miss = __popcll(miss_mask);
+  if (writer) {
+    if (valid && a.slot_idx) a.slot_idx[p] = s;
+    if (valid && !hit) {
+      moe_miss m;
+      m.expert = L.idx[p];
+      m.token = tok;
+      m.gate = L.gate[p];
+      a.miss[mpos] = m;
+    }
+    if (first_of_token) a.miss_off[tok] = mpos;
+    if (p == 0) a.miss_off[a.T] = n_miss;
+  }
+  int pos = 0;
+  bool first = hit;
+  for (int q = 0; q < P; ++q) {
+    const int sq = __builtin_amdgcn_readlane(s, q);
+    if (sq >= 0) {
+      pos += (sq < s || (sq == s && q < p)) ? 1 : 0;
+      first = first && !(sq == s && q < p);
+    }
+  }
+  const uint64_t first_mask = __ballot(hit && first);
+  int apos = 0;
+  for (int q = 0; q < P; ++q)
+    if ((first_mask >> q) & 1ull) apos += __builtin_amdgcn_readlane(s, q) < s ? 1 : 0;
+  if (hit) {
+    L.bpair[pos] = p;
+    L.tok[pos] = tok;
+    L.sorted[pos] = s;
+  }
+  if (hit && first) {
+    L.act_slot[apos] = s;
+    L.act_start[apos] = pos;
+  }
+  if (p == 0) {
+    const int n_act = __popcll(first_mask);
+    L.act_start[n_act] = P - n_miss;
+    L.n_act = n_act;
+  }
+}
+
+// Resolution of one token's k choices by the wave that chose them (lane j
+// holds choice j and its gate).  The choices are distinct experts, so the
+// hits need no sorting: they stay in choice order, one bucket each.
+__device__ __forceinline__ void resolve_one(const LayerArgs& a, Lds& L, int e, float g, int lane,
+                                            bool writer) {
+  const int k = a.k;
+  const bool valid = lane < k;
+  const int s = valid ? slot_of_choice(a, L, e) : -1;
+  const bool hit = s >= 0;
+  const uint64_t miss_mask = __ballot(valid && !hit);
+  const uint64_t hit_mask = __ballot(hit);
+  const int mpos = __builtin_amdgcn_mbcnt_hi(uint32_t(miss_mask >> 32),
+                                             __builtin_amdgcn_mbcnt_lo(uint32_t(miss_mask), 0u));
+  const int hpos = __builtin_amdgcn_mbcnt_hi(uint32_t(hit_mask >> 32),
+                                             __builtin_amdgcn_mbcnt_lo(uint32_t(hit_mask), 0u));
+  const int n_hit = __popcll(hit_mask);
+  if (writer) {
+    if (valid && a.slot_idx) a.slot_idx[lane] = s;
+    if (valid && !hit) {
+      moe_miss m;
+      m.expert = e;
+      m.token = 0;
+      m.gate = g;
+      a.miss[mpos] = m;
+    }
+    if (lane == 0) a.miss_off[0] = 0;
+    if (lane == 1) a.miss_off[1] = __popcll(miss_mask);
+  }
+  if (hit) {
+    L.bpair[hpos] = lane;
+    L.tok[hpos] = 0;
+    L.act_slot[hpos] = s;
+    L.act_start[hpos] = hpos;
+  }
+  if (lane == 0) {
+    L.act_start[n_hit] = n_hit;
+    L.n_act = n_hit;
+  }
+}
+
+// Resolution of up to 256 pairs by the whole workgroup (thread p = pair p).
+__device__ __forceinline__ void resolve_block(const LayerArgs& a, Lds& L, int P, bool writer) {
+  const int p = threadIdx.x;
+  const int tok = p < P ? L.ptok[p] : 0;
+  const bool first_of_token = p < P && (p == 0 || L.ptok[p - 1] != tok);
+  const int s = p < P ? slot_of_choice(a, L, L.idx[p]) : -1;
+  if (writer && p < P && a.slot_idx) a.slot_idx[p] = s;
+  if (p < kPMax) L.slot[p] = s;
+  const int is_miss = (p < P && s < 0) ? 1 : 0;
+  int n_miss;
+  const int mpos = block_exclusive_scan(is_miss, L.tmp, &n_miss);
+  if (writer) {
+    if (is_miss) {
+      moe_miss m;
+      m.expert = L.idx[p];
+      m.token = tok;
+      m.gate = L.gate[p];
+      a.miss[mpos] = m;
+    }
+    if (first_of_token) a.miss_off[tok] = mpos;
+    if (p == 0) a.miss_off[a.T] = n_miss;
+  }
+  __syncthreads();
+  const int n_hit = P - n_miss;
+  if (p < P && s >= 0) {
+    int pos = 0;
+    for (int q = 0; q < P; ++q) {
+      const int sq = L.slot[q];
+      pos += (sq >= 0 && (sq < s || (sq == s && q < p))) ? 1 : 0;
+    }
+    L.bpair[pos] = p;
+    L.tok[pos] = tok;
+    L.sorted[pos] = s;
+  }
+  __syncthreads();
+  const int first = (p < n_hit && (p == 0 || L.sorted[p] != L.sorted[p - 1])) ? 1 : 0;
+  int n_act;
+  const int apos = block_exclusive_scan(first, L.tmp, &n_act);
+  if (first) {
+    L.act_slot[apos] = L.sorted[p];
+    L.act_start[apos] = p;
+  }
+  if (p == 0) {
+    L.act_start[n_act] = n_hit;
+    L.n_act = n_act;
   }
 }
 
 // --------------------------------------------------------------- kernel
 template <int FMT>
-__global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs a) {
+__global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   constexpr int kLprGU = Lanes<FMT>::kGU, kRowsGU = Lanes<FMT>::kRowsGU;
   constexpr int kLprD = Lanes<FMT>::kD, kRowsD = Lanes<FMT>::kRowsD;
   extern __shared__ uint32_t smem[];
   __shared__ Lds L;
-  __shared__ const float* srcs[kTMax];
+  __shared__ const uint64_t* srcs[kTMax];
+  // The arguments are copied to LDS: after the first loads every phase reads
+  // the fields it needs from there, so they do not occupy scalar registers
+  // for the whole launch.
+  __shared__ LayerArgs sa;
   const int G = gridDim.x, b = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int T = a.T, k = a.k, P = T * k, E = a.E;
-  const int K = a.H;
+  if (tid == 0) sa = ka;
+  const int T = ka.T, k = ka.k, P = T * k, E = ka.E;
+  const int K = ka.H;
   const int vstride = FMT == MOE_W_F32 ? K : (K / Fmt<FMT>::kWPC) * Fmt<FMT>::kCS;
-  const int sstride = K / 32;
   // LDS: tokens | block sums | group sums | logits
   uint32_t* xs = smem;
   float* xsum = reinterpret_cast<float*>(xs + T * vstride);
-  float* psum = xsum + T * sstride;
+  float* psum = xsum + T * (K / 32);
   float* lg = psum + T * (K / 16);
 
-  if (tid == 0) L.flag0 = ld_dev(a.sync + kSyncCalls);
-  stage_tokens<FMT>(a.x, T, K, xs, xsum, psum, vstride);
-  __syncthreads();
-  const uint32_t epoch = L.flag0 + 1u;     // this call's number
-  uint32_t* task_flag = a.sync + kSyncTasks;
-
-  // ---- A: router rows, shared gate/up rows, zero y
-  {
-    const int lpr = router_lpr<FMT>(K);
-    const int n_router = (E + (64 / lpr) - 1) / (64 / lpr);
-    const int n_shared = a.has_sh ? a.I / kRowsGU : 0;
-    for (int task = b + wave * G; task < n_router + n_shared; task += kWaves * G) {
-      if (task < n_router) {
-        router_task<FMT>(a, task, xs, vstride, lane);
-      } else {
-        const int i = (task - n_router) * kRowsGU + lane / kLprGU;
-        gateup_task<FMT>(a, a.sg, a.su, 0, i, T, nullptr, nullptr, a.h_sh, xs, xsum, vstride,
-                         lane % kLprGU);
-      }
-    }
-    for (int i = b * kThreads + tid; i < T * K; i += G * kThreads) st_dev(a.y + i, 0.f);
+  // ---- A: loads first (call counter, slot table, first task's rows)
+  const uint32_t calls = tid == 0 ? ld_dev(region_calls(ka)) : 0u;
+  int so[kEMax / kThreads];
+#pragma unroll
+  for (int r = 0; r < kEMax / kThreads; ++r) {
+    const int e = tid + r * kThreads;
+    so[r] = (ka.slot_of && e < E) ? ka.slot_of[e] : -1;
   }
-  wait_mem();
+  const int n_router = (E + (64 / router_lpr<FMT>(K)) - 1) / (64 / router_lpr<FMT>(K));
+  const int n_shared = ka.has_sh ? ka.I / kRowsGU : 0;
+  const int n_a = n_router + n_shared;
+  const int task0 = b + wave * G;
+  const int lane_gu = lane % kLprGU;
+  RouterRegs<FMT> rr;
+  RowRegs<FMT, kNChMax> rg, ru;
+  if (task0 < n_router)
+    router_load<FMT>(rr, ka, task0, n_router, lane);
+  else if (task0 < n_a)
+    gateup_load<FMT>(rg, ru, ka, ka.sg, ka.su, 0, (task0 - n_router) * kRowsGU + lane / kLprGU,
+                     lane_gu);
+  stage_tokens<FMT>(ka.x, T, K, xs, psum, vstride);
+  if (tid == 0) L.calls = calls;
+#pragma unroll
+  for (int r = 0; r < kEMax / kThreads; ++r)
+    if (tid + r * kThreads < E) L.slot_of[tid + r * kThreads] = so[r];
   __syncthreads();
-  if (tid == 0) st_dev(a.sync + kSyncArrive + b, epoch);
-  while (!__syncthreads_and(tid >= G || ld_dev(a.sync + kSyncArrive + tid) == epoch))
-    __builtin_amdgcn_s_sleep(1);
-  if (b == 0 && tid == 0) st_dev(a.sync + kSyncCalls, epoch);   // every workgroup has read it
+  const LayerArgs& a = sa;
+  token_block_sums(T, K, xsum, psum);
+  __syncthreads();
+  const uint32_t epoch = L.calls + 1u;   // this call's number
+  for (int task = task0; task < n_a; task += kWaves * G) {
+    if (task < n_router) {
+      if (task != task0) router_load<FMT>(rr, a, task, n_router, lane);
+      router_compute<FMT>(rr, a, task, xs, vstride, lane, epoch);
+    } else {
+      const int i = (task - n_router) * kRowsGU + lane / kLprGU;
+      if (task != task0) gateup_load<FMT>(rg, ru, a, a.sg, a.su, 0, i, lane_gu);
+      gateup_compute<FMT>(rg, ru, a, i, T, nullptr, nullptr, region_h_sh(a), xs, xsum, vstride, lane_gu,
+                          epoch);
+    }
+  }
 
-  // ---- B: routing, in every workgroup
+  // this workgroup has read the counter (workgroup 0 checks before it
+  // advances the counter)
+  if (tid == 0) st_dev(region_arrive(a) + b, tag_word(0.f, epoch));
+
+  // ---- B: every logit of this call, then routing
   {
-    constexpr int kR = 8;
-    for (int base = 0; base < T * E; base += kR * kThreads) {
-      float v[kR];
+    const int n_lg = T * E;
+    constexpr int kR = kTMax * kEMax / kThreads / 2;
+    for (int base = 0; base < n_lg; base += kR * kThreads) {
+      uint64_t w[kR];
 #pragma unroll
       for (int r = 0; r < kR; ++r) {
         const int i = base + r * kThreads + tid;
-        if (i < T * E) v[r] = ld_dev(a.logits + i);
+        if (i < n_lg) w[r] = ld_dev(region_lg(a) + i);
+      }
+      for (;;) {
+        bool ok = true;
+#pragma unroll
+        for (int r = 0; r < kR; ++r) {
+          const int i = base + r * kThreads + tid;
+          ok = ok && (i >= n_lg || tag_ok(w[r], epoch));
+        }
+        if (ok) break;
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int r = 0; r < kR; ++r) {
+          const int i = base + r * kThreads + tid;
+          if (i < n_lg && !tag_ok(w[r], epoch)) w[r] = ld_dev(region_lg(a) + i);
+        }
       }
 #pragma unroll
       for (int r = 0; r < kR; ++r) {
         const int i = base + r * kThreads + tid;
-        if (i < T * E) lg[i] = v[r];
+        if (i < n_lg) lg[i] = tag_val(w[r]);
       }
     }
   }
   __syncthreads();
-  for (int t = wave; t < T; t += kWaves) {
+  const bool one_token = T == 1 && E <= 8 * 64 && k <= kTopkListMax;
+  for (int t = one_token ? 0 : wave; t < T; t += kWaves) {
     int my_e;
     float my_v;
-    if (E <= 512) wave_topk<8>(lg + t * E, E, k, lane, &my_e, &my_v);
+    if (one_token) block_topk_one(lg, E, k, wave, lane, L.cand, &my_e, &my_v);
+    else if (E <= 512) wave_topk<8>(lg + t * E, E, k, lane, &my_e, &my_v);
     else wave_topk<16>(lg + t * E, E, k, lane, &my_e, &my_v);
-    const float vmax = __shfl(my_v, 0, 64);
+    if (one_token && wave != 0) continue;
+    // gates: softmax over the k chosen logits (lane 0 holds the largest)
+    const float vmax = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_v), 0));
     const float ex = lane < k ? expf(my_v - vmax) : 0.f;
-    float z = ex;
-    for (int m = 1; m < 64; m <<= 1) z += __shfl_xor(z, m, 64);
+    const float z = wave_sum_f32(ex);
+    const float g = ex / z;
     if (lane < k) {
-      const float g = ex / z;
       L.idx[t * k + lane] = my_e;
       L.gate[t * k + lane] = g;
+      L.ptok[t * k + lane] = t;
       if (b == 0) {
         a.idx[t * k + lane] = my_e;
         a.gate[t * k + lane] = g;
       }
     }
+    if (one_token) resolve_one(a, L, my_e, g, lane, b == 0);
+  }
+  if (!one_token) {
+    __syncthreads();
+    if (P <= 64) {
+      if (wave == 0) resolve_wave(a, L, P, lane, b == 0);
+    } else {
+      resolve_block(a, L, P, b == 0);
+    }
   }
   __syncthreads();
-  {
-    const int p = tid;
-    int s = -1;
-    if (p < P) {
-      const int e = L.idx[p];
-      s = (e >= 0 && e < E) ? (a.slot_of ? a.slot_of[e] : e) : -1;
-      s = (s >= 0 && s < a.S) ? s : -1;
-      if (b == 0 && a.slot_idx) a.slot_idx[p] = s;
-    }
-    if (p < kPMax) L.slot[p] = s;
-    const int is_miss = (p < P && s < 0) ? 1 : 0;
-    int n_miss;
-    const int mpos = block_exclusive_scan(is_miss, L.tmp, &n_miss);
-    if (b == 0) {
-      if (is_miss) {
-        moe_miss m;
-        m.expert = L.idx[p];
-        m.token = p / k;
-        m.gate = L.gate[p];
-        a.miss[mpos] = m;
-      }
-      if (p < P && p % k == 0) a.miss_off[p / k] = mpos;
-      if (p == 0) a.miss_off[T] = n_miss;
-    }
-    __syncthreads();
-    const int n_hit = P - n_miss;
-    if (p < P && s >= 0) {
-      int pos = 0;
-      for (int q = 0; q < P; ++q) {
-        const int sq = L.slot[q];
-        pos += (sq >= 0 && (sq < s || (sq == s && q < p))) ? 1 : 0;
-      }
-      L.bpair[pos] = p;
-      L.tok[pos] = p / k;
-      L.sorted[pos] = s;
-    }
-    __syncthreads();
-    const int first = (p < n_hit && (p == 0 || L.sorted[p] != L.sorted[p - 1])) ? 1 : 0;
-    int n_act;
-    const int apos = block_exclusive_scan(first, L.tmp, &n_act);
-    if (first) {
-      L.act_slot[apos] = L.sorted[p];
-      L.act_start[apos] = p;
-    }
-    if (p == 0) {
-      L.act_start[n_act] = n_hit;
-      L.n_act = n_act;
-    }
-    __syncthreads();
-  }
   const int n_act = L.n_act;
 
-  // ---- C: routed gate/up, 8 rows of one expert per wave task
+  // ---- C: the first down unit's loads, then routed gate/up
+  const int Kd = a.I;
+  constexpr int kVPP = FMT == MOE_W_F32 ? 1 : 2;
+  const int vs_d = FMT == MOE_W_F32 ? Kd : (Kd / Fmt<FMT>::kWPC) * Fmt<FMT>::kCS;
+  const int ss_d = Kd / 32;
+  const int nch_d = chunks_of<FMT>(Kd) / kLprD;
+  const int64_t row_bytes_d = int64_t(Kd) * fmt_bits(FMT) / 8;
+  const int nrb = (a.H + kRowsD - 1) / kRowsD;
+  const int n_units = (n_act + (a.has_sh ? 1 : 0)) * nrb;
+  const int lane_gd = lane % kLprD;
+  RowRegs<FMT, kNChMax> rd;
+  auto load_down = [&](int unit) {
+    const int u = unit / nrb, rb = unit % nrb;
+    const bool shared = u >= n_act;
+    const Planes D = shared ? a.sd : a.d;
+    const int slot = shared ? 0 : L.act_slot[u];
+    const int r = rb * kRowsD + wave * (64 / kLprD) + lane / kLprD;
+    const int rr_ = r < a.H ? r : a.H - 1;
+    const int64_t blk = int64_t(slot) * a.mat_blocks + int64_t(rr_) * ss_d;
+    load_row<FMT, kNChMax>(rd, D.codes + slot * a.mat_bytes + rr_ * row_bytes_d, D.scale + blk,
+                           D.mn + blk, nch_d, lane_gd, kLprD);
+  };
+  if (b < n_units) load_down(b);
+  uint64_t arr = 0;
+  if (b == 0 && tid < G) arr = ld_dev(region_arrive(a) + tid);
   {
-    const int tasks_per_expert = a.I / kRowsGU;
-    const int n_tasks = n_act * tasks_per_expert;
+    const int tpe = a.I / kRowsGU;
+    const int n_tasks = n_act * tpe;
     for (int task = b + wave * G; task < n_tasks; task += kWaves * G) {
-      const int u = task / tasks_per_expert;
-      const int i = (task % tasks_per_expert) * kRowsGU + lane / kLprGU;
+      const int u = task / tpe;
+      const int i = (task % tpe) * kRowsGU + lane / kLprGU;
       const int st = L.act_start[u];
       const int n = L.act_start[u + 1] - st;
-      gateup_task<FMT>(a, a.g, a.u, L.act_slot[u], i, n, L.tok + st, L.bpair + st, a.h, xs, xsum,
-                       vstride, lane % kLprGU);
-      wait_mem();
-      if (lane == 0) st_dev(task_flag + u * tasks_per_expert + task % tasks_per_expert, epoch);
+      gateup_load<FMT>(rg, ru, a, a.g, a.u, L.act_slot[u], i, lane_gu);
+      gateup_compute<FMT>(rg, ru, a, i, n, L.tok + st, L.bpair + st, region_h(a), xs, xsum, vstride,
+                          lane_gu, epoch);
     }
   }
 
-  // ---- D: down units (expert or shared, 128-row block), y += gate * D h
+  // ---- D: down units (expert or shared, block of rows), y += gate * D h
   {
-    const int Kd = a.I;
-    constexpr int kVPP = FMT == MOE_W_F32 ? 1 : 2;
-    const int vs_d = FMT == MOE_W_F32 ? Kd : (Kd / Fmt<FMT>::kWPC) * Fmt<FMT>::kCS;
-    const int ss_d = Kd / 32;
-    const int nch = chunks_of<FMT>(Kd) / kLprD;
-    const int64_t row_bytes = int64_t(Kd) * fmt_bits(FMT) / 8;
-    const int nrb = (a.H + kRowsD - 1) / kRowsD;
-    const int contributors = n_act + (a.has_sh ? 1 : 0);
-    const int n_units = contributors * nrb;
     uint32_t* xd = smem;                                    // reuses the token area
     float* sd = reinterpret_cast<float*>(xd + kVPP * kTMax * vs_d);
     float* pd = sd + kVPP * kTMax * ss_d;
-    const int lane_g = lane % kLprD;
     for (int unit = b; unit < n_units; unit += G) {
+      if (unit != b) load_down(unit);
       const int u = unit / nrb, rb = unit % nrb;
       const bool shared = u >= n_act;
       const int st = shared ? 0 : L.act_start[u];
       const int n = shared ? T : L.act_start[u + 1] - st;
-      const MatView D = shared ? a.sd : a.d;
-      const int slot = shared ? 0 : L.act_slot[u];
       const int r = rb * kRowsD + wave * (64 / kLprD) + lane / kLprD;
-      const int rr = r < a.H ? r : a.H - 1;
-      RowRegs<FMT, kNChMax> rd;
-      const int64_t blk = int64_t(slot) * D.mat_blocks + int64_t(rr) * ss_d;
-      load_row<FMT, kNChMax>(rd, D.codes + slot * D.mat_bytes + rr * row_bytes, D.scale + blk,
-                              D.mn + blk, nch, lane_g, kLprD);
-      // wait for this expert's gate/up tasks (also the barrier for LDS reuse)
-      const int tpe = a.I / kRowsGU;
-      while (!__syncthreads_and(shared || tid >= tpe ||
-                                ld_dev(task_flag + u * tpe + tid) == epoch))
-        __builtin_amdgcn_s_sleep(1);
+      __syncthreads();   // gate/up tasks and the previous unit are done with the LDS
       if (tid < n)
-        srcs[tid] = shared ? a.h_sh + int64_t(tid) * Kd : a.h + int64_t(L.bpair[st + tid]) * Kd;
+        srcs[tid] = shared ? region_h_sh(a) + int64_t(tid) * Kd
+                           : region_h(a) + int64_t(L.bpair[st + tid]) * Kd;
       __syncthreads();
-      stage_h<FMT>(srcs, n, Kd, xd, sd, pd, vs_d);
+      stage_h<FMT>(srcs, n, Kd, xd, sd, pd, vs_d, epoch);
       __syncthreads();
       for (int v = 0; v < n; ++v) {
-        float o = row_vec_dot<FMT, kNChMax>(rd, nch, lane_g, kLprD, xd + (kVPP * v) * vs_d,
+        float o = row_vec_dot<FMT, kNChMax>(rd, nch_d, lane_gd, kLprD, xd + (kVPP * v) * vs_d,
                                             sd + (kVPP * v) * ss_d);
         if (kVPP == 2)
-          o += row_vec_dot<FMT, kNChMax>(rd, nch, lane_g, kLprD, xd + (kVPP * v + 1) * vs_d,
+          o += row_vec_dot<FMT, kNChMax>(rd, nch_d, lane_gd, kLprD, xd + (kVPP * v + 1) * vs_d,
                                          sd + (kVPP * v + 1) * ss_d);
         o = group_sum<kLprD>(o);
-        if (r < a.H && lane_g == 0) {
+        if (r < a.H && lane_gd == 0) {
           const int t = shared ? v : L.tok[st + v];
           const float g = shared ? 1.f : L.gate[L.bpair[st + v]];
           fadd_dev(a.y + int64_t(t) * a.H + r, g * o);
         }
       }
     }
+  }
+  // Workgroup 0 advances the call counter once every workgroup has read it.
+  if (b == 0) {
+    if (tid < G)
+      while (!tag_ok(arr, epoch)) {
+        __builtin_amdgcn_s_sleep(1);
+        arr = ld_dev(region_arrive(a) + tid);
+      }
+    __syncthreads();
+    if (tid == 0) st_dev(region_calls(a), epoch);
   }
 }
 
@@ -832,7 +1171,8 @@ hipError_t launch_fmt(const LayerArgs& a, size_t lds, hipStream_t st, int* grid_
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    if (per_cu < 1 || cus > kThreads) return hipErrorInvalidConfiguration;
+    // one arrival word per workgroup; the block-wide scans take <= 512 threads
+    if (per_cu < 1 || cus > kLayerMaxGrid || cus > kThreads) return hipErrorInvalidConfiguration;
     c.lds = lds;
     c.device = dev;
     c.grid = cus;   // one workgroup of 8 waves per CU
@@ -863,22 +1203,22 @@ size_t layer_fused_lds(int fmt, int T, int E, int H, int I) {
 bool layer_fused_ok(int fmt, int T, int k, int E, int H, int I) {
   if (T < 1 || T > kTMax || T * k > kPMax) return false;
   if (fmt != MOE_W_F32 && fmt != MOE_W_Q2B32 && fmt != MOE_W_Q4B32) return false;
-  if (H % 32 || I % 32 || E > 1024) return false;
+  if (H % 32 || I % 32 || E > kEMax) return false;
   const int wpc = fmt == MOE_W_Q2B32 ? 64 : fmt == MOE_W_Q4B32 ? 32 : 4;
   const int lgu = fmt == MOE_W_Q4B32 ? Lanes<MOE_W_Q4B32>::kGU : Lanes<MOE_W_Q2B32>::kGU;
   const int ld = fmt == MOE_W_Q4B32 ? Lanes<MOE_W_Q4B32>::kD : Lanes<MOE_W_Q2B32>::kD;
   const int chunks = H / wpc, chunks_d = I / wpc;
   if (chunks % lgu || chunks / lgu > kNChMax) return false;
   if (chunks_d % ld || chunks_d / ld > kNChMax) return false;
-  if (I / (64 / lgu) > kThreads) return false;   // one thread per task flag
   if (fmt != MOE_W_F32 && (chunks > 64 ? (chunks % 64) != 0 : (chunks & (chunks - 1)) != 0))
     return false;
-  return layer_fused_lds(fmt, T, E, H, I) <= 150 * 1024;
+  // dynamic LDS beside the static routing tables (~13 KB) within 160 KB
+  return layer_fused_lds(fmt, T, E, H, I) <= 144 * 1024;
 }
 
-hipError_t launch_layer_fused(const LayerArgs& a, hipStream_t st, int* grid) {
-  const size_t lds = layer_fused_lds(a.fmt, a.T, a.E, a.H, a.I);
-  switch (a.fmt) {
+hipError_t launch_layer_fused(const LayerArgs& a, int fmt, hipStream_t st, int* grid) {
+  const size_t lds = layer_fused_lds(fmt, a.T, a.E, a.H, a.I);
+  switch (fmt) {
     case MOE_W_Q2B32: return launch_fmt<MOE_W_Q2B32>(a, lds, st, grid);
     case MOE_W_Q4B32: return launch_fmt<MOE_W_Q4B32>(a, lds, st, grid);
     case MOE_W_F32: return launch_fmt<MOE_W_F32>(a, lds, st, grid);
