@@ -19,8 +19,8 @@
 //        - section "粗から細へ" (coarse to fine) and its placement figure: a
 //          per-card slot table of individual resident experts.
 //
-// Where the pages are silent the plain readings are used (each is listed in
-// the design doc of the repository): SwiGLU with silu on the gate projection;
+// Where the pages are silent the plain readings are used: SwiGLU with silu
+// on the gate projection;
 // gate weights = softmax over the k selected logits (router bias included);
 // shared expert added with weight 1; top-k order = descending logit, lower
 // expert id first on ties; quantised blocks of 32 weights along a row with

@@ -1074,7 +1074,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   const int n_units = (n_act + (a.has_sh ? 1 : 0)) * nrb;
   const int lane_gd = lane % kLprD;
   RowRegs<FMT, kNChMax> rd;
-  auto load_down = [&](int unit) {
+  auto load_down = [&](int unit, RowRegs<FMT, kNChMax>& rd) {
     const int u = unit / nrb, rb = unit % nrb;
     const bool shared = u >= n_act;
     const Planes D = shared ? a.sd : a.d;
@@ -1085,20 +1085,33 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     load_row<FMT, kNChMax>(rd, D.codes + slot * a.mat_bytes + rr_ * row_bytes_d, D.scale + blk,
                            D.mn + blk, nch_d, lane_gd, kLprD);
   };
-  if (b < n_units) load_down(b);
+  if (b < n_units) load_down(b, rd);
   uint64_t arr = 0;
   if (b == 0 && tid < G) arr = ld_dev(region_arrive(a) + tid);
   {
+    // each wave's tasks in turn, the next task's rows loading while the
+    // current one computes
     const int tpe = a.I / kRowsGU;
     const int n_tasks = n_act * tpe;
-    for (int task = b + wave * G; task < n_tasks; task += kWaves * G) {
+    const int stride = kWaves * G;
+    int task = b + wave * G;
+    if (task < n_tasks)
+      gateup_load<FMT>(rg, ru, a, a.g, a.u, L.act_slot[task / tpe],
+                       (task % tpe) * kRowsGU + lane / kLprGU, lane_gu);
+    for (; task < n_tasks; task += stride) {
+      const int next = task + stride;
+      RowRegs<FMT, kNChMax> ng, nu;
+      if (next < n_tasks)
+        gateup_load<FMT>(ng, nu, a, a.g, a.u, L.act_slot[next / tpe],
+                         (next % tpe) * kRowsGU + lane / kLprGU, lane_gu);
       const int u = task / tpe;
       const int i = (task % tpe) * kRowsGU + lane / kLprGU;
       const int st = L.act_start[u];
       const int n = L.act_start[u + 1] - st;
-      gateup_load<FMT>(rg, ru, a, a.g, a.u, L.act_slot[u], i, lane_gu);
       gateup_compute<FMT>(rg, ru, a, i, n, L.tok + st, L.bpair + st, region_h(a), xs, xsum, vstride,
                           lane_gu, epoch);
+      rg = ng;
+      ru = nu;
     }
   }
 
@@ -1108,7 +1121,8 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     float* sd = reinterpret_cast<float*>(xd + kVPP * kTMax * vs_d);
     float* pd = sd + kVPP * kTMax * ss_d;
     for (int unit = b; unit < n_units; unit += G) {
-      if (unit != b) load_down(unit);
+      RowRegs<FMT, kNChMax> nd;   // the next unit's rows load meanwhile
+      if (unit + G < n_units) load_down(unit + G, nd);
       const int u = unit / nrb, rb = unit % nrb;
       const bool shared = u >= n_act;
       const int st = shared ? 0 : L.act_start[u];
@@ -1134,6 +1148,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
           fadd_dev(a.y + int64_t(t) * a.H + r, g * o);
         }
       }
+      rd = nd;
     }
   }
   // Workgroup 0 advances the call counter once every workgroup has read it.
