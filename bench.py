@@ -35,6 +35,39 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+# HBM bytes per launch of the roofline kernel(s), from two rocprofv3 --pmc
+# passes (FETCH_SIZE, then WRITE_SIZE) over the same bench command, each
+# scaled by what the counter reads for a 256 MiB device copy run in the same
+# process (--copy-probe 256).  The summaries are under profiles/.  A figure
+# is reported only while the kernel sources it was measured on are unchanged
+# (their SHA-256 below); otherwise traffic is null.
+KERNEL_SOURCES = {
+    "decode": ["routed_expert_ffn_gemv_amd/csrc/layer.hip", "routed_expert_ffn_gemv_amd/csrc/layer.h",
+               "routed_expert_ffn_gemv_amd/csrc/gemv_core.h", "routed_expert_ffn_gemv_amd/csrc/common.h"],
+    "prefill": ["routed_expert_ffn_gemv_amd/csrc/ffn_gemm.hip", "routed_expert_ffn_gemv_amd/csrc/gemv_core.h",
+                "routed_expert_ffn_gemv_amd/csrc/common.h"],
+}
+TRAFFIC = {
+    # workload: {"sha256": ..., "bytes": fetched + written per launch}
+}
+
+
+def sources_sha256(kind):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kind):
+    t = TRAFFIC.get(workload)
+    if t is None or t["sha256"] != sources_sha256(kind):
+        return None
+    return t["bytes"]
+
+
 def algorithmic_bytes_decode(cfg, n_experts_read, T):
     """HBM bytes one layer must move: router weights + bias, each distinct
     expert read once (gate, up, down planes), the shared expert, the
@@ -166,7 +199,8 @@ def bench_decode(args, cfg_name):
                    else f"{L} moe_layer calls (one per layer)"},
         "hbm_gbs": round(gbs, 1),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(cfg.name, "decode"),
                      "kernel": "moe_layer (whole call)", "bytes_per_launch": int(bytes_call),
                      "launch_ms": round(ms_call, 5), "distinct_experts_per_layer": round(u, 2)},
     }
@@ -300,7 +334,8 @@ def bench_prefill(args, cfg_name):
         "ms_expert_ffn": round(ffn_ms, 4), "ms_combine": round(float(parts[3]), 4),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
-                     "traffic": None, "kernel": "moe_expert_ffn (grouped gate/up + down GEMMs)",
+                     "traffic": measured_traffic(cfg.name, "prefill"),
+                     "kernel": "moe_expert_ffn (grouped gate/up + down GEMMs)",
                      "flops_per_launch": int(flops)},
     }
     if not args.no_cpu_baseline:

@@ -125,6 +125,17 @@ moe_status check_ws(const moe_layer_desc* d, int64_t T, void* ws, size_t ws_byte
 
 moe_status device_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
 
+// The grouped GEMM reads eight scales (or mins) at a time: every scale and
+// min plane 16-byte aligned (the ABI only promises 4).
+bool planes_16b_aligned(const moe_layer_desc* d) {
+  const moe_mat* m[6] = {&d->gate, &d->up, &d->down, &d->sh_gate, &d->sh_up, &d->sh_down};
+  for (int i = 0; i < 6; ++i) {
+    if (i >= 3 && !has_shared(d)) break;
+    if (!aligned(m[i]->scale, 16) || !aligned(m[i]->min, 16)) return false;
+  }
+  return true;
+}
+
 FfnArgs ffn_args(const moe_layer_desc* d, const uint16_t* x, int T) {
   FfnArgs a;
   memset(&a, 0, sizeof(a));
@@ -254,7 +265,8 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const uint16_t* x, int32_t
   a.shared_out = shared_out;
   hipError_t e = launch_active_from_offsets(desc->num_slots, bucket_off, a.act, st);
   if (e == hipSuccess) {
-    if (int64_t(T) * desc->k >= kFfnGemmMinPairs && ffn_gemm_ok(a.fmt, desc->H, desc->I))
+    if (int64_t(T) * desc->k >= kFfnGemmMinPairs && ffn_gemm_ok(a.fmt, desc->H, desc->I) &&
+        planes_16b_aligned(desc))
       e = launch_ffn_gemm(a, desc->num_slots, bucket_off, at<void>(ws, w.h), st);
     else
       e = launch_ffn_gemv(a, st);

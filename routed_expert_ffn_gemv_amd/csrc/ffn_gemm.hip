@@ -7,14 +7,27 @@
 // routes to it -- so each expert bucket becomes one GEMM whose weights are
 // read once per tile of tokens instead of once per token.
 //
-// Tiles: 128 rows (tokens of one bucket) x 64 output features x 64 K per
-// step, 4 waves of 64 x 32.  gate/up tiles carry the 64 gate rows and the 64
-// up rows of the same features, so SwiGLU happens in registers and h leaves
-// as fp16; down tiles are 128 x 128 and scatter fp32 rows to pair_out by pair
-// id.  Quantised weights are dequantised (d * q + m in fp32, rounded to fp16)
-// into LDS one K step ahead; activations bf16 -> fp16 (exact for the
-// magnitudes here).  Tiles are ordered so that consecutive tiles of one
-// expert run on the same XCD and share its weights in that XCD's L2.
+// Work split (C = A B^T, A = tokens or h rows, B = weight rows):
+//  - A tiles of 128 rows x 64 K live in LDS (double-buffered, rows padded),
+//    filled through registers two K steps ahead, 8 lanes per 128-byte row.
+//    A is fp16 and stored in a K order permuted inside each 32-wide block
+//    (perm_pos) -- the tokens by a conversion pass, h by the gate/up
+//    epilogue.
+//  - B never goes through LDS: each wave owns 64 weight rows, and each lane
+//    builds its MFMA operands from the one 32-weight block it needs (16 or 8
+//    code bytes, loaded two K steps ahead; scales and mins of 8 blocks at a
+//    time go through a small LDS table).  v_perm puts each code byte under
+//    the exponent byte of fp16 1024, giving two exact values 1024 + q;
+//    v_pk_add_f16 removes the 1024 exactly and v_pk_fma_f16 applies
+//    d * q + m with one rounding.  The next K step's operands are built while
+//    the current step's MFMAs run.
+//  - Waves: 4 per block, two blocks per CU, wave tile 128 rows x 64 columns
+//    (4 x 2 MFMA 32x32x16 tiles, fp32 accumulation).  gate/up waves hold 32
+//    gate rows and the 32 up rows of the same features, so SwiGLU happens in
+//    registers; h goes through LDS and leaves as whole fp16 rows.  Down waves
+//    hold 64 output columns and write fp32 rows to pair_out by pair id.
+//  - Tiles are ordered so that consecutive tiles of one expert run on the
+//    same XCD and share its weights in that XCD's L2.
 #include "gemv_core.h"
 #include "kernels.h"
 
@@ -23,18 +36,32 @@ namespace moe {
 namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 128;          // rows per tile
+constexpr int kBM = 128;          // rows per router tile
+constexpr int kQM = 128;          // rows per grouped-GEMM tile
 constexpr int kBK = 64;           // K per step
 constexpr int kLdsRow = kBK + 8;  // halves per LDS row (padding spreads banks)
 constexpr int kXcds = 8;
 
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t v) {
-  const float lo = __uint_as_float(v << 16), hi = __uint_as_float(v & 0xFFFF0000u);
-  const _Float16 a = _Float16(lo), b = _Float16(hi);
-  return uint32_t(__builtin_bit_cast(uint16_t, a)) | (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);
+// Position, inside its 32-wide block, at which the activation of K index
+// j (0..31) is stored: the order in which the weight operand of one lane
+// holds the block (w_operand below).
+//   4-bit: dword i (weights 8i..8i+7) gives operand kk = i with elements
+//          [0,2,4,6,1,3,5,7] + 8i;
+//   2-bit: dword i (weights 16i..16i+15) gives operands kk = 2i + t, t = 0,1,
+//          with elements r + 4b for r = 2t, 2t+1 (outer) and b = 0..3 (inner).
+template <int FMT>
+__host__ __device__ __forceinline__ int perm_pos(int j) {
+  if (FMT == MOE_W_Q4B32) {
+    const int g = j >> 3, r = j & 7;
+    return 8 * g + ((r & 1) ? 4 + (r >> 1) : (r >> 1));
+  } else {
+    const int i = j >> 4, r = j & 3, b = (j >> 2) & 3;
+    return 8 * (2 * i + (r >> 1)) + 4 * (r & 1) + b;
+  }
 }
 
 __device__ __forceinline__ uint32_t f32x2_to_f16x2(float lo, float hi) {
@@ -42,38 +69,39 @@ __device__ __forceinline__ uint32_t f32x2_to_f16x2(float lo, float hi) {
   return uint32_t(__builtin_bit_cast(uint16_t, a)) | (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);
 }
 
-// One 32-weight block of a quantised row -> 32 fp16 in 4 x u32x4.
-template <int FMT>
-__device__ __forceinline__ void dequant_block(const uint32_t* codes, uint16_t sb, uint16_t mb,
-                                              u32x4* out) {
-  const float d = f16_to_f32(sb), m = f16_to_f32(mb);
-  float w[32];
-  if (FMT == MOE_W_Q4B32) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) w[i * 8 + j] = d * float((codes[i] >> (4 * j)) & 15u) + m;
-  } else {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) w[i * 16 + j] = d * float((codes[i] >> (2 * j)) & 3u) + m;
-  }
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    out[q] = u32x4{f32x2_to_f16x2(w[8 * q + 0], w[8 * q + 1]), f32x2_to_f16x2(w[8 * q + 2], w[8 * q + 3]),
-                   f32x2_to_f16x2(w[8 * q + 4], w[8 * q + 5]), f32x2_to_f16x2(w[8 * q + 6], w[8 * q + 7])};
+// Codes -> fp16 pairs (1024 + q, 1024 + q'): v_perm places a code byte (at
+// most 15) under the exponent byte 0x64 of fp16 1024.  Selector bytes 0-3
+// pick the code bytes, 4 the magic byte.
+constexpr uint32_t kMagic = 0x64646464u;
+constexpr uint32_t kSelB01 = 0x04010400u;   // code bytes 0, 1
+constexpr uint32_t kSelB23 = 0x04030402u;   // code bytes 2, 3
+
+__device__ __forceinline__ uint32_t dq_pair(uint32_t pr, f16x2 d2, f16x2 m2) {
+  const f16x2 k1024 = {_Float16(1024.f), _Float16(1024.f)};
+  const f16x2 q = __builtin_bit_cast(f16x2, pr) - k1024;                 // the codes, exact
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, d2, m2));   // d q + m, one rounding
 }
 
-// Register stage of one K step: this thread's share of the A rows (64 B of
-// one row) and of the B rows (one 32-weight block of one row).
+// MFMA B operand kk (0..3) of a lane's block: 8 dequantised fp16 weights in
+// the order perm_pos describes.
 template <int FMT>
-struct Stage {
-  u32x4 a[4];
-  uint32_t b[4];      // codes of one block (Q4: 16 B, Q2: 8 B)
-  uint16_t bs, bm;    // its scale and min
-  u32x4 bw[4];        // bf16 weights (router)
-};
+__device__ __forceinline__ f16x8 w_operand(const uint32_t* c, int kk, f16x2 d2, f16x2 m2) {
+  uint32_t g0, g1;
+  if constexpr (FMT == MOE_W_Q4B32) {
+    g0 = c[kk] & 0x0F0F0F0Fu;
+    g1 = (c[kk] >> 4) & 0x0F0F0F0Fu;
+  } else {
+    const uint32_t w = c[kk >> 1];
+    const int t = kk & 1;
+    g0 = (w >> (4 * t)) & 0x03030303u;
+    g1 = (w >> (4 * t + 2)) & 0x03030303u;
+  }
+  const u32x4 v = {dq_pair(__builtin_amdgcn_perm(kMagic, g0, kSelB01), d2, m2),
+                   dq_pair(__builtin_amdgcn_perm(kMagic, g0, kSelB23), d2, m2),
+                   dq_pair(__builtin_amdgcn_perm(kMagic, g1, kSelB01), d2, m2),
+                   dq_pair(__builtin_amdgcn_perm(kMagic, g1, kSelB23), d2, m2)};
+  return __builtin_bit_cast(f16x8, v);
+}
 
 struct TileInfo {
   int bucket, m0;
@@ -93,11 +121,11 @@ __global__ __launch_bounds__(1024) void gemm_schedule_kernel(ActiveList act, int
     int cnt = 0;
     if (u < nb) {
       const int n = u < n_act ? act.start[u + 1] - act.start[u] : T;
-      cnt = (n + kBM - 1) / kBM;
+      cnt = (n + kQM - 1) / kQM;
     }
     int tot;
     const int off = before + block_exclusive_scan(cnt, tmp, &tot);
-    for (int i = 0; i < cnt; ++i) tiles[off + i] = make_int2(u, i * kBM);
+    for (int i = 0; i < cnt; ++i) tiles[off + i] = make_int2(u, i * kQM);
     before += tot;
   }
   if (threadIdx.x == 0) *n_tiles = before;
@@ -115,15 +143,15 @@ __device__ __forceinline__ int xcd_item() {
 }
 
 struct GemmArgs {
-  const uint16_t* x;        // bf16 [T][H]
-  int T, k, H, I, fmt;
+  const uint16_t* x16;      // fp16 [T][H], K-permuted
+  int T, k, H, I;
   MatView g, u, d, sg, su, sd;
   ActiveList act;
   const int32_t* bucket_pair;
   const int2* tiles;
   const int* n_tiles;
-  _Float16* h;              // fp16 [n_hit][I] by bucket position
-  _Float16* h_sh;           // fp16 [T][I]
+  uint16_t* h;              // fp16 [n_hit][I] by bucket position, K-permuted
+  uint16_t* h_sh;           // fp16 [T][I]
   float* pair_out;          // [T*k][H]
   float* shared_out;        // [T][H]
 };
@@ -141,21 +169,289 @@ __device__ __forceinline__ RowMap row_map(const GemmArgs& a, int2 t, int n_act) 
   r.shared = t.x >= n_act;
   if (!r.shared) {
     const int st = a.act.start[t.x], n = a.act.start[t.x + 1] - st;
-    r.rows = min(kBM, n - t.y);
+    r.rows = min(kQM, n - t.y);
     r.slot = a.act.slot[t.x];
     r.pos0 = st + t.y;
   } else {
-    r.rows = min(kBM, a.T - t.y);
+    r.rows = min(kQM, a.T - t.y);
     r.slot = 0;
     r.pos0 = t.y;
   }
   return r;
 }
 
-// MFMA on one K step from LDS: wave tile = (MT x 32 rows) x (NT x 32 cols).
-template <int MT, int NT, bool BF16>
-__device__ __forceinline__ void mma_step(const uint16_t* As, const uint16_t* Bs, int wm, int wn,
-                                         int lane, f32x16 (&acc)[MT][NT], int n_stride) {
+// ---------------------------------------------------------------- tokens
+// x (bf16) -> x16 (fp16) with K permuted inside each 32-wide block.
+template <int FMT>
+__global__ __launch_bounds__(256) void x16_kernel(const uint16_t* __restrict__ x, int64_t n_blocks,
+                                                  uint16_t* __restrict__ x16) {
+  const int64_t b = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (b >= n_blocks) return;
+  const u32x4* src = reinterpret_cast<const u32x4*>(x + b * 32);
+  uint32_t w[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const u32x4 v = src[q];
+    w[4 * q] = v[0]; w[4 * q + 1] = v[1]; w[4 * q + 2] = v[2]; w[4 * q + 3] = v[3];
+  }
+  uint16_t o[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const uint32_t bits = (w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+    o[perm_pos<FMT>(j)] = __builtin_bit_cast(uint16_t, _Float16(__uint_as_float(bits << 16)));
+  }
+  u32x4* dst = reinterpret_cast<u32x4*>(x16 + b * 32);
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    dst[q] = u32x4{uint32_t(o[8 * q]) | (uint32_t(o[8 * q + 1]) << 16),
+                   uint32_t(o[8 * q + 2]) | (uint32_t(o[8 * q + 3]) << 16),
+                   uint32_t(o[8 * q + 4]) | (uint32_t(o[8 * q + 5]) << 16),
+                   uint32_t(o[8 * q + 6]) | (uint32_t(o[8 * q + 7]) << 16)};
+}
+
+// ---------------------------------------------------------------- GEMM
+// One grouped-GEMM tile: 128 rows of one bucket x 256 weight rows (gate/up:
+// 128 gate + 128 up rows of 128 features; down: 256 output columns).  Each
+// wave holds all 128 rows x 64 columns (4 x 2 MFMA tiles), so every
+// dequantised weight feeds 4 MFMAs; two workgroups share a CU.
+constexpr int kBN = 256;          // weight rows per tile
+constexpr int kSdRow = 9;         // dwords per weight row in the scale table (8 + pad)
+constexpr int kGroup = 4;         // K steps per scale group (8 blocks)
+constexpr int kMT = kQM / 32;     // MFMA row tiles per wave
+
+template <int FMT, bool GU>
+__global__ __launch_bounds__(256, 2) void qgemm_kernel(GemmArgs a, int n_ntiles) {
+  constexpr int kCW = FMT == MOE_W_Q4B32 ? 4 : 2;   // code dwords of one block
+  __shared__ uint16_t As[2][kQM * kLdsRow];
+  __shared__ uint32_t Sd[2][kBN * kSdRow];   // d | m << 16 per (weight row, block of the group)
+  __shared__ int arow[kQM];
+  __shared__ int orow[kQM];      // down: pair_out row of each tile row
+  const int w = xcd_item();
+  const int total = *a.n_tiles * n_ntiles;
+  if (w >= total) return;
+  const int n_act = *a.act.count;
+  const int2 tinfo = a.tiles[w / n_ntiles];
+  const int nt = w % n_ntiles;
+  const RowMap rm = row_map(a, tinfo, n_act);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = GU ? a.H : a.I;
+  const int nk = K / kBK, nb = K / 32;
+  // A source rows: gate/up gathers token rows of x16; down reads h rows at
+  // the bucket positions.  Rows past the bucket read row 0 of the tile.
+  if (tid < kQM) {
+    const int r = tid < rm.rows ? tid : 0;
+    const int p = rm.shared ? rm.pos0 + r : a.bucket_pair[rm.pos0 + r];
+    arow[tid] = GU ? (rm.shared ? p : p / a.k) : rm.pos0 + r;
+    orow[tid] = p;
+  }
+  __syncthreads();
+  const uint16_t* abase = GU ? a.x16 : (rm.shared ? a.h_sh : a.h);
+  // A staging: 8 lanes per row (16 bytes each, a whole 128-byte K step);
+  // this thread's rows q * 32 + tid / 8, q = 0..3
+  const int achunk = tid & 7;
+  uint32_t aoff[kMT];
+#pragma unroll
+  for (int q = 0; q < kMT; ++q) aoff[q] = uint32_t(arow[q * 32 + (tid >> 3)]) * uint32_t(K) + achunk * 8;
+  // weight rows: tile row R = wave * 64 + j * 32 + col (j = MFMA column tile)
+  const MatView W0 = GU ? (rm.shared ? a.sg : a.g) : (rm.shared ? a.sd : a.d);
+  const MatView W1 = GU ? (rm.shared ? a.su : a.u) : W0;
+  const int slot = rm.shared ? 0 : rm.slot;
+  auto weight_row = [&](int R, const MatView*& Wm) {
+    const int wv = R >> 6, j = (R >> 5) & 1, c = R & 31;
+    if (GU) {
+      Wm = j ? &W1 : &W0;
+      return nt * 128 + wv * 32 + c;
+    }
+    Wm = &W0;
+    return nt * 256 + wv * 64 + j * 32 + c;
+  };
+  const int col = lane & 31, bh = lane >> 5;
+  const int64_t row_bytes = int64_t(K) * fmt_bits(FMT) / 8;
+  const uint8_t* cw[2];
+  int wrow0 = 0;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const MatView* Wm;
+    const int r = weight_row(wave * 64 + j * 32 + col, Wm);
+    if (j == 0) wrow0 = r;
+    cw[j] = Wm->codes + slot * Wm->mat_bytes + r * row_bytes;
+  }
+  // scale group staging: thread tid loads weight row tid's 8 scales and mins
+  const uint16_t *sg_sc, *sg_mn;
+  {
+    const MatView* Wm;
+    const int r = weight_row(tid, Wm);
+    const int64_t b = int64_t(slot) * Wm->mat_blocks + int64_t(r) * nb;
+    sg_sc = Wm->scale + b;
+    sg_mn = Wm->mn + b;
+  }
+
+  u32x4 ra1[kMT], ra2[kMT];      // A of K steps kt+1, kt+2 in flight
+  uint32_t wc[3][2][kCW];        // codes of K steps kt, kt+1, kt+2
+  u32x4 gsc, gmn;                // scales / mins of the next group in flight
+  auto load_a = [&](int kt, u32x4* ra) {
+#pragma unroll
+    for (int q = 0; q < kMT; ++q) ra[q] = *reinterpret_cast<const u32x4*>(abase + aoff[q] + kt * kBK);
+  };
+  auto store_a = [&](const u32x4* ra, int buf) {
+#pragma unroll
+    for (int q = 0; q < kMT; ++q)
+      *reinterpret_cast<u32x4*>(&As[buf][(q * 32 + (tid >> 3)) * kLdsRow + achunk * 8]) = ra[q];
+  };
+  auto load_codes = [&](int kt, uint32_t (*c)[kCW]) {
+    const int blk = 2 * kt + bh;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if constexpr (FMT == MOE_W_Q4B32) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(cw[j] + blk * 16);
+        c[j][0] = v[0]; c[j][1] = v[1]; c[j][2] = v[2]; c[j][3] = v[3];
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(cw[j] + blk * 8);
+        c[j][0] = v.x; c[j][1] = v.y;
+      }
+    }
+  };
+  auto load_group = [&](int g) {
+    gsc = *reinterpret_cast<const u32x4*>(sg_sc + 8 * g);
+    gmn = *reinterpret_cast<const u32x4*>(sg_mn + 8 * g);
+  };
+  auto store_group = [&](int buf) {
+    uint32_t* d = &Sd[buf][tid * kSdRow];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      d[2 * q] = (gsc[q] & 0xFFFFu) | (gmn[q] << 16);
+      d[2 * q + 1] = (gsc[q] >> 16) | (gmn[q] & 0xFFFF0000u);
+    }
+  };
+  f32x16 acc[kMT][2];
+#pragma unroll
+  for (int i = 0; i < kMT; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+  // Scale group g sits in Sd[g & 1] from the K step before its first one
+  // on; its loads are issued three K steps before that.
+  const int ngroups = nk / kGroup;
+  auto scales = [&](int kt, int j, f16x2& d2, f16x2& m2) {
+    const uint32_t dm = Sd[(kt / kGroup) & 1][(wave * 64 + j * 32 + col) * kSdRow + 2 * (kt % kGroup) + bh];
+    d2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(dm, dm, 0x01000100u));
+    m2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(dm, dm, 0x03020302u));
+  };
+  load_group(0);
+  load_a(0, ra1);
+  load_codes(0, wc[0]);
+  if (nk > 1) {
+    load_a(1, ra2);
+    load_codes(1, wc[1]);
+  }
+  store_group(0);
+  if (ngroups > 1) load_group(1);
+  store_a(ra1, 0);
+#pragma unroll
+  for (int q = 0; q < kMT; ++q) ra1[q] = ra2[q];
+  __syncthreads();
+  // weight operands of K step 0
+  f16x8 bv[2][4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    f16x2 d2, m2;
+    scales(0, j, d2, m2);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) bv[j][kk] = w_operand<FMT>(wc[0][j], kk, d2, m2);
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 2 < nk) {
+      load_a(kt + 2, ra2);
+      load_codes(kt + 2, wc[2]);
+    }
+    const bool more = kt + 1 < nk;
+    f16x2 dn[2], mn[2];   // scales of the next K step
+#pragma unroll
+    for (int j = 0; j < 2; ++j) scales(more ? kt + 1 : kt, j, dn[j], mn[j]);
+    const uint16_t* Ab = As[kt & 1];
+    // the next K step's weight operand kk is built while the MFMAs of kk
+    // run, in the registers those MFMAs have just read
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      f16x8 av[kMT];
+#pragma unroll
+      for (int i = 0; i < kMT; ++i)
+        av[i] = *reinterpret_cast<const f16x8*>(Ab + (i * 32 + col) * kLdsRow + bh * 32 + kk * 8);
+#pragma unroll
+      for (int i = 0; i < kMT; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j][kk], acc[i][j], 0, 0, 0);
+      if (more) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) bv[j][kk] = w_operand<FMT>(wc[1][j], kk, dn[j], mn[j]);
+      }
+    }
+    const int g = kt / kGroup, ks = kt % kGroup;
+    if (more) store_a(ra1, (kt + 1) & 1);
+    if (ks == kGroup - 2 && g + 1 < ngroups) {
+      store_group((g + 1) & 1);
+      if (g + 2 < ngroups) load_group(g + 2);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kMT; ++q) ra1[q] = ra2[q];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int c = 0; c < kCW; ++c) {
+        wc[0][j][c] = wc[1][j][c];
+        wc[1][j][c] = wc[2][j][c];
+      }
+  }
+  // epilogue: element v of lane l is row 8 (v / 4) + 4 (l / 32) + v % 4 of
+  // the 32 x 32 tile, column l % 32
+  if constexpr (GU) {
+    // h tile (128 rows x 128 features, fp16, features in the permuted order)
+    // through LDS, then whole 256-byte rows to global memory
+    constexpr int kHRow = 128 + 8;   // halves per LDS row
+    static_assert(kQM * kHRow <= 2 * kQM * kLdsRow, "h tile fits in the A buffers");
+    uint16_t* ht = &As[0][0];        // the A buffers are free after the last K step
+    const int fl = wave * 32 + col;  // feature within the tile
+    const int fcol = (fl & ~31) + perm_pos<FMT>(fl & 31);
+#pragma unroll
+    for (int i = 0; i < kMT; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = i * 32 + 8 * (v >> 2) + 4 * bh + (v & 3);
+        const float hv = silu_f32(acc[i][0][v]) * acc[i][1][v];
+        ht[row * kHRow + fcol] = __builtin_bit_cast(uint16_t, _Float16(hv));
+      }
+    __syncthreads();
+    uint16_t* out = (rm.shared ? a.h_sh : a.h) + int64_t(rm.pos0) * a.I + nt * 128;
+#pragma unroll
+    for (int q = 0; q < kQM * 16 / 256; ++q) {
+      const int c = q * 256 + tid, row = c >> 4, ch = c & 15;
+      if (row < rm.rows)
+        *reinterpret_cast<u32x4*>(out + int64_t(row) * a.I + ch * 8) =
+            *reinterpret_cast<const u32x4*>(ht + row * kHRow + ch * 8);
+    }
+  } else {
+    float* out = rm.shared ? a.shared_out : a.pair_out;
+#pragma unroll
+    for (int i = 0; i < kMT; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = i * 32 + 8 * (v >> 2) + 4 * bh + (v & 3);
+        if (row < rm.rows) {
+          const int64_t o = int64_t(orow[row]) * a.H + wrow0;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) out[o + 32 * j] = acc[i][j][v];
+        }
+      }
+  }
+}
+
+// MFMA on one K step from LDS (bf16 router): wave tile = (MT x 32 rows) x
+// (NT x 32 cols), A and B rows of kLdsRow halves.
+template <int MT, int NT>
+__device__ __forceinline__ void mma_step_bf16(const uint16_t* As, const uint16_t* Bs, int wm, int wn,
+                                              int lane, f32x16 (&acc)[MT][NT], int n_stride) {
 #pragma unroll
   for (int kk = 0; kk < kBK / 16; ++kk) {
     u32x4 av[MT], bv[NT];
@@ -170,201 +466,11 @@ __device__ __forceinline__ void mma_step(const uint16_t* As, const uint16_t* Bs,
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        if constexpr (BF16)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[i]),
-                                                              __builtin_bit_cast(bf16x8, bv[j]),
-                                                              acc[i][j], 0, 0, 0);
-        else
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, av[i]),
-                                                             __builtin_bit_cast(f16x8, bv[j]),
-                                                             acc[i][j], 0, 0, 0);
-      }
+      for (int j = 0; j < NT; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[i]),
+                                                            __builtin_bit_cast(bf16x8, bv[j]),
+                                                            acc[i][j], 0, 0, 0);
   }
-}
-
-// ---------------------------------------------------------------- gate/up
-// Tile: 128 rows x 64 features; B rows 0..63 = gate rows n0.., 64..127 = up.
-template <int FMT>
-__global__ __launch_bounds__(256) void gateup_gemm_kernel(GemmArgs a, int n_ntiles) {
-  __shared__ uint16_t As[2][kBM * kLdsRow];
-  __shared__ uint16_t Bs[2][128 * kLdsRow];
-  __shared__ int tok[kBM];
-  const int w = xcd_item();
-  const int total = *a.n_tiles * n_ntiles;
-  if (w >= total) return;
-  const int n_act = *a.act.count;
-  const int2 tinfo = a.tiles[w / n_ntiles];
-  const int n0 = (w % n_ntiles) * 64;
-  const RowMap rm = row_map(a, tinfo, n_act);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid < kBM) {
-    int t = 0;
-    if (tid < rm.rows) t = rm.shared ? rm.pos0 + tid : a.bucket_pair[rm.pos0 + tid] / a.k;
-    tok[tid] = t;
-  }
-  __syncthreads();
-  const bool up_row = (tid >> 1) >= 64;
-  const uint8_t* wcodes = rm.shared ? (up_row ? a.su.codes : a.sg.codes)
-                                    : (up_row ? a.u.codes : a.g.codes);
-  const uint16_t* wscale = rm.shared ? (up_row ? a.su.scale : a.sg.scale)
-                                     : (up_row ? a.u.scale : a.g.scale);
-  const uint16_t* wmin = rm.shared ? (up_row ? a.su.mn : a.sg.mn) : (up_row ? a.u.mn : a.g.mn);
-  const int64_t mat_bytes = a.g.mat_bytes, mat_blocks = a.g.mat_blocks;
-  const int K = a.H;
-  const int nk = K / kBK;
-  // this thread's A row (64 B) and B row block
-  const int ar = tid >> 1, ah = tid & 1;
-  const uint16_t* xrow = a.x + int64_t(tok[ar]) * K + ah * 32;
-  const int br = tid >> 1, bblk = tid & 1;          // B row 0..127, block 0..1 of the step
-  const int wrow = n0 + (br & 63);
-  const int64_t blk_base = int64_t(rm.slot) * mat_blocks + int64_t(wrow) * (K / 32);
-  const uint8_t* code_row = wcodes + rm.slot * mat_bytes + int64_t(wrow) * (K * fmt_bits(FMT) / 8);
-  Stage<FMT> st;
-  auto load = [&](int kt) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(xrow + kt * kBK);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) st.a[q] = src[q];
-    const int blk = kt * 2 + bblk;
-    if (FMT == MOE_W_Q4B32) {
-      const u32x4 c = *reinterpret_cast<const u32x4*>(code_row + blk * 16);
-      st.b[0] = c[0]; st.b[1] = c[1]; st.b[2] = c[2]; st.b[3] = c[3];
-    } else {
-      const uint2 c = *reinterpret_cast<const uint2*>(code_row + blk * 8);
-      st.b[0] = c.x; st.b[1] = c.y;
-    }
-    st.bs = wscale[blk_base + blk];
-    st.bm = wmin[blk_base + blk];
-  };
-  auto store = [&](int buf) {
-    u32x4* da = reinterpret_cast<u32x4*>(&As[buf][ar * kLdsRow + ah * 32]);
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      da[q] = u32x4{bf16x2_to_f16x2(st.a[q][0]), bf16x2_to_f16x2(st.a[q][1]),
-                    bf16x2_to_f16x2(st.a[q][2]), bf16x2_to_f16x2(st.a[q][3])};
-    u32x4 wv[4];
-    dequant_block<FMT>(st.b, st.bs, st.bm, wv);
-    u32x4* db = reinterpret_cast<u32x4*>(&Bs[buf][br * kLdsRow + bblk * 32]);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) db[q] = wv[q];
-  };
-  // waves: 2 (rows) x 2 (features); each: 64 rows x (32 gate + 32 up)
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 32;
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) load(kt + 1);
-    mma_step<2, 2, false>(As[kt & 1], Bs[kt & 1], wm, wn, lane, acc, 64);
-    if (kt + 1 < nk) store((kt + 1) & 1);
-    __syncthreads();
-  }
-  // epilogue: h = silu(gate) * up -> fp16
-  _Float16* out = rm.shared ? a.h_sh : a.h;
-  const int out_row0 = rm.pos0;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = wm + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      const int col = n0 + wn + (lane & 31);
-      if (row < rm.rows) {
-        const float g = acc[i][0][v], u = acc[i][1][v];
-        out[int64_t(out_row0 + row) * a.I + col] = _Float16(silu_f32(g) * u);
-      }
-    }
-}
-
-// ---------------------------------------------------------------- down
-// Tile: 128 rows x 128 output features over K = I.
-template <int FMT>
-__global__ __launch_bounds__(256) void down_gemm_kernel(GemmArgs a, int n_ntiles) {
-  __shared__ uint16_t As[2][kBM * kLdsRow];
-  __shared__ uint16_t Bs[2][128 * kLdsRow];
-  __shared__ int orow[kBM];
-  const int w = xcd_item();
-  const int total = *a.n_tiles * n_ntiles;
-  if (w >= total) return;
-  const int n_act = *a.act.count;
-  const int2 tinfo = a.tiles[w / n_ntiles];
-  const int n0 = (w % n_ntiles) * 128;
-  const RowMap rm = row_map(a, tinfo, n_act);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid < kBM) {
-    int o = -1;
-    if (tid < rm.rows) o = rm.shared ? rm.pos0 + tid : a.bucket_pair[rm.pos0 + tid];
-    orow[tid] = o;
-  }
-  __syncthreads();
-  const MatView D = rm.shared ? a.sd : a.d;
-  const int K = a.I;
-  const int nk = K / kBK;
-  const int ar = tid >> 1, ah = tid & 1;
-  const _Float16* hsrc = rm.shared ? a.h_sh : a.h;
-  const int arow = ar < rm.rows ? rm.pos0 + ar : rm.pos0;   // rows past the bucket read a valid row
-  const _Float16* hrow = hsrc + int64_t(arow) * K + ah * 32;
-  const int br = tid >> 1, bblk = tid & 1;
-  const int wrow = n0 + br;
-  const int64_t blk_base = int64_t(rm.slot) * D.mat_blocks + int64_t(wrow) * (K / 32);
-  const uint8_t* code_row = D.codes + rm.slot * D.mat_bytes + int64_t(wrow) * (K * fmt_bits(FMT) / 8);
-  Stage<FMT> st;
-  auto load = [&](int kt) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(hrow + kt * kBK);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) st.a[q] = src[q];
-    const int blk = kt * 2 + bblk;
-    if (FMT == MOE_W_Q4B32) {
-      const u32x4 c = *reinterpret_cast<const u32x4*>(code_row + blk * 16);
-      st.b[0] = c[0]; st.b[1] = c[1]; st.b[2] = c[2]; st.b[3] = c[3];
-    } else {
-      const uint2 c = *reinterpret_cast<const uint2*>(code_row + blk * 8);
-      st.b[0] = c.x; st.b[1] = c.y;
-    }
-    st.bs = D.scale[blk_base + blk];
-    st.bm = D.mn[blk_base + blk];
-  };
-  auto store = [&](int buf) {
-    u32x4* da = reinterpret_cast<u32x4*>(&As[buf][ar * kLdsRow + ah * 32]);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) da[q] = st.a[q];
-    u32x4 wv[4];
-    dequant_block<FMT>(st.b, st.bs, st.bm, wv);
-    u32x4* db = reinterpret_cast<u32x4*>(&Bs[buf][br * kLdsRow + bblk * 32]);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) db[q] = wv[q];
-  };
-  // waves 2 x 2, each 64 rows x 64 features
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) load(kt + 1);
-    mma_step<2, 2, false>(As[kt & 1], Bs[kt & 1], wm, wn, lane, acc, 32);
-    if (kt + 1 < nk) store((kt + 1) & 1);
-    __syncthreads();
-  }
-  float* out = rm.shared ? a.shared_out : a.pair_out;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = wm + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        const int col = n0 + wn + j * 32 + (lane & 31);
-        if (row < rm.rows) out[int64_t(orow[row]) * a.H + col] = acc[i][j][v];
-      }
 }
 
 // ---------------------------------------------------------------- router
@@ -411,7 +517,7 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     if (kt + 1 < nk) load(kt + 1);
-    mma_step<2, 2, true>(As[kt & 1], Bs[kt & 1], wm, wn, lane, acc, 32);
+    mma_step_bf16<2, 2>(As[kt & 1], Bs[kt & 1], wm, wn, lane, acc, 32);
     if (kt + 1 < nk) store((kt + 1) & 1);
     __syncthreads();
   }
@@ -428,47 +534,57 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
 }
 
 template <int FMT>
-hipError_t launch_gemm_fmt(const GemmArgs& ga, int max_tiles, hipStream_t st) {
-  const int nt_gu = ga.I / 64, nt_d = ga.H / 128;
-  hipLaunchKernelGGL(gateup_gemm_kernel<FMT>, dim3(round_xcd(max_tiles * nt_gu)), dim3(256), 0, st,
+hipError_t launch_gemm_fmt(const GemmArgs& ga, const uint16_t* x, int max_tiles, hipStream_t st) {
+  const int64_t n_blocks = int64_t(ga.T) * ga.H / 32;
+  hipLaunchKernelGGL(x16_kernel<FMT>, dim3(unsigned((n_blocks + 255) / 256)), dim3(256), 0, st, x,
+                     n_blocks, const_cast<uint16_t*>(ga.x16));
+  const int nt_gu = ga.I / 128, nt_d = ga.H / 256;
+  hipLaunchKernelGGL((qgemm_kernel<FMT, true>), dim3(round_xcd(max_tiles * nt_gu)), dim3(256), 0, st,
                      ga, nt_gu);
-  hipLaunchKernelGGL(down_gemm_kernel<FMT>, dim3(round_xcd(max_tiles * nt_d)), dim3(256), 0, st, ga,
-                     nt_d);
+  hipLaunchKernelGGL((qgemm_kernel<FMT, false>), dim3(round_xcd(max_tiles * nt_d)), dim3(256), 0, st,
+                     ga, nt_d);
   return hipGetLastError();
+}
+
+int gemm_max_tiles(int T, int k, int S) {
+  const int64_t P = int64_t(T) * k;
+  return int(P / kQM + (P < S ? P : S) + T / kQM + 2);
 }
 
 }  // namespace
 
-// Workspace: tile list then fp16 h (positions) then fp16 shared h.
+// Workspace: tile list, fp16 h (bucket positions, then the shared expert's
+// rows), fp16 tokens.
 size_t ffn_gemm_ws(int T, int k, int H, int I, int S) {
-  (void)H;
   const int64_t P = int64_t(T) * k;
-  const int64_t max_tiles = P / kBM + (P < S ? P : S) + T / kBM + 2;
-  return size_t(max_tiles * 8 + 8) + 256 + size_t(P + T) * I * 2 + 256;
+  const size_t tiles = (size_t(gemm_max_tiles(T, k, S)) * 8 + 8 + 255) / 256 * 256;
+  const size_t h = (size_t(P + T) * I * 2 + 255) / 256 * 256;
+  return tiles + h + size_t(T) * H * 2;
 }
 
+// K of both GEMMs a multiple of 256 (whole groups of 8 scale blocks); the
+// gate/up tile covers 128 features, the down tile 256 columns.
 bool ffn_gemm_ok(int fmt, int H, int I) {
-  return (fmt == MOE_W_Q2B32 || fmt == MOE_W_Q4B32) && H % 128 == 0 && I % 64 == 0;
+  return (fmt == MOE_W_Q2B32 || fmt == MOE_W_Q4B32) && H % 256 == 0 && I % 256 == 0;
 }
 
 hipError_t launch_ffn_gemm(const FfnArgs& f, int S, const int32_t* bucket_off, void* ws,
                            hipStream_t st) {
   (void)bucket_off;
   const int64_t P = int64_t(f.T) * f.k;
-  const int max_tiles = int(P / kBM + (P < S ? P : S) + f.T / kBM + 2);
+  const int max_tiles = gemm_max_tiles(f.T, f.k, S);
   uint8_t* base = static_cast<uint8_t*>(ws);
   int* n_tiles = reinterpret_cast<int*>(base);
   int2* tiles = reinterpret_cast<int2*>(base + 8);
-  size_t off = (size_t(max_tiles) * 8 + 8 + 255) / 256 * 256;
-  _Float16* h = reinterpret_cast<_Float16*>(base + off);
-  _Float16* h_sh = h + P * f.I;
+  const size_t off = (size_t(max_tiles) * 8 + 8 + 255) / 256 * 256;
+  uint16_t* h = reinterpret_cast<uint16_t*>(base + off);
+  uint16_t* x16 = reinterpret_cast<uint16_t*>(base + off + (size_t(P + f.T) * f.I * 2 + 255) / 256 * 256);
   GemmArgs ga;
-  ga.x = f.x;
+  ga.x16 = x16;
   ga.T = f.T;
   ga.k = f.k;
   ga.H = f.H;
   ga.I = f.I;
-  ga.fmt = f.fmt;
   ga.g = f.g; ga.u = f.u; ga.d = f.d;
   ga.sg = f.sg; ga.su = f.su; ga.sd = f.sd;
   ga.act = f.act;
@@ -476,15 +592,15 @@ hipError_t launch_ffn_gemm(const FfnArgs& f, int S, const int32_t* bucket_off, v
   ga.tiles = tiles;
   ga.n_tiles = n_tiles;
   ga.h = h;
-  ga.h_sh = h_sh;
+  ga.h_sh = h + P * f.I;
   ga.pair_out = f.pair_out;
   ga.shared_out = f.shared_out;
   const int has_sh = f.sg.codes != nullptr ? 1 : 0;
   hipLaunchKernelGGL(gemm_schedule_kernel, dim3(1), dim3(1024), 0, st, f.act, f.T, has_sh, tiles,
                      n_tiles);
   switch (f.fmt) {
-    case MOE_W_Q4B32: return launch_gemm_fmt<MOE_W_Q4B32>(ga, max_tiles, st);
-    case MOE_W_Q2B32: return launch_gemm_fmt<MOE_W_Q2B32>(ga, max_tiles, st);
+    case MOE_W_Q4B32: return launch_gemm_fmt<MOE_W_Q4B32>(ga, f.x, max_tiles, st);
+    case MOE_W_Q2B32: return launch_gemm_fmt<MOE_W_Q2B32>(ga, f.x, max_tiles, st);
     default: return hipErrorInvalidValue;
   }
 }
