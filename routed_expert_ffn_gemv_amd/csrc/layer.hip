@@ -519,6 +519,36 @@ __device__ __forceinline__ void chunk_dot(u32x4 w, const uint32_t* xv, float* p)
   }
 }
 
+// One code chunk against the hi and lo halves of a split vector: each code
+// pair is unpacked once for both; p[bb] returns the sum of the two.
+template <int FMT>
+__device__ __forceinline__ void chunk_dot_hl(u32x4 w, const uint32_t* xh, const uint32_t* xl,
+                                             float* p) {
+  w = fresh(w);
+  const u32x4* h4 = reinterpret_cast<const u32x4*>(xh);
+  const u32x4* l4 = reinterpret_cast<const u32x4*>(xl);
+#pragma unroll
+  for (int bb = 0; bb < (FMT == MOE_W_Q2B32 ? 2 : 1); ++bb) {
+    u32x4 hh[4], ll[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      hh[q] = h4[4 * bb + q];
+      ll[q] = l4[4 * bb + q];
+    }
+    float a[4] = {0.f, 0.f, 0.f, 0.f}, c[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t pr = FMT == MOE_W_Q2B32 ? q2_pair(w[2 * bb + (q >> 1)], (q & 1) * 4 + e)
+                                                : q4_pair(w[q], e);
+        a[e] = dot2_bf16(pr, hh[q][e], a[e]);
+        c[e] = dot2_bf16(pr, ll[q][e], c[e]);
+      }
+    p[bb] = ((a[0] + a[1]) + (a[2] + a[3])) + ((c[0] + c[1]) + (c[2] + c[3]));
+  }
+}
+
 // The same for two code chunks (gate and up rows) against one vector chunk.
 template <int FMT>
 __device__ __forceinline__ void chunk_dot2(u32x4 wg, u32x4 wu, const uint32_t* xv,
@@ -578,6 +608,34 @@ __device__ __forceinline__ float row_vec_dot(const RowRegs<FMT, NCH>& R, int nch
       const float d = f16_to_f32(uint16_t(R.sc[j]));
       const float m = f16_to_f32(uint16_t(R.mn[j])) - 128.f * d;
       acc += d * p[0] + m * sv_base[c];
+    }
+  }
+  return acc;
+}
+
+// One row . a vector split into hi and lo bf16 halves (staged at xh / xl
+// with block sums sh / sl): the down projection of fp32 h in one pass.
+template <int FMT, int NCH>
+__device__ __forceinline__ float row_vec_dot_hl(const RowRegs<FMT, NCH>& R, int nch, int lane_g,
+                                                int lpr, const uint32_t* xh, const float* sh,
+                                                const uint32_t* xl, const float* sl) {
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    if (j >= nch) continue;
+    const int c = lane_g + j * lpr;
+    float p[2];
+    chunk_dot_hl<FMT>(R.w[j], xh + c * Fmt<FMT>::kCS, xl + c * Fmt<FMT>::kCS, p);
+    if constexpr (FMT == MOE_W_Q2B32) {
+      const float d0 = f16_to_f32(uint16_t(R.sc[j] & 0xFFFFu));
+      const float d1 = f16_to_f32(uint16_t(R.sc[j] >> 16));
+      const float m0 = f16_to_f32(uint16_t(R.mn[j] & 0xFFFFu)) - 128.f * d0;
+      const float m1 = f16_to_f32(uint16_t(R.mn[j] >> 16)) - 128.f * d1;
+      acc += (d0 * p[0] + m0 * (sh[2 * c] + sl[2 * c])) + (d1 * p[1] + m1 * (sh[2 * c + 1] + sl[2 * c + 1]));
+    } else {
+      const float d = f16_to_f32(uint16_t(R.sc[j]));
+      const float m = f16_to_f32(uint16_t(R.mn[j])) - 128.f * d;
+      acc += d * p[0] + m * (sh[c] + sl[c]);
     }
   }
   return acc;
@@ -710,16 +768,16 @@ __device__ __forceinline__ void router_load(RouterRegs<FMT>& R, const LayerArgs&
 // Logits of the task's rows for every token, published as tagged words
 // once this wave's zeroes of y have landed (a workgroup adds into y only
 // after it has seen every logit).
-template <int FMT>
+template <int FMT, int TB>
 __device__ __forceinline__ void router_compute(const RouterRegs<FMT>& R, const LayerArgs& a,
                                                int task, const uint32_t* xs, int vstride,
                                                int lane, uint32_t epoch) {
   const int lpr = router_lpr<FMT>(a.H);
   const int e = task * (64 / lpr) + lane / lpr;
   const int lane_g = lane % lpr;
-  float acc[kTMax];
+  float acc[TB];
 #pragma unroll
-  for (int t = 0; t < kTMax; ++t) acc[t] = 0.f;
+  for (int t = 0; t < TB; ++t) acc[t] = 0.f;
   if (e < a.E) {
     if constexpr (FMT == MOE_W_Q2B32 || FMT == MOE_W_Q4B32) {
       constexpr int kQ = RouterRegs<FMT>::kQ;
@@ -742,7 +800,7 @@ __device__ __forceinline__ void router_compute(const RouterRegs<FMT>& R, const L
           pr[g * kS + 2 * m + 1] = __builtin_amdgcn_perm(hi_w, lo_w, 0x07060302u);
         }
 #pragma unroll
-      for (int t = 0; t < kTMax; ++t) {
+      for (int t = 0; t < TB; ++t) {
         if (t < a.T) {
           const uint32_t* xv = xs + t * vstride + lane_g * Fmt<FMT>::kCS;
           float s4[4] = {0.f, 0.f, 0.f, 0.f};
@@ -758,14 +816,14 @@ __device__ __forceinline__ void router_compute(const RouterRegs<FMT>& R, const L
                              ? static_cast<const float*>(a.W)[int64_t(e) * a.H + col]
                              : bf16_to_f32(static_cast<const uint16_t*>(a.W)[int64_t(e) * a.H + col]);
 #pragma unroll
-        for (int t = 0; t < kTMax; ++t)
+        for (int t = 0; t < TB; ++t)
           if (t < a.T) acc[t] = fmaf(wv, xf[t * vstride + col], acc[t]);
       }
     }
   }
   wait_mem();
 #pragma unroll
-  for (int t = 0; t < kTMax; ++t) {
+  for (int t = 0; t < TB; ++t) {
     if (t < a.T) {
       float s = acc[t];
       for (int m = 1; m < lpr; m <<= 1) s += __shfl_xor(s, m, 64);
@@ -925,7 +983,9 @@ __device__ __forceinline__ void resolve_block(const LayerArgs& a, Lds& L, int P,
 }
 
 // --------------------------------------------------------------- kernel
-template <int FMT>
+// TB: the largest token count the instance serves (1, 4 or 16), so per-token
+// loops are unrolled no further than needed.
+template <int FMT, int TB>
 __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   constexpr int kLprGU = Lanes<FMT>::kGU, kRowsGU = Lanes<FMT>::kRowsGU;
   constexpr int kLprD = Lanes<FMT>::kD, kRowsD = Lanes<FMT>::kRowsD;
@@ -981,7 +1041,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   for (int task = task0; task < n_a; task += kWaves * G) {
     if (task < n_router) {
       if (task != task0) router_load<FMT>(rr, a, task, n_router, lane);
-      router_compute<FMT>(rr, a, task, xs, vstride, lane, epoch);
+      router_compute<FMT, TB>(rr, a, task, xs, vstride, lane, epoch);
     } else {
       const int i = (task - n_router) * kRowsGU + lane / kLprGU;
       if (task != task0) gateup_load<FMT>(rg, ru, a, a.sg, a.su, 0, i, lane_gu);
@@ -997,7 +1057,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   // ---- B: every logit of this call, then routing
   {
     const int n_lg = T * E;
-    constexpr int kR = kTMax * kEMax / kThreads / 2;
+    constexpr int kR = TB * kEMax / kThreads > 16 ? 16 : TB * kEMax / kThreads;
     for (int base = 0; base < n_lg; base += kR * kThreads) {
       uint64_t w[kR];
 #pragma unroll
@@ -1136,11 +1196,13 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
       stage_h<FMT>(srcs, n, Kd, xd, sd, pd, vs_d, epoch);
       __syncthreads();
       for (int v = 0; v < n; ++v) {
-        float o = row_vec_dot<FMT, kNChMax>(rd, nch_d, lane_gd, kLprD, xd + (kVPP * v) * vs_d,
-                                            sd + (kVPP * v) * ss_d);
-        if (kVPP == 2)
-          o += row_vec_dot<FMT, kNChMax>(rd, nch_d, lane_gd, kLprD, xd + (kVPP * v + 1) * vs_d,
-                                         sd + (kVPP * v + 1) * ss_d);
+        float o;
+        if constexpr (kVPP == 2)
+          o = row_vec_dot_hl<FMT, kNChMax>(rd, nch_d, lane_gd, kLprD, xd + (2 * v) * vs_d,
+                                           sd + (2 * v) * ss_d, xd + (2 * v + 1) * vs_d,
+                                           sd + (2 * v + 1) * ss_d);
+        else
+          o = row_vec_dot<FMT, kNChMax>(rd, nch_d, lane_gd, kLprD, xd + v * vs_d, sd + v * ss_d);
         o = group_sum<kLprD>(o);
         if (r < a.H && lane_gd == 0) {
           const int t = shared ? v : L.tok[st + v];
@@ -1169,19 +1231,18 @@ struct Occ {
   int grid = 0;
 };
 
-template <int FMT>
+template <int FMT, int TB>
 hipError_t launch_fmt(const LayerArgs& a, size_t lds, hipStream_t st, int* grid_out) {
-  static thread_local Occ cache[3];
-  Occ& c = cache[FMT == MOE_W_F32 ? 0 : FMT == MOE_W_Q2B32 ? 1 : 2];
+  static thread_local Occ c;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (c.lds != lds || c.device != dev) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_layer_kernel<FMT>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_layer_kernel<FMT, TB>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return e;
     int per_cu = 0, cus = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, moe_layer_kernel<FMT>, kThreads,
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, moe_layer_kernel<FMT, TB>, kThreads,
                                                      lds);
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -1193,8 +1254,15 @@ hipError_t launch_fmt(const LayerArgs& a, size_t lds, hipStream_t st, int* grid_
     c.grid = cus;   // one workgroup of 8 waves per CU
   }
   if (grid_out) *grid_out = c.grid;
-  hipLaunchKernelGGL(moe_layer_kernel<FMT>, dim3(c.grid), dim3(kThreads), lds, st, a);
+  hipLaunchKernelGGL((moe_layer_kernel<FMT, TB>), dim3(c.grid), dim3(kThreads), lds, st, a);
   return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_tb(const LayerArgs& a, size_t lds, hipStream_t st, int* grid_out) {
+  if (a.T <= 1) return launch_fmt<FMT, 1>(a, lds, st, grid_out);
+  if (a.T <= 4) return launch_fmt<FMT, 4>(a, lds, st, grid_out);
+  return launch_fmt<FMT, kTMax>(a, lds, st, grid_out);
 }
 
 size_t vec_bytes(int fmt, int K) {
@@ -1234,9 +1302,9 @@ bool layer_fused_ok(int fmt, int T, int k, int E, int H, int I) {
 hipError_t launch_layer_fused(const LayerArgs& a, int fmt, hipStream_t st, int* grid) {
   const size_t lds = layer_fused_lds(fmt, a.T, a.E, a.H, a.I);
   switch (fmt) {
-    case MOE_W_Q2B32: return launch_fmt<MOE_W_Q2B32>(a, lds, st, grid);
-    case MOE_W_Q4B32: return launch_fmt<MOE_W_Q4B32>(a, lds, st, grid);
-    case MOE_W_F32: return launch_fmt<MOE_W_F32>(a, lds, st, grid);
+    case MOE_W_Q2B32: return launch_tb<MOE_W_Q2B32>(a, lds, st, grid);
+    case MOE_W_Q4B32: return launch_tb<MOE_W_Q4B32>(a, lds, st, grid);
+    case MOE_W_F32: return launch_fmt<MOE_W_F32, kTMax>(a, lds, st, grid);
     default: return hipErrorInvalidValue;
   }
 }
