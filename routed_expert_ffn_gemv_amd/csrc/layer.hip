@@ -230,60 +230,23 @@ __device__ __forceinline__ void wave_topk(const float* l, int E, int k, int lane
   *v_out = my_v;
 }
 
-// Top-k of one token over E <= 512 logits with every wave of the block:
-// wave w keeps the k best of experts [64w, 64w + 64) (one key per lane, no
-// sorting), then wave 0 picks the k best of those 8 sorted lists (two keys
-// per lane).  The same choices and order as wave_topk; k <= 16.  Lane j < k
-// of wave 0 returns the j-th choice.  Called by every thread of the block.
+// Largest k that the threshold selection serves (k <= 32 is required by its
+// threshold step; the per-wave selection takes larger k).
 constexpr int kTopkListMax = 16;
-__device__ __forceinline__ void block_topk_one(const float* l, int E, int k, int wave, int lane,
-                                               uint64_t* cand, int* e_out, float* v_out) {
-  {
-    const int e = wave * 64 + lane;
-    uint64_t key = e < E ? (uint64_t(ordered_bits(l[e])) << 32) | uint64_t(~uint32_t(e)) : 0ull;
-    for (int j = 0; j < k; ++j) {
-      const Pick pk = wave_pick(uint32_t(key >> 32), uint32_t(key));
-      if (lane == 0) cand[wave * kTopkListMax + j] = (uint64_t(pk.hv) << 32) | pk.lo;
-      if (lane == pk.owner) key = 0ull;
-    }
-  }
-  __syncthreads();
-  int my_e = 0;
-  float my_v = 0.f;
-  if (wave == 0) {
-    // lane = (list, pair of positions); each list is already descending
-    const int list = lane >> 3, pos = 2 * (lane & 7);
-    uint64_t k0 = pos < k ? cand[list * kTopkListMax + pos] : 0ull;
-    uint64_t k1 = pos + 1 < k ? cand[list * kTopkListMax + pos + 1] : 0ull;
-    for (int j = 0; j < k; ++j) {
-      const Pick pk = wave_pick(uint32_t(k0 >> 32), uint32_t(k0));
-      if (lane == j) {
-        my_e = int(~pk.lo);
-        my_v = key_value(pk.hv);
-      }
-      if (lane == pk.owner) {
-        k0 = k1;
-        k1 = 0ull;
-      }
-    }
-  }
-  *e_out = my_e;
-  *v_out = my_v;
-}
 
 struct Lds {
-  int idx[kPMax];
+  int idx[kPMax];        // choices (token-major); logits until the gates are made
   float gate[kPMax];
-  int slot[kPMax];
-  int sorted[kPMax];
-  int bpair[kPMax];      // hit pairs sorted by (slot, t, j)
+  int bpair[kPMax];      // hit pairs grouped by bucket
   int tok[kPMax];        // their tokens
-  int act_slot[kPMax];   // distinct hit slots, ascending
+  int act_slot[kPMax];   // the buckets' slots
   int act_start[kPMax + 1];
   int slot_of[kEMax];    // the slot table (when the layer has one)
-  uint64_t cand[8 * kTopkListMax];   // per-wave top-k lists of block_topk_one
-  int ptok[kPMax];       // token of each pair
-  int tmp[32];
+  uint32_t emask[kEMax]; // per expert: tokens that chose it | bucket start << 16
+  uint64_t rkey[kThreads];   // segment maxima, then candidates (top-k)
+  uint64_t tau[kTMax];       // per-token thresholds
+  int ncand[kTMax];          // per-token candidate counts
+  uint32_t tmp[32];
   int n_act;
   uint32_t calls;
 };
@@ -838,60 +801,125 @@ __device__ __forceinline__ int slot_of_choice(const LayerArgs& a, const Lds& L, 
   return (s >= 0 && s < a.S) ? s : -1;
 }
 
-// Resolution of P <= 64 pairs by wave 0 alone, lane p = pair p: ballots give
-// the miss positions; bucket positions and distinct slots come from one
-// pass over the pairs with their slots read as scalars.
-__device__ __forceinline__ void resolve_wave(const LayerArgs& a, Lds& L, int P, int lane,
-                                             bool writer) {
-  const int p = lane;
-  const bool valid = p < P;
-  const int tok = valid ? L.ptok[p] : 0;
-  const bool first_of_token = valid && (p == 0 || L.ptok[p - 1] != tok);
-  const int s = valid ? slot_of_choice(a, L, L.idx[p]) : -1;
-  const bool hit = s >= 0;
-  const uint64_t miss_mask = __ballot(valid && !hit);
-  const int mpos = __builtin_amdgcn_mbcnt_hi(uint32_t(miss_mask >> 32),
-                                             __builtin_amdgcn_mbcnt_lo(uint32_t(miss_mask), 0u));
-  const int n_miss = __popcll(miss_mask);
-  if (writer) {
-    if (valid && a.slot_idx) a.slot_idx[p] = s;
-    if (valid && !hit) {
-      moe_miss m;
-      m.expert = L.idx[p];
-      m.token = tok;
-      m.gate = L.gate[p];
-      a.miss[mpos] = m;
+// ---- top-k of every token: threshold, candidates, ranks
+// Keys are (order-preserving logit bits << 32) | ~expert: unique, so the
+// largest key is the largest logit and, among equal logits, the lowest id.
+__device__ __forceinline__ uint64_t logit_key(const float* l, int e) {
+  return (uint64_t(ordered_bits(l[e])) << 32) | uint64_t(~uint32_t(e));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t key_max_dpp(uint64_t v) {
+  const uint64_t p = (uint64_t(dpp_u32<CTRL>(uint32_t(v >> 32))) << 32) | dpp_u32<CTRL>(uint32_t(v));
+  return p > v ? p : v;
+}
+
+// Token t < T is served by the GS = kThreads / TB threads [t*GS, (t+1)*GS);
+// thread j of them holds the keys e = j + GS*i.  Three barriered steps, then
+// the ranks:
+//  1. the largest key of each of 32 segments (GS/32 neighbouring threads);
+//  2. tau = the k-th largest of those 32 maxima.  k distinct keys (the
+//     maxima of k segments) are >= tau, so all of the token's k best are;
+//  3. the keys >= tau are appended to the token's candidate list (at most
+//     CAP = kThreads / TB kept, the count in L.ncand);
+//  4. a candidate's rank among the candidates is its place in the top-k.
+// L.idx[t*k + r] and L.gate[t*k + r] receive the r-th choice and its logit.
+// A token with more than CAP candidates (many equal logits) is left to the
+// caller.  Called by every thread; k <= kTopkListMax.
+template <int TB>
+__device__ __forceinline__ void topk_threshold(const float* lg, int T, int E, int k, Lds& L) {
+  constexpr int GS = kThreads / TB, SL = GS / 32, CAP = kThreads / TB;
+  const int tid = threadIdx.x, t = tid / GS, j = tid % GS;
+  const bool on = t < T;
+  const float* l = lg + t * E;
+  uint64_t m = 0;
+  if (on)
+    for (int e = j; e < E; e += GS) {
+      const uint64_t key = logit_key(l, e);
+      m = key > m ? key : m;
     }
-    if (first_of_token) a.miss_off[tok] = mpos;
-    if (p == 0) a.miss_off[a.T] = n_miss;
-  }
-  int pos = 0;
-  bool first = hit;
-  for (int q = 0; q < P; ++q) {
-    const int sq = __builtin_amdgcn_readlane(s, q);
-    if (sq >= 0) {
-      pos += (sq < s || (sq == s && q < p)) ? 1 : 0;
-      first = first && !(sq == s && q < p);
+  if constexpr (SL >= 2) m = key_max_dpp<0xB1>(m);    // quad_perm [1,0,3,2]
+  if constexpr (SL >= 4) m = key_max_dpp<0x4E>(m);    // quad_perm [2,3,0,1]
+  if constexpr (SL >= 8) m = key_max_dpp<0x141>(m);   // row_half_mirror
+  if constexpr (SL >= 16) m = key_max_dpp<0x140>(m);  // row_mirror
+  if (on && j % SL == 0) L.rkey[t * 32 + j / SL] = m;
+  __syncthreads();
+  {
+    const int tt = tid / 32, sg = tid % 32;
+    if (tt < T) {
+      const uint64_t* sk = L.rkey + tt * 32;
+      const uint64_t my = sk[sg];
+      int gt = 0, eq = 0;
+#pragma unroll
+      for (int q = 0; q < 32; ++q) {
+        const uint64_t o = sk[q];
+        gt += o > my ? 1 : 0;
+        eq += o == my ? 1 : 0;
+      }
+      // empty segments share the key 0; their writers agree
+      if (gt <= k - 1 && k - 1 < gt + eq) L.tau[tt] = my;
     }
   }
-  const uint64_t first_mask = __ballot(hit && first);
-  int apos = 0;
-  for (int q = 0; q < P; ++q)
-    if ((first_mask >> q) & 1ull) apos += __builtin_amdgcn_readlane(s, q) < s ? 1 : 0;
-  if (hit) {
-    L.bpair[pos] = p;
-    L.tok[pos] = tok;
-    L.sorted[pos] = s;
+  __syncthreads();
+  if (on) {
+    const uint64_t tau = L.tau[t];
+    for (int e = j; e < E; e += GS) {
+      const uint64_t key = logit_key(l, e);
+      if (key >= tau) {
+        const int pos = atomicAdd(&L.ncand[t], 1);
+        if (pos < CAP) L.rkey[t * CAP + pos] = key;
+      }
+    }
   }
-  if (hit && first) {
-    L.act_slot[apos] = s;
-    L.act_start[apos] = pos;
+  __syncthreads();
+  if (on) {
+    const int n = L.ncand[t];
+    if (n <= CAP) {
+      const uint64_t* ck = L.rkey + t * CAP;
+      for (int c = j; c < n; c += GS) {
+        const uint64_t my = ck[c];
+        int r = 0;
+        for (int q = 0; q < n; ++q) r += ck[q] > my ? 1 : 0;
+        if (r < k) {
+          L.idx[t * k + r] = int(~uint32_t(my));
+          L.gate[t * k + r] = key_value(uint32_t(my >> 32));
+        }
+      }
+    }
   }
-  if (p == 0) {
-    const int n_act = __popcll(first_mask);
-    L.act_start[n_act] = P - n_miss;
-    L.n_act = n_act;
+}
+
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u));
+}
+
+// Exclusive scan of one value per thread over the workgroup: a DPP scan in
+// each wave (row shifts, then the row broadcasts), wave totals through LDS.
+// *total receives the sum.  Called by every thread; one barrier.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_shift(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, ROWS, 0xF, true));
+}
+__device__ __forceinline__ uint32_t block_scan_u32(uint32_t v, uint32_t* wtot, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t x = v;
+  x += dpp_shift<0x111, 0xF>(x);   // row_shr:1
+  x += dpp_shift<0x112, 0xF>(x);   // row_shr:2
+  x += dpp_shift<0x114, 0xF>(x);   // row_shr:4
+  x += dpp_shift<0x118, 0xF>(x);   // row_shr:8
+  x += dpp_shift<0x142, 0xA>(x);   // row_bcast:15 into rows 1 and 3
+  x += dpp_shift<0x143, 0xC>(x);   // row_bcast:31 into rows 2 and 3
+  if (lane == 63) wtot[wave] = x;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const uint32_t c = wtot[w];
+    before += w < wave ? c : 0u;
+    all += c;
   }
+  *total = all;
+  return before + x - v;
 }
 
 // Resolution of one token's k choices by the wave that chose them (lane j
@@ -934,51 +962,72 @@ __device__ __forceinline__ void resolve_one(const LayerArgs& a, Lds& L, int e, f
   }
 }
 
-// Resolution of up to 256 pairs by the whole workgroup (thread p = pair p).
-__device__ __forceinline__ void resolve_block(const LayerArgs& a, Lds& L, int P, bool writer) {
-  const int p = threadIdx.x;
-  const int tok = p < P ? L.ptok[p] : 0;
-  const bool first_of_token = p < P && (p == 0 || L.ptok[p - 1] != tok);
-  const int s = p < P ? slot_of_choice(a, L, L.idx[p]) : -1;
-  if (writer && p < P && a.slot_idx) a.slot_idx[p] = s;
-  if (p < kPMax) L.slot[p] = s;
-  const int is_miss = (p < P && s < 0) ? 1 : 0;
-  int n_miss;
-  const int mpos = block_exclusive_scan(is_miss, L.tmp, &n_miss);
+// Resolution of the P = T*k pairs of T >= 2 tokens (thread p = pair p).
+// Misses keep pair order (a ballot scan).  Hits are bucketed by expert, the
+// buckets in ascending expert order, each bucket's pairs in token order (a
+// token chooses an expert at most once): every expert gathers the mask of
+// the tokens that chose it, and one scan over the experts of (bucket
+// exists, bucket size) places the buckets and their pairs.  L.emask must be
+// zero on entry; three barriers.
+__device__ __forceinline__ void resolve_multi(const LayerArgs& a, Lds& L, int P, bool writer) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int k = a.k, E = a.E;
+  const bool valid = tid < P;
+  const int e = valid ? L.idx[tid] : 0;
+  const int t = valid ? tid / k : 0;
+  const int s = valid ? slot_of_choice(a, L, e) : -1;
+  const bool hit = s >= 0;
+  if (hit) atomicOr(&L.emask[e], 1u << t);
+  const uint64_t mm = __ballot(valid && !hit);
+  if (lane == 0) L.tmp[wave] = uint32_t(__popcll(mm));
+  __syncthreads();
+  int mpos = lanes_below(mm), n_miss = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int c = int(L.tmp[w]);
+    mpos += w < wave ? c : 0;
+    n_miss += c;
+  }
   if (writer) {
-    if (is_miss) {
+    if (valid && a.slot_idx) a.slot_idx[tid] = s;
+    if (valid && !hit) {
       moe_miss m;
-      m.expert = L.idx[p];
-      m.token = tok;
-      m.gate = L.gate[p];
+      m.expert = e;
+      m.token = t;
+      m.gate = L.gate[tid];
       a.miss[mpos] = m;
     }
-    if (first_of_token) a.miss_off[tok] = mpos;
-    if (p == 0) a.miss_off[a.T] = n_miss;
+    if (valid && tid % k == 0) a.miss_off[t] = mpos;
+    if (tid == 0) a.miss_off[a.T] = n_miss;
+  }
+  // experts 2*tid and 2*tid + 1 (E <= 2 * kThreads)
+  const int e0 = 2 * tid;
+  const uint32_t m0 = e0 < E ? L.emask[e0] : 0u, m1 = e0 + 1 < E ? L.emask[e0 + 1] : 0u;
+  const uint32_t v0 = m0 ? (1u << 16) | uint32_t(__popc(m0)) : 0u;
+  const uint32_t v1 = m1 ? (1u << 16) | uint32_t(__popc(m1)) : 0u;
+  uint32_t total;
+  const uint32_t x0 = block_scan_u32(v0 + v1, L.tmp + 8, &total);
+  const uint32_t x1 = x0 + v0;
+  if (m0) {
+    L.act_slot[x0 >> 16] = slot_of_choice(a, L, e0);
+    L.act_start[x0 >> 16] = int(x0 & 0xFFFFu);
+    L.emask[e0] = m0 | (x0 << 16);
+  }
+  if (m1) {
+    L.act_slot[x1 >> 16] = slot_of_choice(a, L, e0 + 1);
+    L.act_start[x1 >> 16] = int(x1 & 0xFFFFu);
+    L.emask[e0 + 1] = m1 | (x1 << 16);
+  }
+  if (tid == 0) {
+    L.act_start[total >> 16] = int(total & 0xFFFFu);
+    L.n_act = int(total >> 16);
   }
   __syncthreads();
-  const int n_hit = P - n_miss;
-  if (p < P && s >= 0) {
-    int pos = 0;
-    for (int q = 0; q < P; ++q) {
-      const int sq = L.slot[q];
-      pos += (sq >= 0 && (sq < s || (sq == s && q < p))) ? 1 : 0;
-    }
-    L.bpair[pos] = p;
-    L.tok[pos] = tok;
-    L.sorted[pos] = s;
-  }
-  __syncthreads();
-  const int first = (p < n_hit && (p == 0 || L.sorted[p] != L.sorted[p - 1])) ? 1 : 0;
-  int n_act;
-  const int apos = block_exclusive_scan(first, L.tmp, &n_act);
-  if (first) {
-    L.act_slot[apos] = L.sorted[p];
-    L.act_start[apos] = p;
-  }
-  if (p == 0) {
-    L.act_start[n_act] = n_hit;
-    L.n_act = n_act;
+  if (hit) {
+    const uint32_t w = L.emask[e];
+    const int pos = int(w >> 16) + __popc(w & ((1u << t) - 1u));
+    L.bpair[pos] = tid;
+    L.tok[pos] = t;
   }
 }
 
@@ -1030,6 +1079,8 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
                      lane_gu);
   stage_tokens<FMT>(ka.x, T, K, xs, psum, vstride);
   if (tid == 0) L.calls = calls;
+  for (int e = tid; e < kEMax; e += kThreads) L.emask[e] = 0u;
+  if (tid < kTMax) L.ncand[tid] = 0;
 #pragma unroll
   for (int r = 0; r < kEMax / kThreads; ++r)
     if (tid + r * kThreads < E) L.slot_of[tid + r * kThreads] = so[r];
@@ -1088,37 +1139,41 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     }
   }
   __syncthreads();
-  const bool one_token = T == 1 && E <= 8 * 64 && k <= kTopkListMax;
-  for (int t = one_token ? 0 : wave; t < T; t += kWaves) {
+  const bool thresh = k <= kTopkListMax;
+  if (thresh) topk_threshold<TB>(lg, T, E, k, L);
+  // tokens the threshold selection did not take: one wave each
+  for (int t = wave; t < T; t += kWaves) {
+    if (thresh && L.ncand[t] <= kThreads / TB) continue;
     int my_e;
     float my_v;
-    if (one_token) block_topk_one(lg, E, k, wave, lane, L.cand, &my_e, &my_v);
-    else if (E <= 512) wave_topk<8>(lg + t * E, E, k, lane, &my_e, &my_v);
+    if (E <= 512) wave_topk<8>(lg + t * E, E, k, lane, &my_e, &my_v);
     else wave_topk<16>(lg + t * E, E, k, lane, &my_e, &my_v);
-    if (one_token && wave != 0) continue;
-    // gates: softmax over the k chosen logits (lane 0 holds the largest)
+    if (lane < k) {
+      L.idx[t * k + lane] = my_e;
+      L.gate[t * k + lane] = my_v;
+    }
+  }
+  __syncthreads();
+  for (int t = wave; t < T; t += kWaves) {
+    // gates: softmax over the k chosen logits (choice 0 is the largest)
+    const int my_e = lane < k ? L.idx[t * k + lane] : 0;
+    const float my_v = lane < k ? L.gate[t * k + lane] : 0.f;
     const float vmax = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_v), 0));
     const float ex = lane < k ? expf(my_v - vmax) : 0.f;
     const float z = wave_sum_f32(ex);
     const float g = ex / z;
     if (lane < k) {
-      L.idx[t * k + lane] = my_e;
       L.gate[t * k + lane] = g;
-      L.ptok[t * k + lane] = t;
       if (b == 0) {
         a.idx[t * k + lane] = my_e;
         a.gate[t * k + lane] = g;
       }
     }
-    if (one_token) resolve_one(a, L, my_e, g, lane, b == 0);
+    if (T == 1) resolve_one(a, L, my_e, g, lane, b == 0);
   }
-  if (!one_token) {
+  if (T > 1) {
     __syncthreads();
-    if (P <= 64) {
-      if (wave == 0) resolve_wave(a, L, P, lane, b == 0);
-    } else {
-      resolve_block(a, L, P, b == 0);
-    }
+    resolve_multi(a, L, P, b == 0);
   }
   __syncthreads();
   const int n_act = L.n_act;
@@ -1295,8 +1350,8 @@ bool layer_fused_ok(int fmt, int T, int k, int E, int H, int I) {
   if (chunks_d % ld || chunks_d / ld > kNChMax) return false;
   if (fmt != MOE_W_F32 && (chunks > 64 ? (chunks % 64) != 0 : (chunks & (chunks - 1)) != 0))
     return false;
-  // dynamic LDS beside the static routing tables (~13 KB) within 160 KB
-  return layer_fused_lds(fmt, T, E, H, I) <= 144 * 1024;
+  // dynamic LDS beside the static routing tables (~19 KB) within 160 KB
+  return layer_fused_lds(fmt, T, E, H, I) <= 140 * 1024;
 }
 
 hipError_t launch_layer_fused(const LayerArgs& a, int fmt, hipStream_t st, int* grid) {

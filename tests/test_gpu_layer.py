@@ -47,6 +47,54 @@ def test_small_layer(name, path):
             assert rowwise_rel_err(host(o["shared_out"]), ref["shared_out"]) <= TOL
 
 
+def _tie_bias(pattern, E, seed):
+    e = np.arange(E)
+    if pattern == "levels":      # four values, ~E/4 experts each
+        return (np.random.default_rng(seed).integers(0, 4, E) * 0.25).astype(np.float32)
+    if pattern == "equal":
+        return np.zeros(E, np.float32)
+    if pattern == "crowd128":    # 224 equal leaders above one runner-up
+        return np.where(e % 128 < 28, 2.0, np.where(e % 128 < 32, 1.5, 0.0)).astype(np.float32)
+    if pattern == "crowd32":     # every 32nd expert ahead
+        return np.where(e % 32 == 0, 1.0, 0.0).astype(np.float32)
+    raise ValueError(pattern)
+
+
+TIES = {
+    "T1_levels": dict(E=512, k=10, T=1, pattern="levels"),
+    "T3_equal": dict(E=256, k=8, T=3, pattern="equal"),
+    # more keys at or above a token's threshold than the selection keeps
+    "T3_crowd": dict(E=1024, k=8, T=3, pattern="crowd128"),
+    "T9_crowd": dict(E=1024, k=10, T=9, pattern="crowd32"),
+    "T4_k20": dict(E=64, k=20, T=4, pattern="levels"),
+}
+
+
+@pytest.mark.parametrize("name", list(TIES))
+@pytest.mark.parametrize("path", ["layer", "steps"])
+def test_tied_logits(name, path):
+    """Exactly equal logits (zero router weights, bias on a few levels): the
+    lower expert id wins every tie, bit for bit."""
+    import torch
+    c = TIES[name]
+    cfg = small_cfg(E=c["E"], k=c["k"], H=128, I=64, T=c["T"], bias="zipf", seed=41)
+    say(f"[gpu] tied logits {name} via {path}: E={cfg.E} k={cfg.k} T={cfg.T}")
+    L = DeviceLayer(cfg, 0)
+    bias = _tie_bias(c["pattern"], cfg.E, 5)
+    L.inp["router_w"].zero_()
+    L.inp["bias"].copy_(torch.from_numpy(bias))
+    o = L.run_layer() if path == "layer" else L.run_steps()
+    logits = oracle.router(L.inp["x_host"], np.zeros((cfg.E, cfg.H), np.uint16),
+                           cfg.router_fmt, bias)
+    idx, gate = oracle.topk(logits, cfg.k)
+    slot_idx, me, mt, mg, moff = oracle.resolve(idx, gate, cfg.E)
+    route = {"logits": logits, "idx": idx, "gate": gate, "slot_idx": slot_idx,
+             "miss_expert": me, "miss_token": mt, "miss_gate": mg, "miss_off": moff}
+    ref = oracle.layer_from_synth(cfg, 0, L.inp["x_host"], route=route)
+    check_routing(o, ref, cfg.k)
+    assert rowwise_rel_err(host(o["y"]), ref["y"]) <= TOL
+
+
 def test_tiered_small_with_misses():
     """A partial slot table: misses listed bit-exactly; y holds hits only and
     y + sum over misses of gate * FFN equals the all-resident layer."""
