@@ -247,6 +247,8 @@ struct Lds {
   uint64_t tau[kTMax];       // per-token thresholds
   int ncand[kTMax];          // per-token candidate counts
   uint32_t tmp[32];
+  int cstart[kWaves + 1];   // this workgroup's waves' gate/up task ranges
+  int dstart[2];            // this workgroup's down unit range
   int n_act;
   uint32_t calls;
 };
@@ -643,6 +645,119 @@ __device__ __forceinline__ void row_pair_vec_dot(const RowRegs<FMT, NCH>& RG,
   }
 }
 
+// Up to NG tokens at once: the code pairs of a block are unpacked once for
+// the group.  Block scale d and min m enter as d * sum (128 + q) x +
+// (m - 128 d) * sum x, with the block sums of the vectors staged beside them.
+template <int FMT>
+__device__ __forceinline__ void block_scales(uint32_t sc, uint32_t mn, int bb, float& d, float& m) {
+  const uint32_t dsh = FMT == MOE_W_Q2B32 ? 16u * uint32_t(bb) : 0u;
+  d = f16_to_f32(uint16_t((sc >> dsh) & 0xFFFFu));
+  m = f16_to_f32(uint16_t((mn >> dsh) & 0xFFFFu)) - 128.f * d;
+}
+template <int FMT>
+__device__ __forceinline__ void unpack_block(u32x4 w, int bb, uint32_t (&pr)[16]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      pr[q * 4 + e] = FMT == MOE_W_Q2B32 ? q2_pair(w[2 * bb + (q >> 1)], (q & 1) * 4 + e)
+                                         : q4_pair(w[q], e);
+}
+// sum over one block of the code pairs . the vector's pairs (4 chains)
+__device__ __forceinline__ float block_dot(const uint32_t (&pr)[16], const u32x4* x4) {
+  float a[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const u32x4 xx = x4[q];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a[e] = dot2_bf16(pr[q * 4 + e], xx[e], a[e]);
+  }
+  return (a[0] + a[1]) + (a[2] + a[3]);
+}
+
+// Gate and up rows . the vectors xv[v] (block sums sv[v]) of tokens v < nv.
+template <int FMT, int NCH, int NG>
+__device__ __forceinline__ void row_pair_vecs_dot(const RowRegs<FMT, NCH>& RG,
+                                                  const RowRegs<FMT, NCH>& RU, int nch, int lane_g,
+                                                  int lpr, const uint32_t* const (&xv)[NG],
+                                                  const float* const (&sv)[NG], int nv,
+                                                  float (&g)[NG], float (&u)[NG]) {
+#pragma unroll
+  for (int v = 0; v < NG; ++v) {
+    g[v] = 0.f;
+    u[v] = 0.f;
+  }
+  if constexpr (FMT == MOE_W_F32) {
+#pragma unroll
+    for (int v = 0; v < NG; ++v)
+      if (v < nv) {
+        g[v] = row_vec_dot<FMT, NCH>(RG, nch, lane_g, lpr, xv[v], sv[v]);
+        u[v] = row_vec_dot<FMT, NCH>(RU, nch, lane_g, lpr, xv[v], sv[v]);
+      }
+  } else {
+    constexpr int kBlk = FMT == MOE_W_Q2B32 ? 2 : 1;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      if (j >= nch) continue;
+      const int c = lane_g + j * lpr;
+      // unpacked here, once per call: not hoisted out of the caller's loops
+      const u32x4 wg = fresh(RG.w[j]), wu = fresh(RU.w[j]);
+#pragma unroll
+      for (int bb = 0; bb < kBlk; ++bb) {
+        float dg, mg, du, mu;
+        block_scales<FMT>(RG.sc[j], RG.mn[j], bb, dg, mg);
+        block_scales<FMT>(RU.sc[j], RU.mn[j], bb, du, mu);
+        uint32_t pg[16], pu[16];
+        unpack_block<FMT>(wg, bb, pg);
+        unpack_block<FMT>(wu, bb, pu);
+#pragma unroll
+        for (int v = 0; v < NG; ++v) {
+          if (v >= nv) continue;
+          const u32x4* x4 = reinterpret_cast<const u32x4*>(xv[v] + c * Fmt<FMT>::kCS) + 4 * bb;
+          const float sx = sv[v][kBlk * c + bb];
+          g[v] += dg * block_dot(pg, x4) + mg * sx;
+          u[v] += du * block_dot(pu, x4) + mu * sx;
+        }
+        __builtin_amdgcn_sched_barrier(0);   // one block's pairs live at a time
+      }
+    }
+  }
+}
+
+// One row . the hi and lo halves of h for tokens v0 .. v0 + nv - 1 (hi of
+// token t at xd + 2t * vs with block sums at sd + 2t * ss, lo at 2t + 1).
+template <int FMT, int NCH, int NG>
+__device__ __forceinline__ void row_vecs_dot_hl(const RowRegs<FMT, NCH>& R, int nch, int lane_g,
+                                                int lpr, const uint32_t* xd, const float* sd,
+                                                int vs, int ss, int v0, int nv, float (&o)[NG]) {
+#pragma unroll
+  for (int v = 0; v < NG; ++v) o[v] = 0.f;
+  constexpr int kBlk = FMT == MOE_W_Q2B32 ? 2 : 1;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    if (j >= nch) continue;
+    const int c = lane_g + j * lpr;
+    const u32x4 w = fresh(R.w[j]);
+#pragma unroll
+    for (int bb = 0; bb < kBlk; ++bb) {
+      float d, m;
+      block_scales<FMT>(R.sc[j], R.mn[j], bb, d, m);
+      uint32_t pr[16];
+      unpack_block<FMT>(w, bb, pr);
+#pragma unroll
+      for (int v = 0; v < NG; ++v) {
+        if (v >= nv) continue;
+        const int t2 = 2 * (v0 + v);
+        const u32x4* h4 = reinterpret_cast<const u32x4*>(xd + t2 * vs + c * Fmt<FMT>::kCS) + 4 * bb;
+        const u32x4* l4 = reinterpret_cast<const u32x4*>(xd + (t2 + 1) * vs + c * Fmt<FMT>::kCS) + 4 * bb;
+        const float sx = sd[t2 * ss + kBlk * c + bb] + sd[(t2 + 1) * ss + kBlk * c + bb];
+        o[v] += d * (block_dot(pr, h4) + block_dot(pr, l4)) + m * sx;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 template <int FMT>
 __host__ __device__ __forceinline__ int chunks_of(int K) {
   return FMT == MOE_W_F32 ? K / 4 : K / Fmt<FMT>::kWPC;
@@ -663,28 +778,40 @@ __device__ __forceinline__ void gateup_load(RowRegs<FMT, kNChMax>& rg, RowRegs<F
   load_row<FMT, kNChMax>(ru, U.codes + off, U.scale + blk, U.mn + blk, nch, lane_g, kLprGU);
 }
 
-// SwiGLU of row i for the expert's n tokens (vid: their staged vectors);
-// h of token v is published at out[ids(v)][i] (ids = pair ids, or the
-// tokens themselves when ids is null).
-template <int FMT>
+// SwiGLU of row i for the expert's n tokens (vid: their staged vectors,
+// or tokens t0 + v when vid is null); h of token v is published at
+// out[ids(v)][i] (ids = pair ids, or the token itself when ids is null).
+template <int FMT, int NG>
 __device__ __forceinline__ void gateup_compute(const RowRegs<FMT, kNChMax>& rg,
                                                const RowRegs<FMT, kNChMax>& ru, const LayerArgs& a,
                                                int i, int n, const int* vid, const int* ids,
-                                               uint64_t* out, const uint32_t* xs,
+                                               int t0, uint64_t* out, const uint32_t* xs,
                                                const float* xsum, int vstride, int lane_g,
                                                uint32_t epoch) {
   constexpr int kLprGU = Lanes<FMT>::kGU;
   const int K = a.H, sstride = K / 32;
   const int nch = chunks_of<FMT>(K) / kLprGU;
-  for (int v = 0; v < n; ++v) {
-    const int id = vid ? vid[v] : v;
-    float g, u;
-    row_pair_vec_dot<FMT, kNChMax>(rg, ru, nch, lane_g, kLprGU, xs + id * vstride,
-                                   xsum + id * sstride, g, u);
-    g = group_sum<kLprGU>(g);
-    u = group_sum<kLprGU>(u);
-    if (lane_g == 0)
-      st_dev(out + int64_t(ids ? ids[v] : v) * a.I + i, tag_word(silu_f32(g) * u, epoch));
+  for (int v0 = 0; v0 < n; v0 += NG) {
+    const int nv = min(NG, n - v0);
+    const uint32_t* xv[NG];
+    const float* sv[NG];
+#pragma unroll
+    for (int v = 0; v < NG; ++v) {
+      const int id = v < nv ? (vid ? vid[v0 + v] : t0 + v0 + v) : 0;
+      xv[v] = xs + id * vstride;
+      sv[v] = xsum + id * sstride;
+    }
+    float g[NG], u[NG];
+    row_pair_vecs_dot<FMT, kNChMax, NG>(rg, ru, nch, lane_g, kLprGU, xv, sv, nv, g, u);
+#pragma unroll
+    for (int v = 0; v < NG; ++v) {
+      if (v >= nv) continue;
+      const float gs = group_sum<kLprGU>(g[v]);
+      const float us = group_sum<kLprGU>(u[v]);
+      if (lane_g == 0)
+        st_dev(out + int64_t(ids ? ids[v0 + v] : t0 + v0 + v) * a.I + i,
+               tag_word(silu_f32(gs) * us, epoch));
+    }
   }
 }
 
@@ -706,16 +833,17 @@ struct RouterRegs {
   float bias;
 };
 
-// Issues the task's loads: zeroes its share of y (every router task has
-// one; they cover y), then loads this lane's router chunk and bias.
+// Router task = (row group rg of 64 / lpr rows, token group).  Issues the
+// task's loads: zeroes its share of y (every router task has one; they
+// cover y), then loads this lane's router chunk and bias.
 template <int FMT>
 __device__ __forceinline__ void router_load(RouterRegs<FMT>& R, const LayerArgs& a, int task,
-                                            int n_router, int lane) {
+                                            int rg, int n_router, int lane) {
   const int TH = a.T * a.H, per = (TH + n_router - 1) / n_router;
   const int y0 = task * per, y1 = min(y0 + per, TH);
   for (int i = y0 + lane; i < y1; i += 64) st_dev(a.y + i, 0.f);
   const int lpr = router_lpr<FMT>(a.H);
-  const int e = task * (64 / lpr) + lane / lpr;
+  const int e = rg * (64 / lpr) + lane / lpr;
   if constexpr (FMT != MOE_W_F32) {
     if (e < a.E) {
       const u32x4* row = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.W) +
@@ -728,16 +856,19 @@ __device__ __forceinline__ void router_load(RouterRegs<FMT>& R, const LayerArgs&
   R.bias = (e < a.E && a.bias) ? a.bias[e] : 0.f;
 }
 
-// Logits of the task's rows for every token, published as tagged words
-// once this wave's zeroes of y have landed (a workgroup adds into y only
-// after it has seen every logit).
-template <int FMT, int TB>
+// Logits of the row group's rows for tokens [t0, t0 + TG), published as
+// tagged words once this wave's zeroes of y have landed (a workgroup adds
+// into y only after it has seen every logit).
+template <int FMT, int TG>
 __device__ __forceinline__ void router_compute(const RouterRegs<FMT>& R, const LayerArgs& a,
-                                               int task, const uint32_t* xs, int vstride,
+                                               int rg, int t0, const uint32_t* xs, int vstride,
                                                int lane, uint32_t epoch) {
+  constexpr int TB = TG;
   const int lpr = router_lpr<FMT>(a.H);
-  const int e = task * (64 / lpr) + lane / lpr;
+  const int e = rg * (64 / lpr) + lane / lpr;
   const int lane_g = lane % lpr;
+  const int nt = min(TG, a.T - t0);
+  xs += t0 * vstride;
   float acc[TB];
 #pragma unroll
   for (int t = 0; t < TB; ++t) acc[t] = 0.f;
@@ -764,7 +895,7 @@ __device__ __forceinline__ void router_compute(const RouterRegs<FMT>& R, const L
         }
 #pragma unroll
       for (int t = 0; t < TB; ++t) {
-        if (t < a.T) {
+        if (t < nt) {
           const uint32_t* xv = xs + t * vstride + lane_g * Fmt<FMT>::kCS;
           float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -780,18 +911,34 @@ __device__ __forceinline__ void router_compute(const RouterRegs<FMT>& R, const L
                              : bf16_to_f32(static_cast<const uint16_t*>(a.W)[int64_t(e) * a.H + col]);
 #pragma unroll
         for (int t = 0; t < TB; ++t)
-          if (t < a.T) acc[t] = fmaf(wv, xf[t * vstride + col], acc[t]);
+          if (t < nt) acc[t] = fmaf(wv, xf[t * vstride + col], acc[t]);
       }
     }
   }
-  wait_mem();
+  // sums over each row's lpr lanes (a power of two), the tokens side by side
+  if (lpr >= 2)
 #pragma unroll
-  for (int t = 0; t < TB; ++t) {
-    if (t < a.T) {
-      float s = acc[t];
-      for (int m = 1; m < lpr; m <<= 1) s += __shfl_xor(s, m, 64);
-      if (e < a.E && lane_g == 0) st_dev(region_lg(a) + t * a.E + e, tag_word(s + R.bias, epoch));
-    }
+    for (int t = 0; t < TB; ++t) acc[t] += dpp_f32<0xB1>(acc[t]);    // quad_perm [1,0,3,2]
+  if (lpr >= 4)
+#pragma unroll
+    for (int t = 0; t < TB; ++t) acc[t] += dpp_f32<0x4E>(acc[t]);    // quad_perm [2,3,0,1]
+  if (lpr >= 8)
+#pragma unroll
+    for (int t = 0; t < TB; ++t) acc[t] += dpp_f32<0x141>(acc[t]);   // row_half_mirror
+  if (lpr >= 16)
+#pragma unroll
+    for (int t = 0; t < TB; ++t) acc[t] += dpp_f32<0x140>(acc[t]);   // row_mirror
+  if (lpr >= 32)
+#pragma unroll
+    for (int t = 0; t < TB; ++t) acc[t] += __shfl_xor(acc[t], 16, 64);
+  if (lpr >= 64)
+#pragma unroll
+    for (int t = 0; t < TB; ++t) acc[t] += __shfl_xor(acc[t], 32, 64);
+  wait_mem();
+  if (e < a.E && lane_g == 0) {
+#pragma unroll
+    for (int t = 0; t < TB; ++t)
+      if (t < nt) st_dev(region_lg(a) + (t0 + t) * a.E + e, tag_word(acc[t] + R.bias, epoch));
   }
 }
 
@@ -828,15 +975,20 @@ __device__ __forceinline__ uint64_t key_max_dpp(uint64_t v) {
 template <int TB>
 __device__ __forceinline__ void topk_threshold(const float* lg, int T, int E, int k, Lds& L) {
   constexpr int GS = kThreads / TB, SL = GS / 32, CAP = kThreads / TB;
+  constexpr int KPT = kEMax / GS;   // keys per thread at most
   const int tid = threadIdx.x, t = tid / GS, j = tid % GS;
   const bool on = t < T;
-  const float* l = lg + t * E;
+  const float* l = lg + (on ? t : 0) * E;
+  // the thread's keys stay in registers for step 3 (0 past E)
+  uint64_t key[KPT];
   uint64_t m = 0;
-  if (on)
-    for (int e = j; e < E; e += GS) {
-      const uint64_t key = logit_key(l, e);
-      m = key > m ? key : m;
-    }
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int e = j + GS * i;
+    const uint64_t kv = logit_key(l, e < E ? e : E - 1);
+    key[i] = (on && e < E) ? kv : 0ull;
+    m = key[i] > m ? key[i] : m;
+  }
   if constexpr (SL >= 2) m = key_max_dpp<0xB1>(m);    // quad_perm [1,0,3,2]
   if constexpr (SL >= 4) m = key_max_dpp<0x4E>(m);    // quad_perm [2,3,0,1]
   if constexpr (SL >= 8) m = key_max_dpp<0x141>(m);   // row_half_mirror
@@ -862,11 +1014,11 @@ __device__ __forceinline__ void topk_threshold(const float* lg, int T, int E, in
   __syncthreads();
   if (on) {
     const uint64_t tau = L.tau[t];
-    for (int e = j; e < E; e += GS) {
-      const uint64_t key = logit_key(l, e);
-      if (key >= tau) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      if (key[i] != 0ull && key[i] >= tau) {
         const int pos = atomicAdd(&L.ncand[t], 1);
-        if (pos < CAP) L.rkey[t * CAP + pos] = key;
+        if (pos < CAP) L.rkey[t * CAP + pos] = key[i];
       }
     }
   }
@@ -878,7 +1030,13 @@ __device__ __forceinline__ void topk_threshold(const float* lg, int T, int E, in
       for (int c = j; c < n; c += GS) {
         const uint64_t my = ck[c];
         int r = 0;
-        for (int q = 0; q < n; ++q) r += ck[q] > my ? 1 : 0;
+        for (int q0 = 0; q0 < n; q0 += 8) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int q = q0 + u;
+            if (q < n) r += ck[q] > my ? 1 : 0;
+          }
+        }
         if (r < k) {
           L.idx[t * k + r] = int(~uint32_t(my));
           L.gate[t * k + r] = key_value(uint32_t(my >> 32));
@@ -1065,18 +1223,25 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     const int e = tid + r * kThreads;
     so[r] = (ka.slot_of && e < E) ? ka.slot_of[e] : -1;
   }
-  const int n_router = (E + (64 / router_lpr<FMT>(K)) - 1) / (64 / router_lpr<FMT>(K));
-  const int n_shared = ka.has_sh ? ka.I / kRowsGU : 0;
+  // router tasks: row groups x token groups of kTG (a row group's token
+  // groups share a workgroup when there are at most G row groups)
+  constexpr int kTG = TB == 1 ? 1 : TB == 4 ? 2 : 4;
+  constexpr int kNG = TB == 1 ? 1 : 4;   // tokens per unpacked block
+  const int n_rg = (E + (64 / router_lpr<FMT>(K)) - 1) / (64 / router_lpr<FMT>(K));
+  const int n_router = n_rg * ((T + kTG - 1) / kTG);
+  // shared-expert gate/up tasks: row blocks x token groups of kTG
+  const int n_srb = ka.I / kRowsGU;
+  const int n_shared = ka.has_sh ? n_srb * ((T + kTG - 1) / kTG) : 0;
   const int n_a = n_router + n_shared;
   const int task0 = b + wave * G;
   const int lane_gu = lane % kLprGU;
   RouterRegs<FMT> rr;
   RowRegs<FMT, kNChMax> rg, ru;
   if (task0 < n_router)
-    router_load<FMT>(rr, ka, task0, n_router, lane);
+    router_load<FMT>(rr, ka, task0, task0 % n_rg, n_router, lane);
   else if (task0 < n_a)
-    gateup_load<FMT>(rg, ru, ka, ka.sg, ka.su, 0, (task0 - n_router) * kRowsGU + lane / kLprGU,
-                     lane_gu);
+    gateup_load<FMT>(rg, ru, ka, ka.sg, ka.su, 0,
+                     ((task0 - n_router) % n_srb) * kRowsGU + lane / kLprGU, lane_gu);
   stage_tokens<FMT>(ka.x, T, K, xs, psum, vstride);
   if (tid == 0) L.calls = calls;
   for (int e = tid; e < kEMax; e += kThreads) L.emask[e] = 0u;
@@ -1091,13 +1256,14 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   const uint32_t epoch = L.calls + 1u;   // this call's number
   for (int task = task0; task < n_a; task += kWaves * G) {
     if (task < n_router) {
-      if (task != task0) router_load<FMT>(rr, a, task, n_router, lane);
-      router_compute<FMT, TB>(rr, a, task, xs, vstride, lane, epoch);
+      if (task != task0) router_load<FMT>(rr, a, task, task % n_rg, n_router, lane);
+      router_compute<FMT, kTG>(rr, a, task % n_rg, (task / n_rg) * kTG, xs, vstride, lane, epoch);
     } else {
-      const int i = (task - n_router) * kRowsGU + lane / kLprGU;
+      const int s = task - n_router, t0 = (s / n_srb) * kTG;
+      const int i = (s % n_srb) * kRowsGU + lane / kLprGU;
       if (task != task0) gateup_load<FMT>(rg, ru, a, a.sg, a.su, 0, i, lane_gu);
-      gateup_compute<FMT>(rg, ru, a, i, T, nullptr, nullptr, region_h_sh(a), xs, xsum, vstride, lane_gu,
-                          epoch);
+      gateup_compute<FMT, kNG>(rg, ru, a, i, min(kTG, T - t0), nullptr, nullptr, t0, region_h_sh(a), xs,
+                          xsum, vstride, lane_gu, epoch);
     }
   }
 
@@ -1187,7 +1353,55 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   const int64_t row_bytes_d = int64_t(Kd) * fmt_bits(FMT) / 8;
   const int nrb = (a.H + kRowsD - 1) / kRowsD;
   const int n_units = (n_act + (a.has_sh ? 1 : 0)) * nrb;
+  const int tpe = a.I / kRowsGU;
+  const int n_tasks = n_act * tpe;
   const int lane_gd = lane % kLprD;
+  // Who does what.  One token: gate/up tasks (bucket, row block) dealt to
+  // the waves in turn and down units (bucket, row block) to the workgroups
+  // in turn -- every bucket has one token, so their costs are equal.  More
+  // tokens: buckets differ in size, so each wave takes a contiguous range
+  // of tasks and each workgroup a contiguous range of units with equal sums
+  // of cost (a fixed part plus the bucket's tokens).  Thread u finds the
+  // range bounds that fall inside bucket u's span of cumulative cost.
+  int c_first = b + wave * G, c_end = n_tasks, c_step = kWaves * G;
+  int d_first = b, d_end = n_units, d_step = G;
+  if constexpr (TB > 1) {
+    constexpr int kCostC = 1, kCostD = 2;
+    const int n_db = n_act + (a.has_sh ? 1 : 0);
+    const int64_t totC = int64_t(tpe) * (kCostC * n_act + L.act_start[n_act]);
+    const int64_t totD = int64_t(nrb) * (kCostD * n_db + L.act_start[n_act] + (a.has_sh ? T : 0));
+    const int u = tid;
+    if (u <= n_act) {
+      const int nu = u < n_act ? L.act_start[u + 1] - L.act_start[u] : 0;
+      const int64_t c0 = int64_t(tpe) * (kCostC * u + L.act_start[u]);
+      const int64_t c1 = c0 + int64_t(tpe) * (kCostC + nu);
+      for (int w = 0; w <= kWaves; ++w) {
+        const int64_t bt = (int64_t(b) * kWaves + w) * totC / (int64_t(G) * kWaves);
+        if (u == n_act ? bt >= c0 : (bt >= c0 && bt < c1))
+          L.cstart[w] = u == n_act ? n_tasks
+                                   : u * tpe + int((bt - c0 + kCostC + nu - 1) / (kCostC + nu));
+      }
+    }
+    if (u <= n_db) {
+      const int pre = u <= n_act ? L.act_start[u] : L.act_start[n_act] + T;   // tokens before u
+      const int nu = u < n_act ? L.act_start[u + 1] - L.act_start[u] : T;
+      const int64_t d0 = int64_t(nrb) * (kCostD * u + pre);
+      const int64_t d1 = d0 + int64_t(nrb) * (kCostD + nu);
+      for (int w = 0; w <= 1; ++w) {
+        const int64_t bt = int64_t(b + w) * totD / G;
+        if (u == n_db ? bt >= d0 : (bt >= d0 && bt < d1))
+          L.dstart[w] = u == n_db ? n_units
+                                  : u * nrb + int((bt - d0 + kCostD + nu - 1) / (kCostD + nu));
+      }
+    }
+    __syncthreads();
+    c_first = L.cstart[wave];
+    c_end = L.cstart[wave + 1];
+    c_step = 1;
+    d_first = L.dstart[0];
+    d_end = L.dstart[1];
+    d_step = 1;
+  }
   RowRegs<FMT, kNChMax> rd;
   auto load_down = [&](int unit, RowRegs<FMT, kNChMax>& rd) {
     const int u = unit / nrb, rb = unit % nrb;
@@ -1200,30 +1414,27 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     load_row<FMT, kNChMax>(rd, D.codes + slot * a.mat_bytes + rr_ * row_bytes_d, D.scale + blk,
                            D.mn + blk, nch_d, lane_gd, kLprD);
   };
-  if (b < n_units) load_down(b, rd);
+  if (d_first < d_end) load_down(d_first, rd);
   uint64_t arr = 0;
   if (b == 0 && tid < G) arr = ld_dev(region_arrive(a) + tid);
   {
     // each wave's tasks in turn, the next task's rows loading while the
     // current one computes
-    const int tpe = a.I / kRowsGU;
-    const int n_tasks = n_act * tpe;
-    const int stride = kWaves * G;
-    int task = b + wave * G;
-    if (task < n_tasks)
+    int task = c_first;
+    if (task < c_end)
       gateup_load<FMT>(rg, ru, a, a.g, a.u, L.act_slot[task / tpe],
                        (task % tpe) * kRowsGU + lane / kLprGU, lane_gu);
-    for (; task < n_tasks; task += stride) {
-      const int next = task + stride;
+    for (; task < c_end; task += c_step) {
+      const int next = task + c_step;
       RowRegs<FMT, kNChMax> ng, nu;
-      if (next < n_tasks)
+      if (next < c_end)
         gateup_load<FMT>(ng, nu, a, a.g, a.u, L.act_slot[next / tpe],
                          (next % tpe) * kRowsGU + lane / kLprGU, lane_gu);
       const int u = task / tpe;
       const int i = (task % tpe) * kRowsGU + lane / kLprGU;
       const int st = L.act_start[u];
       const int n = L.act_start[u + 1] - st;
-      gateup_compute<FMT>(rg, ru, a, i, n, L.tok + st, L.bpair + st, region_h(a), xs, xsum, vstride,
+      gateup_compute<FMT, kNG>(rg, ru, a, i, n, L.tok + st, L.bpair + st, 0, region_h(a), xs, xsum, vstride,
                           lane_gu, epoch);
       rg = ng;
       ru = nu;
@@ -1235,34 +1446,47 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     uint32_t* xd = smem;                                    // reuses the token area
     float* sd = reinterpret_cast<float*>(xd + kVPP * kTMax * vs_d);
     float* pd = sd + kVPP * kTMax * ss_d;
-    for (int unit = b; unit < n_units; unit += G) {
+    int staged = -1;   // bucket whose activations are in the LDS
+    for (int unit = d_first; unit < d_end; unit += d_step) {
       RowRegs<FMT, kNChMax> nd;   // the next unit's rows load meanwhile
-      if (unit + G < n_units) load_down(unit + G, nd);
+      if (unit + d_step < d_end) load_down(unit + d_step, nd);
       const int u = unit / nrb, rb = unit % nrb;
       const bool shared = u >= n_act;
       const int st = shared ? 0 : L.act_start[u];
       const int n = shared ? T : L.act_start[u + 1] - st;
       const int r = rb * kRowsD + wave * (64 / kLprD) + lane / kLprD;
-      __syncthreads();   // gate/up tasks and the previous unit are done with the LDS
-      if (tid < n)
-        srcs[tid] = shared ? region_h_sh(a) + int64_t(tid) * Kd
-                           : region_h(a) + int64_t(L.bpair[st + tid]) * Kd;
-      __syncthreads();
-      stage_h<FMT>(srcs, n, Kd, xd, sd, pd, vs_d, epoch);
-      __syncthreads();
-      for (int v = 0; v < n; ++v) {
-        float o;
-        if constexpr (kVPP == 2)
-          o = row_vec_dot_hl<FMT, kNChMax>(rd, nch_d, lane_gd, kLprD, xd + (2 * v) * vs_d,
-                                           sd + (2 * v) * ss_d, xd + (2 * v + 1) * vs_d,
-                                           sd + (2 * v + 1) * ss_d);
-        else
-          o = row_vec_dot<FMT, kNChMax>(rd, nch_d, lane_gd, kLprD, xd + v * vs_d, sd + v * ss_d);
-        o = group_sum<kLprD>(o);
-        if (r < a.H && lane_gd == 0) {
-          const int t = shared ? v : L.tok[st + v];
-          const float g = shared ? 1.f : L.gate[L.bpair[st + v]];
-          fadd_dev(a.y + int64_t(t) * a.H + r, g * o);
+      if (u != staged) {
+        __syncthreads();   // gate/up tasks and the previous unit are done with the LDS
+        if (tid < n)
+          srcs[tid] = shared ? region_h_sh(a) + int64_t(tid) * Kd
+                             : region_h(a) + int64_t(L.bpair[st + tid]) * Kd;
+        __syncthreads();
+        stage_h<FMT>(srcs, n, Kd, xd, sd, pd, vs_d, epoch);
+        __syncthreads();
+        staged = u;
+      }
+      for (int v0 = 0; v0 < n; v0 += kNG) {
+        const int nv = min(kNG, n - v0);
+        float o[kNG];
+        if constexpr (kVPP == 2) {
+          row_vecs_dot_hl<FMT, kNChMax, kNG>(rd, nch_d, lane_gd, kLprD, xd, sd, vs_d, ss_d, v0, nv,
+                                             o);
+        } else {
+#pragma unroll
+          for (int v = 0; v < kNG; ++v)
+            o[v] = v < nv ? row_vec_dot<FMT, kNChMax>(rd, nch_d, lane_gd, kLprD,
+                                                     xd + (v0 + v) * vs_d, sd + (v0 + v) * ss_d)
+                          : 0.f;
+        }
+#pragma unroll
+        for (int v = 0; v < kNG; ++v) {
+          if (v >= nv) continue;
+          const float os = group_sum<kLprD>(o[v]);
+          if (r < a.H && lane_gd == 0) {
+            const int t = shared ? v0 + v : L.tok[st + v0 + v];
+            const float g = shared ? 1.f : L.gate[L.bpair[st + v0 + v]];
+            fadd_dev(a.y + int64_t(t) * a.H + r, g * os);
+          }
         }
       }
       rd = nd;
