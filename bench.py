@@ -44,11 +44,18 @@ def log(msg):
 KERNEL_SOURCES = {
     "decode": ["routed_expert_ffn_gemv_amd/csrc/layer.hip", "routed_expert_ffn_gemv_amd/csrc/layer.h",
                "routed_expert_ffn_gemv_amd/csrc/gemv_core.h", "routed_expert_ffn_gemv_amd/csrc/common.h"],
-    "prefill": ["routed_expert_ffn_gemv_amd/csrc/ffn_gemm.hip", "routed_expert_ffn_gemv_amd/csrc/gemv_core.h",
-                "routed_expert_ffn_gemv_amd/csrc/common.h"],
+    "prefill": ["routed_expert_ffn_gemv_amd/csrc/ffn_gemm.hip", "routed_expert_ffn_gemv_amd/csrc/resolve.hip",
+                "routed_expert_ffn_gemv_amd/csrc/gemv_core.h", "routed_expert_ffn_gemv_amd/csrc/common.h"],
 }
 TRAFFIC = {
     # workload: {"sha256": ..., "bytes": fetched + written per launch}
+    # c2: the moe_layer kernel (profiles/c2_decode_layer_hbm_traffic.md)
+    "c2_decode_layer_q2": {"sha256": "6730b2f0037e187e91142fd06e5a65a9c375b8783eb6f3127bf2f971c130edc3",
+                           "bytes": 23236681},
+    # c5: the kernels of one moe_expert_ffn call (active list, schedule, x16,
+    # gate/up and down GEMMs; profiles/c5_prefill_hbm_traffic.md)
+    "c5_prefill_q4": {"sha256": "7c6bdd3262b01a17d99ffe4afdcbba63256ab541f07cc2173512ad1b72967401",
+                      "bytes": 8913486161},
 }
 
 

@@ -243,7 +243,7 @@ struct Lds {
   int act_start[kPMax + 1];
   int slot_of[kEMax];    // the slot table (when the layer has one)
   uint32_t emask[kEMax]; // per expert: tokens that chose it | bucket start << 16
-  uint64_t rkey[kThreads];   // segment maxima, then candidates (top-k)
+  alignas(16) uint64_t rkey[kThreads + 8];   // segment maxima, then candidates (top-k)
   uint64_t tau[kTMax];       // per-token thresholds
   int ncand[kTMax];          // per-token candidate counts
   uint32_t tmp[32];
@@ -972,10 +972,9 @@ __device__ __forceinline__ uint64_t key_max_dpp(uint64_t v) {
 // L.idx[t*k + r] and L.gate[t*k + r] receive the r-th choice and its logit.
 // A token with more than CAP candidates (many equal logits) is left to the
 // caller.  Called by every thread; k <= kTopkListMax.
-template <int TB>
-__device__ __forceinline__ void topk_threshold(const float* lg, int T, int E, int k, Lds& L) {
+template <int TB, int KPT>   // KPT: keys per thread, E <= KPT * kThreads / TB
+__device__ __forceinline__ void topk_threshold_k(const float* lg, int T, int E, int k, Lds& L) {
   constexpr int GS = kThreads / TB, SL = GS / 32, CAP = kThreads / TB;
-  constexpr int KPT = kEMax / GS;   // keys per thread at most
   const int tid = threadIdx.x, t = tid / GS, j = tid % GS;
   const bool on = t < T;
   const float* l = lg + (on ? t : 0) * E;
@@ -1002,10 +1001,11 @@ __device__ __forceinline__ void topk_threshold(const float* lg, int T, int E, in
       const uint64_t my = sk[sg];
       int gt = 0, eq = 0;
 #pragma unroll
-      for (int q = 0; q < 32; ++q) {
-        const uint64_t o = sk[q];
-        gt += o > my ? 1 : 0;
-        eq += o == my ? 1 : 0;
+      for (int q = 0; q < 16; ++q) {   // two keys per 16-byte read
+        const u32x4 o4 = reinterpret_cast<const u32x4*>(sk)[q];
+        const uint64_t o0 = (uint64_t(o4[1]) << 32) | o4[0], o1 = (uint64_t(o4[3]) << 32) | o4[2];
+        gt += (o0 > my ? 1 : 0) + (o1 > my ? 1 : 0);
+        eq += (o0 == my ? 1 : 0) + (o1 == my ? 1 : 0);
       }
       // empty segments share the key 0; their writers agree
       if (gt <= k - 1 && k - 1 < gt + eq) L.tau[tt] = my;
@@ -1014,12 +1014,17 @@ __device__ __forceinline__ void topk_threshold(const float* lg, int T, int E, in
   __syncthreads();
   if (on) {
     const uint64_t tau = L.tau[t];
+    int c = 0;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      if (key[i] != 0ull && key[i] >= tau) {
-        const int pos = atomicAdd(&L.ncand[t], 1);
-        if (pos < CAP) L.rkey[t * CAP + pos] = key[i];
-      }
+    for (int i = 0; i < KPT; ++i) c += (key[i] != 0ull && key[i] >= tau) ? 1 : 0;
+    if (c > 0) {
+      int pos = atomicAdd(&L.ncand[t], c);
+#pragma unroll
+      for (int i = 0; i < KPT; ++i)
+        if (key[i] != 0ull && key[i] >= tau) {
+          if (pos < CAP) L.rkey[t * CAP + pos] = key[i];
+          ++pos;
+        }
     }
   }
   __syncthreads();
@@ -1032,9 +1037,12 @@ __device__ __forceinline__ void topk_threshold(const float* lg, int T, int E, in
         int r = 0;
         for (int q0 = 0; q0 < n; q0 += 8) {
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const int q = q0 + u;
-            if (q < n) r += ck[q] > my ? 1 : 0;
+          for (int h = 0; h < 4; ++h) {   // two keys per 16-byte read
+            const u32x4 o4 = reinterpret_cast<const u32x4*>(ck + q0)[h];
+            const uint64_t o0 = (uint64_t(o4[1]) << 32) | o4[0];
+            const uint64_t o1 = (uint64_t(o4[3]) << 32) | o4[2];
+            r += (q0 + 2 * h < n && o0 > my) ? 1 : 0;
+            r += (q0 + 2 * h + 1 < n && o1 > my) ? 1 : 0;
           }
         }
         if (r < k) {
@@ -1044,6 +1052,15 @@ __device__ __forceinline__ void topk_threshold(const float* lg, int T, int E, in
       }
     }
   }
+}
+
+template <int TB>
+__device__ __forceinline__ void topk_threshold(const float* lg, int T, int E, int k, Lds& L) {
+  constexpr int GS = kThreads / TB, KMAX = kEMax / GS;
+  if (KMAX >= 2 && E <= GS * (KMAX / 2))
+    topk_threshold_k<TB, (KMAX >= 2 ? KMAX / 2 : 1)>(lg, T, E, k, L);
+  else
+    topk_threshold_k<TB, KMAX>(lg, T, E, k, L);
 }
 
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
