@@ -112,7 +112,7 @@ hipError_t launch_resolve_small(int T, int k, int E, int S, const int32_t* idx,
 //              the same slot (or among its earlier misses) places it.
 
 struct LargeWs {
-  int32_t* cnt;        // [S][nchunk]
+  int32_t* cnt;        // [nchunk][S]: chunk-major, so a pass over slots is coalesced
   int32_t* cmiss;      // [nchunk + 1]
 };
 
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256) void resolve_count_kernel(int P, int E, int S,
   }
   if (my_miss) atomicAdd(&nm, my_miss);
   __syncthreads();
-  for (int s = threadIdx.x; s < S; s += blockDim.x) w.cnt[int64_t(s) * nchunk + c] = hist[s];
+  for (int s = threadIdx.x; s < S; s += blockDim.x) w.cnt[int64_t(c) * S + s] = hist[s];
   if (threadIdx.x == 0) w.cmiss[c] = nm;
 }
 
@@ -181,16 +181,19 @@ __global__ __launch_bounds__(1024) void resolve_scan_kernel(int T, int S, int nc
   for (int base = 0; base < S; base += blockDim.x) {
     const int s = base + threadIdx.x;
     int tot_s = 0;
-    if (s < S)
-      for (int c = 0; c < nchunk; ++c) tot_s += w.cnt[int64_t(s) * nchunk + c];
+    if (s < S) {
+#pragma unroll 16
+      for (int c = 0; c < nchunk; ++c) tot_s += w.cnt[int64_t(c) * S + s];
+    }
     int tot_all;
     const int off = hits_before + block_exclusive_scan(tot_s, tmp, &tot_all);
     if (s < S) {
       if (bucket_off) bucket_off[s] = off;
       int r = off;
+#pragma unroll 16
       for (int c = 0; c < nchunk; ++c) {
-        const int v = w.cnt[int64_t(s) * nchunk + c];
-        w.cnt[int64_t(s) * nchunk + c] = r;
+        const int v = w.cnt[int64_t(c) * S + s];
+        w.cnt[int64_t(c) * S + s] = r;
         r += v;
       }
     }
@@ -214,7 +217,7 @@ __global__ __launch_bounds__(1024) void resolve_scan_kernel(int T, int S, int nc
 }
 
 __global__ __launch_bounds__(256) void resolve_scatter_kernel(
-    int P, int k, int nchunk, const int32_t* __restrict__ idx, const float* __restrict__ gate,
+    int P, int k, int S, int nchunk, const int32_t* __restrict__ idx, const float* __restrict__ gate,
     const int32_t* __restrict__ slot_idx, LargeWs w, int32_t* __restrict__ bucket_pair,
     moe_miss* __restrict__ miss, int32_t* __restrict__ miss_off) {
   __shared__ int sl[kResolveChunk];
@@ -234,7 +237,7 @@ __global__ __launch_bounds__(256) void resolve_scatter_kernel(
     }
     const int p = p0 + i;
     if (s >= 0) {
-      if (bucket_pair) bucket_pair[w.cnt[int64_t(s) * nchunk + c] + r] = p;
+      if (bucket_pair) bucket_pair[w.cnt[int64_t(c) * S + s] + r] = p;
     } else if (miss) {
       moe_miss m;
       m.expert = idx[p];
@@ -257,7 +260,7 @@ hipError_t launch_resolve_large(int T, int k, int E, int S, const int32_t* idx,
                      nchunk, idx, slot_of, slot_idx, w);
   hipLaunchKernelGGL(resolve_scan_kernel, dim3(1), dim3(1024), 0, st, T, S, nchunk, w,
                      bucket_off, miss_off, act);
-  hipLaunchKernelGGL(resolve_scatter_kernel, dim3(nchunk), dim3(256), 0, st, P, k, nchunk, idx,
+  hipLaunchKernelGGL(resolve_scatter_kernel, dim3(nchunk), dim3(256), 0, st, P, k, S, nchunk, idx,
                      gate, slot_idx, w, bucket_pair, miss, miss_off);
   return hipGetLastError();
 }
