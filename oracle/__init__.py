@@ -45,7 +45,8 @@ def lib():
         L.oracle_f16.restype = ctypes.c_double
         L.oracle_f16.argtypes = [ctypes.c_uint16]
         for name in ("oracle_dequant", "oracle_router", "oracle_topk", "oracle_resolve",
-                     "oracle_bucket", "oracle_ffn", "oracle_combine", "oracle_layer"):
+                     "oracle_bucket", "oracle_ffn", "oracle_combine", "oracle_layer",
+                     "oracle_count_usage", "oracle_slot_refresh"):
             getattr(L, name).restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -124,6 +125,29 @@ def bucket(slot_idx, S):
     pairs = np.empty(max(T * k, 1), np.int32)
     _check(lib().oracle_bucket(T, k, S, _ptr(slot_idx), _ptr(off), _ptr(pairs)), "bucket")
     return off, pairs[: int(off[S])].copy()
+
+
+def count_usage(idx, E, usage=None):
+    """usage[e] += number of choices of e in idx [T][k] (uint32 [E])."""
+    idx = _c(idx, np.int32)
+    T, k = idx.shape
+    usage = np.zeros(E, np.uint32) if usage is None else np.ascontiguousarray(usage, np.uint32).copy()
+    _check(lib().oracle_count_usage(T, k, E, _ptr(idx), _ptr(usage)), "count_usage")
+    return usage
+
+
+def slot_refresh(usage, slot_of, expert_of, max_swaps):
+    """One refresh of a global slot table.  Returns (swaps [n][3], usage,
+    slot_of, expert_of) after it, the inputs left unchanged."""
+    usage = np.array(usage, np.uint32)
+    slot_of = np.array(slot_of, np.int32)
+    expert_of = np.array(expert_of, np.int32)
+    swaps = np.zeros((max(max_swaps, 1), 3), np.int32)
+    n = np.zeros(1, np.int32)
+    _check(lib().oracle_slot_refresh(len(usage), len(expert_of), _ptr(usage), _ptr(slot_of),
+                                     _ptr(expert_of), int(max_swaps), _ptr(swaps), _ptr(n)),
+           "slot_refresh")
+    return swaps[: int(n[0])].copy(), usage, slot_of, expert_of
 
 
 def _mat_args(fmt, m):

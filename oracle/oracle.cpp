@@ -169,6 +169,75 @@ int oracle_resolve(int T, int k, int E, const int32_t* idx, const double* gate,
   return 0;
 }
 
+// Usage counts (the adaptive tier of [MD] "粗から細へ" follows the experts
+// the conversation actually uses): every choice of expert e adds one to
+// usage[e], hits and misses alike.
+int oracle_count_usage(int T, int k, int E, const int32_t* idx, uint32_t* usage) {
+  if (T < 0 || k < 1 || E < 1) return 1;
+  for (int64_t p = 0; p < int64_t(T) * k; ++p) {
+    const int e = idx[p];
+    if (e < 0 || e >= E) return 1;
+    usage[e] += 1u;
+  }
+  return 0;
+}
+
+// One refresh of a global slot table ([MD] "粗から細へ": slots are filled
+// by a usage ranking; the adaptive tier swaps a bounded number of experts
+// toward the ones in use).  Written from the definition, step by step:
+//   u(j) = min(usage[j], 65535);
+//   candidates: experts j with slot_of[j] < 0 and u(j) > 0, ranked by u
+//     descending, then j ascending;
+//   victims: free slots (expert_of[s] < 0) by s ascending, then occupied
+//     slots by u(expert_of[s]) ascending, then s ascending;
+//   swap i takes candidate i into victim i's slot while i < max_swaps, both
+//     lists last and the victim is free or u(candidate) > u(victim's expert);
+//   tables: slot_of[old] = -1, slot_of[new] = s, expert_of[s] = new;
+//   every count is then halved.
+// swaps[3*i .. 3*i+2] = (s, new, old or -1); *n_swaps = the number of swaps.
+int oracle_slot_refresh(int N, int S, uint32_t* usage, int32_t* slot_of, int32_t* expert_of,
+                        int max_swaps, int32_t* swaps, int32_t* n_swaps) {
+  if (N < 1 || S < 1 || max_swaps < 0) return 1;
+  auto u = [&](int j) -> int64_t { return usage[j] < 65535u ? int64_t(usage[j]) : 65535; };
+  std::vector<int> cand;
+  for (int j = 0; j < N; ++j)
+    if (slot_of[j] < 0 && u(j) > 0) cand.push_back(j);
+  std::sort(cand.begin(), cand.end(), [&](int a, int b) {
+    if (u(a) != u(b)) return u(a) > u(b);
+    return a < b;
+  });
+  std::vector<int> vict;
+  for (int s = 0; s < S; ++s)
+    if (expert_of[s] < 0) vict.push_back(s);
+  std::vector<int> occ;
+  for (int s = 0; s < S; ++s)
+    if (expert_of[s] >= 0) occ.push_back(s);
+  std::sort(occ.begin(), occ.end(), [&](int a, int b) {
+    const int64_t ua = u(expert_of[a]), ub = u(expert_of[b]);
+    if (ua != ub) return ua < ub;
+    return a < b;
+  });
+  vict.insert(vict.end(), occ.begin(), occ.end());
+  int n = 0;
+  while (n < max_swaps && n < int(cand.size()) && n < int(vict.size())) {
+    const int s = vict[n], j = cand[n], old = expert_of[s];
+    if (old >= 0 && !(u(j) > u(old))) break;
+    swaps[3 * n] = s;
+    swaps[3 * n + 1] = j;
+    swaps[3 * n + 2] = old;
+    ++n;
+  }
+  for (int i = 0; i < n; ++i) {
+    const int s = swaps[3 * i], j = swaps[3 * i + 1], old = swaps[3 * i + 2];
+    if (old >= 0) slot_of[old] = -1;
+    slot_of[j] = s;
+    expert_of[s] = j;
+  }
+  for (int j = 0; j < N; ++j) usage[j] >>= 1;
+  *n_swaps = n;
+  return 0;
+}
+
 // Bucket the hit pairs by slot, stably: a counting sort over slots 0..S-1
 // in pair order p = t*k + j.  bucket_off[S+1]; bucket_pair[bucket_off[S]].
 // Each distinct resident expert then appears once with all of its tokens

@@ -391,3 +391,95 @@ def test_layer_from_synth_matches_whole_layer():
                         cfg.k, "q4", pools, cfg.I, shared=shared)
     np.testing.assert_array_equal(r["idx"], full["idx"])
     np.testing.assert_allclose(r["y"], full["y"], rtol=1e-13, atol=1e-13)
+
+
+# ---- usage counts and the slot-table refresh
+def test_count_usage_is_a_histogram():
+    rng = np.random.default_rng(3)
+    idx = rng.integers(0, 37, size=(9, 5)).astype(np.int32)
+    base = rng.integers(0, 4, size=37).astype(np.uint32)
+    got = oracle.count_usage(idx, 37, base)
+    np.testing.assert_array_equal(got, base + np.bincount(idx.ravel(), minlength=37))
+
+
+def test_refresh_hand_worked():
+    """6 experts, 3 slots (one free).  Candidates by count: 4 (7), 2 (3),
+    5 (2); victims: free slot 2, then slot 1 (expert 3, count 1), slot 0
+    (expert 0, count 5).  4 -> slot 2, 2 -> slot 1 (3 > 1), 5 stays out
+    (2 > 5 fails)."""
+    usage = [5, 0, 3, 1, 7, 2]
+    slot_of = [0, -1, -1, 1, -1, -1]
+    expert_of = [0, 3, -1]
+    swaps, u, so, eo = oracle.slot_refresh(usage, slot_of, expert_of, 4)
+    np.testing.assert_array_equal(swaps, [[2, 4, -1], [1, 2, 3]])
+    np.testing.assert_array_equal(so, [0, -1, 1, -1, 2, -1])
+    np.testing.assert_array_equal(eo, [0, 2, 4])
+    np.testing.assert_array_equal(u, [2, 0, 1, 0, 3, 1])
+
+
+def test_refresh_ties_do_not_swap_and_limits_hold():
+    # equal counts: no swap; max_swaps = 0: tables unchanged, counts halved
+    swaps, u, so, eo = oracle.slot_refresh([4, 4, 4, 4], [0, 1, -1, -1], [0, 1], 8)
+    assert len(swaps) == 0 and list(so) == [0, 1, -1, -1] and list(u) == [2, 2, 2, 2]
+    swaps, u, so, eo = oracle.slot_refresh([1, 9, 9], [0, -1, -1], [0], 0)
+    assert len(swaps) == 0 and list(so) == [0, -1, -1] and list(u) == [0, 4, 4]
+    # counts above 65535 rank as 65535: the lower id wins
+    swaps, *_ = oracle.slot_refresh([0, 70000, 65535], [0, -1, -1], [0], 1)
+    np.testing.assert_array_equal(swaps, [[0, 1, 0]])
+
+
+def _resident_sets(so, eo):
+    res = {int(j) for j in np.flatnonzero(np.asarray(so) >= 0)}
+    assert res == {int(j) for j in eo if j >= 0}
+    for s, j in enumerate(eo):
+        if j >= 0:
+            assert so[j] == s
+    return res
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_refresh_unbounded_leaves_no_better_outsider(seed):
+    """With enough swaps, afterwards no expert outside the pool has a count
+    (before halving) above any resident's, tables stay inverse, and free
+    slots fill before any resident is evicted."""
+    rng = np.random.default_rng(seed)
+    N, S = 300, 60
+    usage = rng.zipf(1.3, N).clip(0, 100000).astype(np.uint32) * (rng.random(N) < 0.8)
+    slot_of = np.full(N, -1, np.int32)
+    expert_of = np.full(S, -1, np.int32)
+    init = rng.choice(N, 45, replace=False)           # 15 free slots
+    slots = rng.choice(S, 45, replace=False)
+    slot_of[init] = slots
+    expert_of[slots] = init
+    swaps, u, so, eo = oracle.slot_refresh(usage, slot_of, expert_of, 1024)
+    res = _resident_sets(so, eo)
+    cap = np.minimum(usage.astype(np.int64), 65535)
+    outside = [j for j in range(N) if j not in res]
+    if all(e >= 0 for e in eo):      # pool full: nothing outside beats anything inside
+        assert max(cap[outside]) <= min(cap[list(res)])
+    else:                            # free slots left: every outsider had count 0
+        assert all(cap[j] == 0 for j in outside)
+    n_free_before = int((expert_of < 0).sum())
+    n_cand = int(((slot_of < 0) & (cap > 0)).sum())
+    assert sum(1 for sw in swaps if sw[2] < 0) == min(n_free_before, n_cand)
+    assert all(sw[2] < 0 for sw in swaps[:min(n_free_before, n_cand)])
+    np.testing.assert_array_equal(u, usage >> 1)
+
+
+def test_refresh_bounded_takes_the_best_first():
+    """max_swaps = 3 of many possible: the three swapped-in experts are the
+    three highest-count outsiders (ties by lower id), the victims the three
+    lowest-count residents."""
+    rng = np.random.default_rng(9)
+    N, S = 50, 10
+    usage = rng.integers(1, 30, N).astype(np.uint32)
+    slot_of = np.full(N, -1, np.int32)
+    expert_of = np.arange(S, dtype=np.int32)          # experts 0..9 resident
+    slot_of[:S] = np.arange(S)
+    usage[:S] = rng.integers(0, 5, S)                  # weak residents
+    swaps, *_ = oracle.slot_refresh(usage, slot_of, expert_of, 3)
+    outs = sorted(range(S, N), key=lambda j: (-int(usage[j]), j))[:3]
+    vics = sorted(range(S), key=lambda s: (int(usage[s]), s))[:3]
+    np.testing.assert_array_equal(swaps[:, 1], outs)
+    np.testing.assert_array_equal(swaps[:, 0], vics)
+    np.testing.assert_array_equal(swaps[:, 2], vics)
