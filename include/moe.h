@@ -83,7 +83,11 @@ typedef struct {
  * means the layer has none.  Router weights [E][H] are F32 or BF16;
  * router_bias [E] fp32 may be NULL.  Limits: 1 <= k <= min(E, 32), E <= 1024,
  * H and I multiples of 32 (of 64 for Q2B32), H <= 8192, I <= 4096,
- * 1 <= num_slots <= 16384. */
+ * 1 <= num_slots <= 16384.
+ * usage_counts [E] uint32 may be NULL; when set, moe_layer and
+ * moe_resolve_slots add 1 to usage_counts[e] for every choice of expert e
+ * (hits and misses, every token), with device-scope atomic adds: the counts
+ * moe_slot_refresh ranks experts by. */
 typedef struct {
   int32_t E, k, H, I, num_slots;
   int32_t router_fmt;
@@ -92,6 +96,7 @@ typedef struct {
   const int32_t* slot_of_expert;
   moe_mat gate, up, down;
   moe_mat sh_gate, sh_up, sh_down;
+  uint32_t* usage_counts;
 } moe_layer_desc;
 
 /* One missed (not resident) expert of one token, with its gate weight. */
@@ -178,6 +183,51 @@ moe_status moe_combine(const moe_layer_desc* desc, int32_t T, const int32_t* slo
 moe_status moe_layer(const moe_layer_desc* desc, const uint16_t* x, int32_t T, float* y,
                      int32_t* topk_idx, float* topk_gate, int32_t* slot_idx, moe_miss* miss,
                      int32_t* miss_off, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- Adaptive slot table ([MD] section "粗から細へ" and its placement
+ * figure: each card fills its expert slots by a usage ranking, and an
+ * adaptive tier swaps at most 96 experts every 4 rounds toward the experts
+ * the conversation actually uses, raising the share served from the card).
+ *
+ * One pool of num_slots expert slots serves L layers (a global slot table):
+ * layer l's table is slot_of + l*E (its moe_layer_desc.slot_of_expert) and
+ * its counts usage + l*E (its moe_layer_desc.usage_counts).  Expert j =
+ * l*E + e.  All arrays are device memory; the store may also be host memory
+ * the device can read (pinned, allocated as such by the caller). */
+typedef struct {
+  int32_t L, E, H, I, num_slots;
+  moe_mat gate, up, down;              /* the pool: [num_slots] matrices each */
+  moe_mat store_gate, store_up, store_down;  /* every expert: [L*E] matrices each, index j */
+  uint32_t* usage;     /* [L*E] choice counts since the last refresh */
+  int32_t* slot_of;    /* [L*E] slot of expert j, or -1 */
+  int32_t* expert_of;  /* [num_slots] expert j held by the slot, or -1 (free) */
+} moe_slot_pool;
+
+/* Largest max_swaps of one refresh. */
+#define MOE_REFRESH_MAX_SWAPS 1024
+
+moe_status moe_slot_refresh_workspace_size(const moe_slot_pool* pool, size_t* bytes);
+
+/* One refresh.  With u(j) = min(usage[j], 65535):
+ *  candidates = experts j with slot_of[j] < 0 and u(j) > 0, ordered by u
+ *    descending, then j ascending;
+ *  victims = free slots (expert_of[s] < 0) by s ascending, then occupied
+ *    slots by u(expert_of[s]) ascending, then s ascending;
+ *  swap i pairs candidate i with victim i for i = 0, 1, ... while i <
+ *    max_swaps, both lists last, and the victim is free or u(candidate) >
+ *    u(victim's expert).
+ * Each swap copies the candidate's gate/up/down planes from the store into
+ * the victim slot, sets slot_of[old] = -1 (old = the victim's expert, if
+ * any), slot_of[new] = s and expert_of[s] = new.  Then every count is
+ * halved (usage[j] >>= 1), so recent rounds weigh most.  swaps [max_swaps]
+ * [3] int32 receives (s, new, old or -1) for i < *n_swaps; n_swaps is one
+ * device int32.  Stream-ordered: layer calls issued after it on the same
+ * stream see the new tables and weights; calls in flight on other streams
+ * must not use the pool meanwhile.  Limits: L*E <= 65536, num_slots <=
+ * 16384, 0 <= max_swaps <= MOE_REFRESH_MAX_SWAPS; formats as for
+ * moe_layer_desc (all six pools in one expert format). */
+moe_status moe_slot_refresh(const moe_slot_pool* pool, int32_t max_swaps, int32_t* swaps,
+                            int32_t* n_swaps, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -23,7 +23,9 @@ FORMATS = {"f32": MOE_W_F32, "bf16": MOE_W_BF16, "q2": MOE_W_Q2B32, "q4": MOE_W_
 
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_status_string", "moe_version", "moe_workspace_size", "moe_route",
-           "moe_resolve_slots", "moe_expert_ffn", "moe_combine", "moe_layer")
+           "moe_resolve_slots", "moe_expert_ffn", "moe_combine", "moe_layer",
+           "moe_slot_refresh_workspace_size", "moe_slot_refresh")
+MOE_REFRESH_MAX_SWAPS = 1024
 
 
 class MoEError(RuntimeError):
@@ -43,7 +45,17 @@ class moe_layer_desc(ctypes.Structure):
                 ("router_fmt", ctypes.c_int32), ("router_w", ctypes.c_void_p),
                 ("router_bias", ctypes.c_void_p), ("slot_of_expert", ctypes.c_void_p),
                 ("gate", moe_mat), ("up", moe_mat), ("down", moe_mat),
-                ("sh_gate", moe_mat), ("sh_up", moe_mat), ("sh_down", moe_mat)]
+                ("sh_gate", moe_mat), ("sh_up", moe_mat), ("sh_down", moe_mat),
+                ("usage_counts", ctypes.c_void_p)]
+
+
+class moe_slot_pool(ctypes.Structure):
+    _fields_ = [("L", ctypes.c_int32), ("E", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("I", ctypes.c_int32), ("num_slots", ctypes.c_int32),
+                ("gate", moe_mat), ("up", moe_mat), ("down", moe_mat),
+                ("store_gate", moe_mat), ("store_up", moe_mat), ("store_down", moe_mat),
+                ("usage", ctypes.c_void_p), ("slot_of", ctypes.c_void_p),
+                ("expert_of", ctypes.c_void_p)]
 
 
 class moe_miss(ctypes.Structure):
@@ -76,6 +88,11 @@ def _load():
     lib.moe_combine.argtypes = [D, I32, P, P, P, P, P, P]
     lib.moe_layer.restype = I32
     lib.moe_layer.argtypes = [D, P, I32, P, P, P, P, P, P, P, SZ, P]
+    SP = ctypes.POINTER(moe_slot_pool)
+    lib.moe_slot_refresh_workspace_size.restype = I32
+    lib.moe_slot_refresh_workspace_size.argtypes = [SP, ctypes.POINTER(SZ)]
+    lib.moe_slot_refresh.restype = I32
+    lib.moe_slot_refresh.argtypes = [SP, I32, P, P, P, SZ, P]
     return lib
 
 
@@ -118,8 +135,8 @@ class LayerDesc:
     stacked by slot; shared: the same dict for the shared expert or None."""
 
     def __init__(self, E, k, H, I, router_w, router_fmt, wfmt, pools, shared=None,
-                 router_bias=None, slot_of_expert=None, num_slots=None):
-        self._keep = [router_w, router_bias, slot_of_expert, pools, shared]
+                 router_bias=None, slot_of_expert=None, num_slots=None, usage_counts=None):
+        self._keep = [router_w, router_bias, slot_of_expert, pools, shared, usage_counts]
         d = moe_layer_desc()
         d.E, d.k, d.H, d.I = E, k, H, I
         d.num_slots = E if num_slots is None else num_slots
@@ -127,6 +144,7 @@ class LayerDesc:
         d.router_w = _ptr(router_w)
         d.router_bias = _ptr(router_bias)
         d.slot_of_expert = _ptr(slot_of_expert)
+        d.usage_counts = _ptr(usage_counts)
         fmt = FORMATS[wfmt] if isinstance(wfmt, str) else wfmt
         for name in ("gate", "up", "down"):
             setattr(d, name, self._mat(fmt, pools[name]))
@@ -196,6 +214,33 @@ def moe_layer(desc, x, T, y, topk_idx, topk_gate, slot_idx, miss, miss_off, ws, 
     _check(lib.moe_layer(desc.ref, _ptr(x), int(T), _ptr(y), _ptr(topk_idx), _ptr(topk_gate),
                          _ptr(slot_idx), _ptr(miss), _ptr(miss_off), _ptr(ws),
                          ws.numel() if ws is not None else 0, _stream(stream)), "moe_layer")
+
+
+class SlotPool:
+    """A moe_slot_pool built from torch tensors (kept alive here): pools and
+    store as dicts gate/up/down -> tensor (f32) or (codes, scale, min);
+    usage uint32-as-int32 [L*E], slot_of int32 [L*E], expert_of int32 [S]."""
+
+    def __init__(self, L, E, H, I, wfmt, pool, store, usage, slot_of, expert_of, num_slots):
+        self._keep = [pool, store, usage, slot_of, expert_of]
+        p = moe_slot_pool()
+        p.L, p.E, p.H, p.I, p.num_slots = L, E, H, I, num_slots
+        fmt = FORMATS[wfmt] if isinstance(wfmt, str) else wfmt
+        for name in ("gate", "up", "down"):
+            setattr(p, name, LayerDesc._mat(fmt, pool[name]))
+            setattr(p, "store_" + name, LayerDesc._mat(fmt, store[name]))
+        p.usage, p.slot_of, p.expert_of = _ptr(usage), _ptr(slot_of), _ptr(expert_of)
+        self.pool = p
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.pool)
+
+
+def moe_slot_refresh(pool, max_swaps, swaps, n_swaps, stream=None):
+    """swaps: int32 device tensor [>= max_swaps * 3]; n_swaps: int32 [1]."""
+    _check(lib.moe_slot_refresh(pool.ref, int(max_swaps), _ptr(swaps), _ptr(n_swaps), None, 0,
+                                _stream(stream)), "moe_slot_refresh")
 
 
 def unpack_miss(miss_tensor, n):

@@ -56,6 +56,24 @@ moe_status check_desc(const moe_layer_desc* d) {
   return MOE_OK;
 }
 
+// Checks a slot pool for moe_slot_refresh.
+moe_status check_pool(const moe_slot_pool* p) {
+  if (!p) return MOE_ERR_INVALID;
+  if (p->L < 1 || p->E < 1 || p->num_slots < 1 || p->H < 32 || p->I < 32 || p->H % 32 ||
+      p->I % 32)
+    return MOE_ERR_INVALID;
+  if (int64_t(p->L) * p->E > 65536 || p->num_slots > kMaxSlots || p->H > kMaxH || p->I > kMaxI)
+    return MOE_ERR_UNSUPPORTED;
+  const int fmt = p->gate.fmt;
+  if (fmt != MOE_W_F32 && fmt != MOE_W_Q2B32 && fmt != MOE_W_Q4B32) return MOE_ERR_UNSUPPORTED;
+  if (fmt == MOE_W_Q2B32 && (p->H % 64 || p->I % 64)) return MOE_ERR_INVALID;
+  const moe_mat* m[6] = {&p->gate, &p->up, &p->down, &p->store_gate, &p->store_up, &p->store_down};
+  for (int i = 0; i < 6; ++i)
+    if (!valid_pool(*m[i], fmt)) return MOE_ERR_INVALID;
+  if (!p->usage || !p->slot_of || !p->expert_of) return MOE_ERR_INVALID;
+  return MOE_OK;
+}
+
 // Workspace regions (each 256-byte aligned), in this order:
 //   layer   hand-off region of the fused moe_layer (layer_region_bytes;
 //           sized from the layer shape alone, so it sits at the same place
@@ -182,6 +200,8 @@ moe_status run_resolve(const moe_layer_desc* d, const int32_t* idx, const float*
     e = launch_resolve_large(T, d->k, d->E, d->num_slots, idx, gate, d->slot_of_expert, slot_idx,
                              bucket_off, bucket_pair, miss, miss_off, act,
                              at<void>(ws, w.resolve), st);
+  if (e == hipSuccess && d->usage_counts)
+    e = launch_count_usage(T * d->k, d->E, idx, d->usage_counts, st);
   return device_status(e);
 }
 
@@ -200,7 +220,7 @@ const char* moe_status_string(int32_t s) {
   }
 }
 
-int32_t moe_version(void) { return 100; }
+int32_t moe_version(void) { return 101; }
 
 moe_status moe_workspace_size(const moe_layer_desc* desc, int32_t T, size_t* bytes) {
   const moe_status s = check_desc(desc);
@@ -340,6 +360,7 @@ moe_status moe_layer(const moe_layer_desc* desc, const uint16_t* x, int32_t T, f
     L.slot_idx = slot_idx;
     L.miss = miss;
     L.miss_off = miss_off;
+    L.usage = desc->usage_counts;
     L.region = at<uint8_t>(ws, w.layer);
     return device_status(launch_layer_fused(L, fmt, st, nullptr));
   }
@@ -360,6 +381,51 @@ moe_status moe_layer(const moe_layer_desc* desc, const uint16_t* x, int32_t T, f
   if (e == hipSuccess)
     e = launch_combine(T, desc->k, desc->H, sl, topk_gate, pairbuf, shbuf, y, st);
   return device_status(e);
+}
+
+moe_status moe_slot_refresh_workspace_size(const moe_slot_pool* pool, size_t* bytes) {
+  const moe_status s = check_pool(pool);
+  if (s != MOE_OK) return s;
+  if (!bytes) return MOE_ERR_INVALID;
+  *bytes = 0;   // the refresh keeps its working set in LDS
+  return MOE_OK;
+}
+
+moe_status moe_slot_refresh(const moe_slot_pool* pool, int32_t max_swaps, int32_t* swaps,
+                            int32_t* n_swaps, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  const moe_status s = check_pool(pool);
+  if (s != MOE_OK) return s;
+  if (max_swaps < 0 || !n_swaps || (max_swaps > 0 && !swaps)) return MOE_ERR_INVALID;
+  if (max_swaps > MOE_REFRESH_MAX_SWAPS) return MOE_ERR_UNSUPPORTED;
+  RefreshArgs a;
+  memset(&a, 0, sizeof(a));
+  a.N = pool->L * pool->E;
+  a.S = pool->num_slots;
+  a.max_swaps = max_swaps;
+  a.usage = pool->usage;
+  a.slot_of = pool->slot_of;
+  a.expert_of = pool->expert_of;
+  a.swaps = swaps;
+  a.n_swaps = n_swaps;
+  const moe_mat* pm[3] = {&pool->gate, &pool->up, &pool->down};
+  const moe_mat* sm[3] = {&pool->store_gate, &pool->store_up, &pool->store_down};
+  for (int m = 0; m < 3; ++m) {
+    // gate/up [I][H] and down [H][I]: the same size
+    const MatView v = make_view(*pm[m], pool->I, pool->H);
+    RefreshMat& r = a.mats[m];
+    const bool f32 = pm[m]->fmt == MOE_W_F32;
+    r.pool_codes = static_cast<uint8_t*>(const_cast<void*>(pm[m]->data));
+    r.pool_scale = f32 ? nullptr : const_cast<uint16_t*>(pm[m]->scale);
+    r.pool_min = f32 ? nullptr : const_cast<uint16_t*>(pm[m]->min);
+    r.store_codes = static_cast<const uint8_t*>(sm[m]->data);
+    r.store_scale = f32 ? nullptr : sm[m]->scale;
+    r.store_min = f32 ? nullptr : sm[m]->min;
+    r.mat_bytes = v.mat_bytes;
+    r.mat_blocks = f32 ? 0 : v.mat_blocks;
+  }
+  return device_status(launch_slot_refresh(a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -39,6 +39,28 @@ hipError_t launch_resolve_large(int T, int k, int E, int S, const int32_t* idx,
 hipError_t launch_active_from_offsets(int S, const int32_t* bucket_off, ActiveList act,
                                       hipStream_t st);
 
+// usage counts and the adaptive slot table
+hipError_t launch_count_usage(int P, int E, const int32_t* idx, uint32_t* usage, hipStream_t st);
+struct RefreshMat {          // one of gate / up / down
+  uint8_t* pool_codes;       // [S] matrices (codes, or fp32 data)
+  uint16_t* pool_scale;      // [S] planes (nullptr for fp32)
+  uint16_t* pool_min;
+  const uint8_t* store_codes;   // [N] matrices
+  const uint16_t* store_scale;
+  const uint16_t* store_min;
+  int64_t mat_bytes, mat_blocks;
+};
+struct RefreshArgs {
+  int N, S, max_swaps;
+  uint32_t* usage;           // [N]
+  int32_t* slot_of;          // [N]
+  int32_t* expert_of;        // [S]
+  int32_t* swaps;            // [max_swaps][3]
+  int32_t* n_swaps;          // [1]
+  RefreshMat mats[3];
+};
+hipError_t launch_slot_refresh(const RefreshArgs& a, hipStream_t st);
+
 // expert FFN (decode GEMV)
 struct FfnArgs {
   const uint16_t* x;     // bf16 [T][H]

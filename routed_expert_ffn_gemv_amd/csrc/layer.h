@@ -55,6 +55,7 @@ struct LayerArgs {
   int32_t* slot_idx;       // may be null
   moe_miss* miss;
   int32_t* miss_off;
+  uint32_t* usage;         // [E] choice counts (may be null)
   uint8_t* region;         // hand-off region (layout above)
 };
 

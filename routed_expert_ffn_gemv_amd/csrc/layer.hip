@@ -1360,6 +1360,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   }
   __syncthreads();
   const int n_act = L.n_act;
+  if (b == 0 && a.usage && tid < P) atomicAdd(a.usage + L.idx[tid], 1u);
 
   // ---- C: the first down unit's loads, then routed gate/up
   const int Kd = a.I;

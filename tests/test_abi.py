@@ -120,3 +120,39 @@ def test_calls_validate_before_launch():
     assert L.moe_layer(ref, FAKE, 4, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, n,
                        None) == moe.MOE_ERR_INVALID           # miss list is required
     assert L.moe_route(None, FAKE, 4, FAKE, FAKE, FAKE, n, None) == moe.MOE_ERR_INVALID
+
+
+def _pool(**kw):
+    p = moe.moe_slot_pool()
+    p.L, p.E, p.H, p.I, p.num_slots = 48, 512, 2048, 768, 4176
+    for name in ("gate", "up", "down", "store_gate", "store_up", "store_down"):
+        m = getattr(p, name)
+        m.fmt, m.data, m.scale, m.min = moe.MOE_W_Q2B32, FAKE, FAKE, FAKE
+    p.usage, p.slot_of, p.expert_of = FAKE, FAKE, FAKE
+    for k_, v in kw.items():
+        setattr(p, k_, v)
+    return p
+
+
+def test_slot_refresh_validates_before_launch():
+    L = moe.lib
+    n = ctypes.c_size_t(7)
+    assert L.moe_slot_refresh_workspace_size(ctypes.byref(_pool()), ctypes.byref(n)) == moe.MOE_OK
+    assert n.value == 0
+    ok = ctypes.byref(_pool())
+    assert L.moe_slot_refresh(ok, 1025, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_slot_refresh(ok, -1, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_INVALID
+    assert L.moe_slot_refresh(ok, 96, None, FAKE, None, 0, None) == moe.MOE_ERR_INVALID
+    assert L.moe_slot_refresh(ok, 96, FAKE, None, None, 0, None) == moe.MOE_ERR_INVALID
+    assert L.moe_slot_refresh(None, 96, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_INVALID
+    for kw, status in [({"L": 200}, moe.MOE_ERR_UNSUPPORTED),       # L*E > 65536
+                       ({"num_slots": 0}, moe.MOE_ERR_INVALID),
+                       ({"num_slots": 20000}, moe.MOE_ERR_UNSUPPORTED),
+                       ({"usage": None}, moe.MOE_ERR_INVALID),
+                       ({"expert_of": None}, moe.MOE_ERR_INVALID),
+                       ({"H": 2080}, moe.MOE_ERR_INVALID)]:
+        assert L.moe_slot_refresh(ctypes.byref(_pool(**kw)), 96, FAKE, FAKE, None, 0,
+                                  None) == status, kw
+    p = _pool()
+    p.store_down.fmt = moe.MOE_W_Q4B32                      # store and pool differ
+    assert L.moe_slot_refresh(ctypes.byref(p), 96, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_INVALID
