@@ -164,13 +164,23 @@ def bench_decode(args, cfg_name):
                 moe.moe_layer(desc, inp["x"], T, y, idx, gate, slot_idx, miss, miss_off, ws,
                               stream)
 
-    # distinct experts read per layer call (for the algorithmic bytes)
+    # distinct experts read per layer call (for the algorithmic bytes): the
+    # stacks run one step with a slot buffer per layer
     uniq = []
     for s in range(min(64, args.steps)):
-        step(s)
+        if cfg.layers == 1:
+            step(s)
+            torch.cuda.synchronize()
+            sl_h = slot_idx.cpu().numpy()
+            uniq.append(len(np.unique(sl_h[sl_h >= 0])))
+            continue
+        per = torch.empty((L, T, k), dtype=torch.int32, device=dev)
+        for l, (desc, inp, _, _) in enumerate(layers):
+            moe.moe_layer(desc, inp["x"], T, y, idx, gate, per[l], miss, miss_off, ws, stream)
         torch.cuda.synchronize()
-        sl_h = slot_idx.cpu().numpy()
-        uniq.append(len(np.unique(sl_h[sl_h >= 0])))
+        for sl_h in per.cpu().numpy():
+            uniq.append(len(np.unique(sl_h[sl_h >= 0])))
+        break   # the stack's inputs are the same every step
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
@@ -220,6 +230,135 @@ def bench_decode(args, cfg_name):
                                "sample": f"{n} single-token decode layers of {cfg.name} "
                                          f"(router..combine, fp64, one thread, {el:.1f}s)"}
     return out
+
+
+def bench_adaptive(args):
+    """c4's 48-layer, 16-token stack on a pool filled from a profile that does
+    not match the traffic (each layer's residents drawn at random), with the
+    adaptive tier on: usage counted by every layer call, moe_slot_refresh
+    with at most 96 swaps every 4 rounds.  A round is one step (48 layer
+    calls) on fresh tokens.  Reports the hit rate as the pool adapts, then
+    times steady-state rounds, refreshes included."""
+    import torch
+    import routed_expert_ffn_gemv_amd as moe
+    import synth
+    from synth import device as sdev
+
+    cfg = synth.CONFIGS["c4"]
+    T, k, E, H, L = cfg.T, cfg.k, cfg.E, cfg.H, cfg.layers
+    N = L * E
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    log("[bench] c4a: store of every expert, cold pool, layer inputs")
+    t0 = time.time()
+    n_l = synth.resident_counts(cfg)
+    rng = np.random.default_rng(0xC4A)
+    slot_layer, slot_expert = [], []
+    for l in range(L):
+        for e in rng.permutation(E)[: n_l[l]]:
+            slot_layer.append(l)
+            slot_expert.append(int(e))
+    S = len(slot_expert)
+    slot_of_h = np.full(N, -1, np.int32)
+    slot_of_h[np.array(slot_layer) * E + np.array(slot_expert)] = np.arange(S, dtype=np.int32)
+    expert_of_h = (np.array(slot_layer) * E + np.array(slot_expert)).astype(np.int32)
+    store = sdev.expert_pool(cfg, np.repeat(np.arange(L), E), np.tile(np.arange(E), L), dev)
+    pool = sdev.expert_pool(cfg, slot_layer, slot_expert, dev)
+    usage = torch.zeros(N, dtype=torch.int32, device=dev)
+    slot_of = torch.as_tensor(slot_of_h, device=dev)
+    expert_of = torch.as_tensor(expert_of_h, device=dev)
+    sp = moe.SlotPool(L, E, H, cfg.I, cfg.wfmt, pool, store, usage, slot_of, expert_of, S)
+    n_x = 32                      # distinct rounds of tokens, cycled
+    layers = []
+    for l in range(L):
+        inp = sdev.layer_inputs(cfg, l, dev, x=synth.gen_x(cfg, l, T * n_x))
+        desc = moe.LayerDesc(E, k, H, cfg.I, inp["router_w"], cfg.router_fmt, cfg.wfmt, pool,
+                             shared=inp["shared"], router_bias=inp["bias"],
+                             slot_of_expert=slot_of[l * E:(l + 1) * E], num_slots=S,
+                             usage_counts=usage[l * E:(l + 1) * E])
+        layers.append((desc, inp))
+    torch.cuda.synchronize()
+    log(f"[bench] setup {time.time() - t0:.1f}s")
+    ws = moe.workspace(layers[0][0], T, dev)
+    y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    gate = torch.empty((T, k), dtype=torch.float32, device=dev)
+    slot_idx = torch.empty((L, T, k), dtype=torch.int32, device=dev)
+    miss = torch.empty((T * k * 3,), dtype=torch.int32, device=dev)
+    miss_off = torch.empty((L, T + 1), dtype=torch.int32, device=dev)
+    swaps = torch.empty((96 * 3,), dtype=torch.int32, device=dev)
+    n_swaps = torch.zeros((1,), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def round_(r):
+        j = r % n_x
+        for l, (desc, inp) in enumerate(layers):
+            moe.moe_layer(desc, inp["x"][j * T:(j + 1) * T], T, y, idx, gate, slot_idx[l], miss,
+                          miss_off[l], ws, stream)
+        if r % 4 == 3:
+            moe.moe_slot_refresh(sp, 96, swaps, n_swaps, stream)
+
+    # adaptation: hit rate per round (untimed; reads the miss counts)
+    R = 256
+    hits, swapped = [], 0
+    uniq = []
+    for r in range(R):
+        round_(r)
+        mo = miss_off[:, T].cpu().numpy()
+        hits.append(1.0 - mo.sum() / (L * T * k))
+        if r % 4 == 3:
+            swapped += int(n_swaps.item())
+        if r >= R - 8:
+            for sl_h in slot_idx.cpu().numpy():
+                uniq.append(len(np.unique(sl_h[sl_h >= 0])))
+    # refresh cost alone
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(10):
+        moe.moe_slot_refresh(sp, 96, swaps, n_swaps, stream)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    refresh_ms = ev[0].elapsed_time(ev[1]) / 10
+    # timed steady state
+    for r in range(args.warmup):
+        round_(R + r)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for r in range(args.steps):
+        round_(R + args.warmup + r)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    u = float(np.mean(uniq))
+    bytes_step = L * algorithmic_bytes_decode(cfg, u, T)
+    gbs = bytes_step / (ms * 1e-3) / 1e9
+    hr = np.array(hits)
+    return {
+        "metric": METRIC,
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "q2 weights, bf16 activations, f32 accumulation",
+        "data": "synthetic",
+        "config": {"workload": "c4a_adaptive_slots_q2", "E": E, "k": k, "H": H, "I": cfg.I,
+                   "T": T, "layers": L, "weights": cfg.wfmt, "shared_expert": cfg.shared,
+                   "slots": S, "step": "48 moe_layer calls (one per layer); every 4th step "
+                                       "also one moe_slot_refresh (<= 96 swaps)",
+                   "initial_placement": "per layer, n_l experts drawn at random"},
+        "hit_rate": {"round_0": round(float(hr[0]), 4),
+                     "rounds_60_63": round(float(hr[60:64].mean()), 4),
+                     "rounds_124_127": round(float(hr[124:128].mean()), 4),
+                     "rounds_252_255": round(float(hr[252:256].mean()), 4)},
+        "swaps_in_256_rounds": swapped,
+        "refresh_ms": round(refresh_ms, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "48 moe_layer calls + refreshes", "bytes_per_step": int(bytes_step),
+                     "distinct_hit_experts_per_layer": round(u, 2)},
+    }
 
 
 def gemm_flops(cfg, n_hit, T):
@@ -374,7 +513,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c4a", "c5"])
     ap.add_argument("--layers", type=int, default=48)
     ap.add_argument("--cpu-tokens", type=int, default=12)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -387,7 +526,12 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe(args.copy_probe)
-    out = bench_prefill(args, "c5") if args.config == "c5" else bench_decode(args, args.config)
+    if args.config == "c5":
+        out = bench_prefill(args, "c5")
+    elif args.config == "c4a":
+        out = bench_adaptive(args)
+    else:
+        out = bench_decode(args, args.config)
     print(json.dumps(out), flush=True)
 
 
