@@ -53,7 +53,12 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kTMax = MOE_LAYER_MAX_T;
 constexpr int kPMax = kLayerMaxPairs;
 constexpr int kEMax = 1024;
-constexpr int kNChMax = 4;                      // 16-byte chunks per lane and weight row
+// 16-byte chunks a lane holds of one weight row: gate/up rows (K = H) and
+// down rows (K = I).  2-bit gate/up rows take two (H <= 2048), so the
+// registers of several rows in flight stay small.
+constexpr int kNChD = 4;
+template <int FMT>
+constexpr int nch_gu() { return FMT == MOE_W_Q2B32 ? 2 : 4; }
 
 // Lanes per weight row: a lane holds at most 2 (Q2) or 4 (Q4) chunks of a
 // 2048-wide gate/up row and 3 of a 768-wide down row.
@@ -765,7 +770,8 @@ __host__ __device__ __forceinline__ int chunks_of(int K) {
 
 // gate/up rows i of one expert: this lane's chunks (loads only).
 template <int FMT>
-__device__ __forceinline__ void gateup_load(RowRegs<FMT, kNChMax>& rg, RowRegs<FMT, kNChMax>& ru,
+__device__ __forceinline__ void gateup_load(RowRegs<FMT, nch_gu<FMT>()>& rg,
+                                            RowRegs<FMT, nch_gu<FMT>()>& ru,
                                             const LayerArgs& a, const Planes& G, const Planes& U,
                                             int slot, int i, int lane_g) {
   constexpr int kLprGU = Lanes<FMT>::kGU;
@@ -774,16 +780,17 @@ __device__ __forceinline__ void gateup_load(RowRegs<FMT, kNChMax>& rg, RowRegs<F
   const int64_t row_bytes = int64_t(K) * fmt_bits(FMT) / 8;
   const int64_t blk = int64_t(slot) * a.mat_blocks + int64_t(i) * sstride;
   const int64_t off = slot * a.mat_bytes + i * row_bytes;
-  load_row<FMT, kNChMax>(rg, G.codes + off, G.scale + blk, G.mn + blk, nch, lane_g, kLprGU);
-  load_row<FMT, kNChMax>(ru, U.codes + off, U.scale + blk, U.mn + blk, nch, lane_g, kLprGU);
+  load_row<FMT, nch_gu<FMT>()>(rg, G.codes + off, G.scale + blk, G.mn + blk, nch, lane_g, kLprGU);
+  load_row<FMT, nch_gu<FMT>()>(ru, U.codes + off, U.scale + blk, U.mn + blk, nch, lane_g, kLprGU);
 }
 
 // SwiGLU of row i for the expert's n tokens (vid: their staged vectors,
 // or tokens t0 + v when vid is null); h of token v is published at
 // out[ids(v)][i] (ids = pair ids, or the token itself when ids is null).
 template <int FMT, int NG>
-__device__ __forceinline__ void gateup_compute(const RowRegs<FMT, kNChMax>& rg,
-                                               const RowRegs<FMT, kNChMax>& ru, const LayerArgs& a,
+__device__ __forceinline__ void gateup_compute(const RowRegs<FMT, nch_gu<FMT>()>& rg,
+                                               const RowRegs<FMT, nch_gu<FMT>()>& ru,
+                                               const LayerArgs& a,
                                                int i, int n, const int* vid, const int* ids,
                                                int t0, uint64_t* out, const uint32_t* xs,
                                                const float* xsum, int vstride, int lane_g,
@@ -802,7 +809,7 @@ __device__ __forceinline__ void gateup_compute(const RowRegs<FMT, kNChMax>& rg,
       sv[v] = xsum + id * sstride;
     }
     float g[NG], u[NG];
-    row_pair_vecs_dot<FMT, kNChMax, NG>(rg, ru, nch, lane_g, kLprGU, xv, sv, nv, g, u);
+    row_pair_vecs_dot<FMT, nch_gu<FMT>(), NG>(rg, ru, nch, lane_g, kLprGU, xv, sv, nv, g, u);
 #pragma unroll
     for (int v = 0; v < NG; ++v) {
       if (v >= nv) continue;
@@ -1244,6 +1251,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   // groups share a workgroup when there are at most G row groups)
   constexpr int kTG = TB == 1 ? 1 : TB == 4 ? 2 : 4;
   constexpr int kNG = TB == 1 ? 1 : 4;   // tokens per unpacked block
+  constexpr int kNGC = TB == 1 ? 1 : 4;  // the same for routed gate/up
   const int n_rg = (E + (64 / router_lpr<FMT>(K)) - 1) / (64 / router_lpr<FMT>(K));
   const int n_router = n_rg * ((T + kTG - 1) / kTG);
   // shared-expert gate/up tasks: row blocks x token groups of kTG
@@ -1253,7 +1261,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   const int task0 = b + wave * G;
   const int lane_gu = lane % kLprGU;
   RouterRegs<FMT> rr;
-  RowRegs<FMT, kNChMax> rg, ru;
+  RowRegs<FMT, nch_gu<FMT>()> rg, ru;
   if (task0 < n_router)
     router_load<FMT>(rr, ka, task0, task0 % n_rg, n_router, lane);
   else if (task0 < n_a)
@@ -1420,8 +1428,8 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     d_end = L.dstart[1];
     d_step = 1;
   }
-  RowRegs<FMT, kNChMax> rd;
-  auto load_down = [&](int unit, RowRegs<FMT, kNChMax>& rd) {
+  RowRegs<FMT, kNChD> rd;
+  auto load_down = [&](int unit, RowRegs<FMT, kNChD>& rd) {
     const int u = unit / nrb, rb = unit % nrb;
     const bool shared = u >= n_act;
     const Planes D = shared ? a.sd : a.d;
@@ -1429,33 +1437,47 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     const int r = rb * kRowsD + wave * (64 / kLprD) + lane / kLprD;
     const int rr_ = r < a.H ? r : a.H - 1;
     const int64_t blk = int64_t(slot) * a.mat_blocks + int64_t(rr_) * ss_d;
-    load_row<FMT, kNChMax>(rd, D.codes + slot * a.mat_bytes + rr_ * row_bytes_d, D.scale + blk,
+    load_row<FMT, kNChD>(rd, D.codes + slot * a.mat_bytes + rr_ * row_bytes_d, D.scale + blk,
                            D.mn + blk, nch_d, lane_gd, kLprD);
   };
-  if (d_first < d_end) load_down(d_first, rd);
+  // one token: the first down unit's rows load during gate/up; several
+  // tokens keep those registers for the gate/up prefetch instead
+  if (TB == 1 && d_first < d_end) load_down(d_first, rd);
   uint64_t arr = 0;
   if (b == 0 && tid < G) arr = ld_dev(region_arrive(a) + tid);
   {
     // each wave's tasks in turn, the next task's rows loading while the
     // current one computes
+    // With several tasks per wave (T > 1) the rows of the next two tasks
+    // are in flight while one computes; one token has at most one task.
+    constexpr int kAhead = TB > 1 ? 2 : 1;
+    auto load_task = [&](int t, RowRegs<FMT, nch_gu<FMT>()>& g, RowRegs<FMT, nch_gu<FMT>()>& u) {
+      gateup_load<FMT>(g, u, a, a.g, a.u, L.act_slot[t / tpe], (t % tpe) * kRowsGU + lane / kLprGU,
+                       lane_gu);
+    };
     int task = c_first;
-    if (task < c_end)
-      gateup_load<FMT>(rg, ru, a, a.g, a.u, L.act_slot[task / tpe],
-                       (task % tpe) * kRowsGU + lane / kLprGU, lane_gu);
+    RowRegs<FMT, nch_gu<FMT>()> ng, nu;
+    if (task < c_end) load_task(task, rg, ru);
+    if (kAhead == 2 && task + c_step < c_end) load_task(task + c_step, ng, nu);
     for (; task < c_end; task += c_step) {
-      const int next = task + c_step;
-      RowRegs<FMT, kNChMax> ng, nu;
-      if (next < c_end)
-        gateup_load<FMT>(ng, nu, a, a.g, a.u, L.act_slot[next / tpe],
-                         (next % tpe) * kRowsGU + lane / kLprGU, lane_gu);
+      const int ahead = task + kAhead * c_step;
+      RowRegs<FMT, nch_gu<FMT>()> mg, mu;
+      if (ahead < c_end) load_task(ahead, mg, mu);
       const int u = task / tpe;
       const int i = (task % tpe) * kRowsGU + lane / kLprGU;
       const int st = L.act_start[u];
       const int n = L.act_start[u + 1] - st;
-      gateup_compute<FMT, kNG>(rg, ru, a, i, n, L.tok + st, L.bpair + st, 0, region_h(a), xs, xsum, vstride,
+      gateup_compute<FMT, kNGC>(rg, ru, a, i, n, L.tok + st, L.bpair + st, 0, region_h(a), xs, xsum, vstride,
                           lane_gu, epoch);
-      rg = ng;
-      ru = nu;
+      if constexpr (kAhead == 2) {
+        rg = ng;
+        ru = nu;
+        ng = mg;
+        nu = mu;
+      } else {
+        rg = mg;
+        ru = mu;
+      }
     }
   }
 
@@ -1464,9 +1486,10 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     uint32_t* xd = smem;                                    // reuses the token area
     float* sd = reinterpret_cast<float*>(xd + kVPP * kTMax * vs_d);
     float* pd = sd + kVPP * kTMax * ss_d;
+    if (TB > 1 && d_first < d_end) load_down(d_first, rd);
     int staged = -1;   // bucket whose activations are in the LDS
     for (int unit = d_first; unit < d_end; unit += d_step) {
-      RowRegs<FMT, kNChMax> nd;   // the next unit's rows load meanwhile
+      RowRegs<FMT, kNChD> nd;   // the next unit's rows load meanwhile
       if (unit + d_step < d_end) load_down(unit + d_step, nd);
       const int u = unit / nrb, rb = unit % nrb;
       const bool shared = u >= n_act;
@@ -1487,12 +1510,12 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
         const int nv = min(kNG, n - v0);
         float o[kNG];
         if constexpr (kVPP == 2) {
-          row_vecs_dot_hl<FMT, kNChMax, kNG>(rd, nch_d, lane_gd, kLprD, xd, sd, vs_d, ss_d, v0, nv,
+          row_vecs_dot_hl<FMT, kNChD, kNG>(rd, nch_d, lane_gd, kLprD, xd, sd, vs_d, ss_d, v0, nv,
                                              o);
         } else {
 #pragma unroll
           for (int v = 0; v < kNG; ++v)
-            o[v] = v < nv ? row_vec_dot<FMT, kNChMax>(rd, nch_d, lane_gd, kLprD,
+            o[v] = v < nv ? row_vec_dot<FMT, kNChD>(rd, nch_d, lane_gd, kLprD,
                                                      xd + (v0 + v) * vs_d, sd + (v0 + v) * ss_d)
                           : 0.f;
         }
@@ -1588,8 +1611,9 @@ bool layer_fused_ok(int fmt, int T, int k, int E, int H, int I) {
   const int lgu = fmt == MOE_W_Q4B32 ? Lanes<MOE_W_Q4B32>::kGU : Lanes<MOE_W_Q2B32>::kGU;
   const int ld = fmt == MOE_W_Q4B32 ? Lanes<MOE_W_Q4B32>::kD : Lanes<MOE_W_Q2B32>::kD;
   const int chunks = H / wpc, chunks_d = I / wpc;
-  if (chunks % lgu || chunks / lgu > kNChMax) return false;
-  if (chunks_d % ld || chunks_d / ld > kNChMax) return false;
+  const int ngu = fmt == MOE_W_Q2B32 ? nch_gu<MOE_W_Q2B32>() : 4;
+  if (chunks % lgu || chunks / lgu > ngu) return false;
+  if (chunks_d % ld || chunks_d / ld > kNChD) return false;
   if (fmt != MOE_W_F32 && (chunks > 64 ? (chunks % 64) != 0 : (chunks & (chunks - 1)) != 0))
     return false;
   // dynamic LDS beside the static routing tables (~19 KB) within 160 KB
