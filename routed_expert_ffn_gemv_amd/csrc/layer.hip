@@ -70,16 +70,33 @@ struct Lanes {
   static constexpr int kRowsD = kWaves * (64 / kD);         // rows per down unit
 };
 
+// Global-memory views of pointers.  Pointers read back from the LDS copy of
+// the arguments carry no address space, so the compiler would access them
+// with flat instructions -- and a flat access also counts against the LDS
+// wait counter, which makes every later LDS wait wait for HBM too.
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T* gmem(const T* p) {
+  return (const __attribute__((address_space(1))) T*)(p);
+}
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* gmem_w(T* p) {
+  return (__attribute__((address_space(1))) T*)(p);
+}
+__device__ __forceinline__ void store_miss(moe_miss* p, const moe_miss& m) {
+  *gmem_w(&p->expert) = m.expert;
+  *gmem_w(&p->token) = m.token;
+  *gmem_w(&p->gate) = m.gate;
+}
 template <typename V>
 __device__ __forceinline__ V ld_dev(const V* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load(gmem(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 template <typename V>
 __device__ __forceinline__ void st_dev(V* p, V v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(gmem_w(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void fadd_dev(float* p, float v) {
-  __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_fetch_add(gmem_w(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // Marks a register as rewritten here, so work derived from it is redone at
 // this point instead of being hoisted out of the enclosing loop (emits no
@@ -451,13 +468,13 @@ __device__ __forceinline__ void load_row(RowRegs<FMT, NCH>& R, const uint8_t* __
   for (int j = 0; j < NCH; ++j) {
     if (j < nch) {
       const int c = lane_g + j * lpr;
-      R.w[j] = *reinterpret_cast<const u32x4*>(codes + 16 * c);
+      R.w[j] = *gmem(reinterpret_cast<const u32x4*>(codes + 16 * c));
       if constexpr (FMT == MOE_W_Q2B32) {
-        R.sc[j] = *reinterpret_cast<const uint32_t*>(sc + 2 * c);
-        R.mn[j] = *reinterpret_cast<const uint32_t*>(mn + 2 * c);
+        R.sc[j] = *gmem(reinterpret_cast<const uint32_t*>(sc + 2 * c));
+        R.mn[j] = *gmem(reinterpret_cast<const uint32_t*>(mn + 2 * c));
       } else if constexpr (FMT == MOE_W_Q4B32) {
-        R.sc[j] = sc[c];
-        R.mn[j] = mn[c];
+        R.sc[j] = *gmem(sc + c);
+        R.mn[j] = *gmem(mn + c);
       }
     }
   }
@@ -857,10 +874,10 @@ __device__ __forceinline__ void router_load(RouterRegs<FMT>& R, const LayerArgs&
                                                         int64_t(e) * a.H);
       const int c = lane % lpr;
 #pragma unroll
-      for (int q = 0; q < RouterRegs<FMT>::kQ; ++q) R.w[q] = row[c * RouterRegs<FMT>::kQ + q];
+      for (int q = 0; q < RouterRegs<FMT>::kQ; ++q) R.w[q] = gmem(row)[c * RouterRegs<FMT>::kQ + q];
     }
   }
-  R.bias = (e < a.E && a.bias) ? a.bias[e] : 0.f;
+  R.bias = (e < a.E && a.bias) ? *gmem(a.bias + e) : 0.f;
 }
 
 // Logits of the row group's rows for tokens [t0, t0 + TG), published as
@@ -914,8 +931,8 @@ __device__ __forceinline__ void router_compute(const RouterRegs<FMT>& R, const L
       const float* xf = reinterpret_cast<const float*>(xs);
       for (int col = lane_g; col < a.H; col += lpr) {
         const float wv = a.rfmt == MOE_W_F32
-                             ? static_cast<const float*>(a.W)[int64_t(e) * a.H + col]
-                             : bf16_to_f32(static_cast<const uint16_t*>(a.W)[int64_t(e) * a.H + col]);
+                             ? *gmem(static_cast<const float*>(a.W) + int64_t(e) * a.H + col)
+                             : bf16_to_f32(*gmem(static_cast<const uint16_t*>(a.W) + int64_t(e) * a.H + col));
 #pragma unroll
         for (int t = 0; t < TB; ++t)
           if (t < nt) acc[t] = fmaf(wv, xf[t * vstride + col], acc[t]);
@@ -1121,16 +1138,16 @@ __device__ __forceinline__ void resolve_one(const LayerArgs& a, Lds& L, int e, f
                                              __builtin_amdgcn_mbcnt_lo(uint32_t(hit_mask), 0u));
   const int n_hit = __popcll(hit_mask);
   if (writer) {
-    if (valid && a.slot_idx) a.slot_idx[lane] = s;
+    if (valid && a.slot_idx) *gmem_w(a.slot_idx + lane) = s;
     if (valid && !hit) {
       moe_miss m;
       m.expert = e;
       m.token = 0;
       m.gate = g;
-      a.miss[mpos] = m;
+      store_miss(a.miss + mpos, m);
     }
-    if (lane == 0) a.miss_off[0] = 0;
-    if (lane == 1) a.miss_off[1] = __popcll(miss_mask);
+    if (lane == 0) *gmem_w(a.miss_off) = 0;
+    if (lane == 1) *gmem_w(a.miss_off + 1) = __popcll(miss_mask);
   }
   if (hit) {
     L.bpair[hpos] = lane;
@@ -1171,16 +1188,16 @@ __device__ __forceinline__ void resolve_multi(const LayerArgs& a, Lds& L, int P,
     n_miss += c;
   }
   if (writer) {
-    if (valid && a.slot_idx) a.slot_idx[tid] = s;
+    if (valid && a.slot_idx) *gmem_w(a.slot_idx + tid) = s;
     if (valid && !hit) {
       moe_miss m;
       m.expert = e;
       m.token = t;
       m.gate = L.gate[tid];
-      a.miss[mpos] = m;
+      store_miss(a.miss + mpos, m);
     }
-    if (valid && tid % k == 0) a.miss_off[t] = mpos;
-    if (tid == 0) a.miss_off[a.T] = n_miss;
+    if (valid && tid % k == 0) *gmem_w(a.miss_off + t) = mpos;
+    if (tid == 0) *gmem_w(a.miss_off + a.T) = n_miss;
   }
   // experts 2*tid and 2*tid + 1 (E <= 2 * kThreads)
   const int e0 = 2 * tid;
@@ -1356,8 +1373,8 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     if (lane < k) {
       L.gate[t * k + lane] = g;
       if (b == 0) {
-        a.idx[t * k + lane] = my_e;
-        a.gate[t * k + lane] = g;
+        *gmem_w(a.idx + t * k + lane) = my_e;
+        *gmem_w(a.gate + t * k + lane) = g;
       }
     }
     if (T == 1) resolve_one(a, L, my_e, g, lane, b == 0);
@@ -1368,7 +1385,9 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   }
   __syncthreads();
   const int n_act = L.n_act;
-  if (b == 0 && a.usage && tid < P) atomicAdd(a.usage + L.idx[tid], 1u);
+  if (b == 0 && a.usage && tid < P)
+    __hip_atomic_fetch_add(gmem_w(a.usage + L.idx[tid]), 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 
   // ---- C: the first down unit's loads, then routed gate/up
   const int Kd = a.I;
@@ -1394,31 +1413,42 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   if constexpr (TB > 1) {
     constexpr int kCostC = 1, kCostD = 2;
     const int n_db = n_act + (a.has_sh ? 1 : 0);
-    const int64_t totC = int64_t(tpe) * (kCostC * n_act + L.act_start[n_act]);
-    const int64_t totD = int64_t(nrb) * (kCostD * n_db + L.act_start[n_act] + (a.has_sh ? T : 0));
-    const int u = tid;
-    if (u <= n_act) {
-      const int nu = u < n_act ? L.act_start[u + 1] - L.act_start[u] : 0;
-      const int64_t c0 = int64_t(tpe) * (kCostC * u + L.act_start[u]);
-      const int64_t c1 = c0 + int64_t(tpe) * (kCostC + nu);
-      for (int w = 0; w <= kWaves; ++w) {
-        const int64_t bt = (int64_t(b) * kWaves + w) * totC / (int64_t(G) * kWaves);
-        if (u == n_act ? bt >= c0 : (bt >= c0 && bt < c1))
-          L.cstart[w] = u == n_act ? n_tasks
-                                   : u * tpe + int((bt - c0 + kCostC + nu - 1) / (kCostC + nu));
+    // (costs stay below 2^20; a bound's exact quotient a * tot / W comes from
+    // double arithmetic: the product is exact and no quotient lies within a
+    // rounding error of an integer it does not equal)
+    const int totC = tpe * (kCostC * n_act + L.act_start[n_act]);
+    const int totD = nrb * (kCostD * n_db + L.act_start[n_act] + (a.has_sh ? T : 0));
+    auto bound = [](int i, int tot, int parts) {
+      return int(floor(double(i) * double(tot) / double(parts)));
+    };
+    // One thread per range bound (kWaves + 1 task bounds, 2 unit bounds):
+    // a binary search for the bucket whose span of cumulative cost holds the
+    // bound's target, then the first task / unit of that bucket at or past it.
+    if (tid <= kWaves + 2) {
+      const bool is_c = tid <= kWaves;
+      const int n = is_c ? n_act : n_db;
+      const int rows = is_c ? tpe : nrb, fixed = is_c ? kCostC : kCostD;
+      const int bt = is_c ? bound(b * kWaves + tid, totC, G * kWaves)
+                          : bound(b + tid - (kWaves + 1), totD, G);
+      auto tokens_before = [&](int u) {   // tokens of buckets < u (the shared one last)
+        return u <= n_act ? L.act_start[u] : L.act_start[n_act] + T;
+      };
+      auto cum = [&](int u) { return rows * (fixed * u + tokens_before(u)); };
+      int lo = 0, hi = n;   // the largest u <= n with cum(u) <= bt
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cum(mid) <= bt) lo = mid;
+        else hi = mid - 1;
       }
-    }
-    if (u <= n_db) {
-      const int pre = u <= n_act ? L.act_start[u] : L.act_start[n_act] + T;   // tokens before u
-      const int nu = u < n_act ? L.act_start[u + 1] - L.act_start[u] : T;
-      const int64_t d0 = int64_t(nrb) * (kCostD * u + pre);
-      const int64_t d1 = d0 + int64_t(nrb) * (kCostD + nu);
-      for (int w = 0; w <= 1; ++w) {
-        const int64_t bt = int64_t(b + w) * totD / G;
-        if (u == n_db ? bt >= d0 : (bt >= d0 && bt < d1))
-          L.dstart[w] = u == n_db ? n_units
-                                  : u * nrb + int((bt - d0 + kCostD + nu - 1) / (kCostD + nu));
+      int v;
+      if (lo == n) {
+        v = is_c ? n_tasks : n_units;
+      } else {
+        const int cost = fixed + (lo < n_act ? L.act_start[lo + 1] - L.act_start[lo] : T);
+        v = lo * rows + (bt - cum(lo) + cost - 1) / cost;
       }
+      if (is_c) L.cstart[tid] = v;
+      else L.dstart[tid - (kWaves + 1)] = v;
     }
     __syncthreads();
     c_first = L.cstart[wave];
