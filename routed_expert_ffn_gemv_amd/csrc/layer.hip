@@ -352,17 +352,22 @@ __device__ __forceinline__ void token_block_sums(int T, int H, float* xsum, cons
 }
 
 
-// Tagged fp32 vectors published by other workgroups (h) into hi/lo bf16
-// vectors of the pair layout (F32 format: plain fp32), 16 columns per item.
+// Tagged fp32 vectors published by other workgroups (h), staged for the
+// down projection, 16 columns per item.  Quantised formats: fp16 in the pair
+// layout, each 32-column block scaled by a power of two that brings its
+// largest |h| into [0.5, 1) (bsc keeps the inverse, psum the sums of the
+// stored values), so no block overflows fp16 and each keeps 11 bits
+// relative to its largest value.  F32 format: plain fp32.
 // All loads of a batch are issued first; words that do not yet carry this
 // call's number are read again until they do (their producers never wait
-// on anything, so this ends).
+// on anything, so this ends).  Every thread calls it (the block maxima pass
+// between neighbouring lanes).
 template <int FMT>
 __device__ __forceinline__ void stage_h(const uint64_t* const* srcs, int n, int K, uint32_t* xd,
-                                        float* sd, float* psum, int vs, uint32_t epoch) {
+                                        float* sd, float* psum, float* bsc, int vs,
+                                        uint32_t epoch) {
   const int per_vec = K / 16;
   const int n_items = n * per_vec;
-  constexpr int kVPP = FMT == MOE_W_F32 ? 1 : 2;
   constexpr int kIt = 2;   // items per thread and batch
   for (int base = 0; base < n_items; base += kIt * kThreads) {
     uint64_t wv[kIt][16];
@@ -395,44 +400,50 @@ __device__ __forceinline__ void stage_h(const uint64_t* const* srcs, int n, int 
       const int it = base + r * kThreads + threadIdx.x;
       float v[16];
 #pragma unroll
-      for (int c = 0; c < 16; ++c) v[c] = tag_val(wv[r][c]);
-      if (it < n_items) {
-        const int p = it / per_vec, g16 = it % per_vec;
-        if constexpr (FMT == MOE_W_F32) {
+      for (int c = 0; c < 16; ++c) v[c] = src[r] ? tag_val(wv[r][c]) : 0.f;
+      if constexpr (FMT == MOE_W_F32) {
+        if (it < n_items) {
+          const int p = it / per_vec, g16 = it % per_vec;
           float* xf = reinterpret_cast<float*>(xd) + p * vs + g16 * 16;
 #pragma unroll
           for (int c = 0; c < 16; ++c) xf[c] = v[c];
-        } else {
-          uint32_t hi[16], lo[16];
-          float shi = 0.f, slo = 0.f;
+        }
+      } else {
+        // block maximum: items 2b and 2b + 1 of a vector sit in lanes 2j and
+        // 2j + 1 (per_vec is even and batches start at multiples of 512)
+        float amax = 0.f;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) amax = fmaxf(amax, fabsf(v[c]));
+        amax = fmaxf(amax, dpp_f32<0xB1>(amax));   // quad_perm [1,0,3,2]
+        uint32_t ex = (__float_as_uint(amax) >> 23) & 0xFFu;
+        ex = ex > 253u ? 253u : ex;
+        // amax in [2^(ex-127), 2^(ex-126)): scale by 2^(126-ex); zero and
+        // subnormal maxima keep scale 1
+        const float sc = ex == 0u ? 1.f : __uint_as_float((253u - ex) << 23);
+        const float inv = ex == 0u ? 1.f : __uint_as_float((ex + 1u) << 23);
+        if (it < n_items) {
+          const int p = it / per_vec, g16 = it % per_vec;
+          uint32_t hv[16];
+          float sum = 0.f;
 #pragma unroll
           for (int c = 0; c < 16; ++c) {
-            hi[c] = f32_to_bf16_bits(v[c]);
-            const float hf = bf16_to_f32(hi[c]);
-            lo[c] = f32_to_bf16_bits(v[c] - hf);
-            shi += hf;
-            slo += bf16_to_f32(lo[c]);
+            const _Float16 hh = static_cast<_Float16>(v[c] * sc);
+            hv[c] = __builtin_bit_cast(uint16_t, hh);
+            sum += static_cast<float>(hh);
           }
-          psum[(kVPP * p) * per_vec + g16] = shi;
-          psum[(kVPP * p + 1) * per_vec + g16] = slo;
-          uint32_t* dh = xd + (kVPP * p) * vs;
-          uint32_t* dl = xd + (kVPP * p + 1) * vs;
+          psum[p * per_vec + g16] = sum;
+          if ((g16 & 1) == 0) bsc[p * (K / 32) + (g16 >> 1)] = inv;
+          uint32_t* dh = xd + p * vs;
           if constexpr (FMT == MOE_W_Q2B32) {
             const int off = (g16 >> 2) * Fmt<FMT>::kCS + (g16 & 3) * 8;
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-              dh[off + s] = hi[s] | (hi[s + 8] << 16);
-              dl[off + s] = lo[s] | (lo[s + 8] << 16);
-            }
+            for (int q = 0; q < 8; ++q) dh[off + q] = hv[q] | (hv[q + 8] << 16);
           } else {
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
               const int off = (g16 >> 1) * Fmt<FMT>::kCS + ((g16 & 1) * 2 + q) * 4;
 #pragma unroll
-              for (int s = 0; s < 4; ++s) {
-                dh[off + s] = hi[8 * q + s] | (hi[8 * q + s + 4] << 16);
-                dl[off + s] = lo[8 * q + s] | (lo[8 * q + s + 4] << 16);
-              }
+              for (int t = 0; t < 4; ++t) dh[off + t] = hv[8 * q + t] | (hv[8 * q + t + 4] << 16);
             }
           }
         }
@@ -442,7 +453,7 @@ __device__ __forceinline__ void stage_h(const uint64_t* const* srcs, int n, int 
   __syncthreads();
   if (FMT != MOE_W_F32) {
     const int nb = K / 32;
-    for (int i = threadIdx.x; i < kVPP * n * nb; i += kThreads) {
+    for (int i = threadIdx.x; i < n * nb; i += kThreads) {
       const int v = i / nb, b = i % nb;
       sd[v * nb + b] = psum[v * per_vec + 2 * b] + psum[v * per_vec + 2 * b + 1];
     }
@@ -506,36 +517,6 @@ __device__ __forceinline__ void chunk_dot(u32x4 w, const uint32_t* xv, float* p)
   }
 }
 
-// One code chunk against the hi and lo halves of a split vector: each code
-// pair is unpacked once for both; p[bb] returns the sum of the two.
-template <int FMT>
-__device__ __forceinline__ void chunk_dot_hl(u32x4 w, const uint32_t* xh, const uint32_t* xl,
-                                             float* p) {
-  w = fresh(w);
-  const u32x4* h4 = reinterpret_cast<const u32x4*>(xh);
-  const u32x4* l4 = reinterpret_cast<const u32x4*>(xl);
-#pragma unroll
-  for (int bb = 0; bb < (FMT == MOE_W_Q2B32 ? 2 : 1); ++bb) {
-    u32x4 hh[4], ll[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      hh[q] = h4[4 * bb + q];
-      ll[q] = l4[4 * bb + q];
-    }
-    float a[4] = {0.f, 0.f, 0.f, 0.f}, c[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t pr = FMT == MOE_W_Q2B32 ? q2_pair(w[2 * bb + (q >> 1)], (q & 1) * 4 + e)
-                                                : q4_pair(w[q], e);
-        a[e] = dot2_bf16(pr, hh[q][e], a[e]);
-        c[e] = dot2_bf16(pr, ll[q][e], c[e]);
-      }
-    p[bb] = ((a[0] + a[1]) + (a[2] + a[3])) + ((c[0] + c[1]) + (c[2] + c[3]));
-  }
-}
-
 // The same for two code chunks (gate and up rows) against one vector chunk.
 template <int FMT>
 __device__ __forceinline__ void chunk_dot2(u32x4 wg, u32x4 wu, const uint32_t* xv,
@@ -595,34 +576,6 @@ __device__ __forceinline__ float row_vec_dot(const RowRegs<FMT, NCH>& R, int nch
       const float d = f16_to_f32(uint16_t(R.sc[j]));
       const float m = f16_to_f32(uint16_t(R.mn[j])) - 128.f * d;
       acc += d * p[0] + m * sv_base[c];
-    }
-  }
-  return acc;
-}
-
-// One row . a vector split into hi and lo bf16 halves (staged at xh / xl
-// with block sums sh / sl): the down projection of fp32 h in one pass.
-template <int FMT, int NCH>
-__device__ __forceinline__ float row_vec_dot_hl(const RowRegs<FMT, NCH>& R, int nch, int lane_g,
-                                                int lpr, const uint32_t* xh, const float* sh,
-                                                const uint32_t* xl, const float* sl) {
-  float acc = 0.f;
-#pragma unroll
-  for (int j = 0; j < NCH; ++j) {
-    if (j >= nch) continue;
-    const int c = lane_g + j * lpr;
-    float p[2];
-    chunk_dot_hl<FMT>(R.w[j], xh + c * Fmt<FMT>::kCS, xl + c * Fmt<FMT>::kCS, p);
-    if constexpr (FMT == MOE_W_Q2B32) {
-      const float d0 = f16_to_f32(uint16_t(R.sc[j] & 0xFFFFu));
-      const float d1 = f16_to_f32(uint16_t(R.sc[j] >> 16));
-      const float m0 = f16_to_f32(uint16_t(R.mn[j] & 0xFFFFu)) - 128.f * d0;
-      const float m1 = f16_to_f32(uint16_t(R.mn[j] >> 16)) - 128.f * d1;
-      acc += (d0 * p[0] + m0 * (sh[2 * c] + sl[2 * c])) + (d1 * p[1] + m1 * (sh[2 * c + 1] + sl[2 * c + 1]));
-    } else {
-      const float d = f16_to_f32(uint16_t(R.sc[j]));
-      const float m = f16_to_f32(uint16_t(R.mn[j])) - 128.f * d;
-      acc += d * p[0] + m * (sh[c] + sl[c]);
     }
   }
   return acc;
@@ -746,12 +699,48 @@ __device__ __forceinline__ void row_pair_vecs_dot(const RowRegs<FMT, NCH>& RG,
   }
 }
 
-// One row . the hi and lo halves of h for tokens v0 .. v0 + nv - 1 (hi of
-// token t at xd + 2t * vs with block sums at sd + 2t * ss, lo at 2t + 1).
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+// a.lo*b.lo + a.hi*b.hi + c with fp16 pairs and fp32 accumulation
+// (v_dot2_f32_f16).  The pairs come in as scalars: a bit cast of a vector
+// element in place reads the wrong element.
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c,
+                                false);
+}
+
+// fp16 code pairs (1024 + q) of a block, for the fp16-staged h: OR-ing a
+// code below 1024 into the mantissa of fp16(1024) = 0x6400 gives 1024 + q.
+template <int FMT>
+__device__ __forceinline__ void unpack_block_f16(u32x4 w, int bb, uint32_t (&pr)[16]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      pr[q * 4 + e] = FMT == MOE_W_Q2B32
+                          ? ((w[2 * bb + (q >> 1)] >> (2 * ((q & 1) * 4 + e))) & 0x00030003u) | 0x64006400u
+                          : ((w[q] >> (4 * e)) & 0x000F000Fu) | 0x64006400u;
+}
+__device__ __forceinline__ float block_dot_f16(const uint32_t (&pr)[16], const u32x4* x4) {
+  float a[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const u32x4 xx = x4[q];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      a[e] = dot2_f16(pr[q * 4 + e], xx[e], a[e]);
+  }
+  return (a[0] + a[1]) + (a[2] + a[3]);
+}
+
+// One row . h of tokens v0 .. v0 + nv - 1, staged by stage_h (token t's
+// vector at xd + t * vs, block sums at sd + t * ss, block scales at
+// bsc + t * ss).  Per block: 2^e * (d * sum (1024 + q) h' + (m - 1024 d) *
+// sum h'), with h' the scaled fp16 values.
 template <int FMT, int NCH, int NG>
-__device__ __forceinline__ void row_vecs_dot_hl(const RowRegs<FMT, NCH>& R, int nch, int lane_g,
-                                                int lpr, const uint32_t* xd, const float* sd,
-                                                int vs, int ss, int v0, int nv, float (&o)[NG]) {
+__device__ __forceinline__ void row_vecs_dot_f16(const RowRegs<FMT, NCH>& R, int nch, int lane_g,
+                                                 int lpr, const uint32_t* xd, const float* sd,
+                                                 const float* bsc, int vs, int ss, int v0, int nv,
+                                                 float (&o)[NG]) {
 #pragma unroll
   for (int v = 0; v < NG; ++v) o[v] = 0.f;
   constexpr int kBlk = FMT == MOE_W_Q2B32 ? 2 : 1;
@@ -762,18 +751,17 @@ __device__ __forceinline__ void row_vecs_dot_hl(const RowRegs<FMT, NCH>& R, int 
     const u32x4 w = fresh(R.w[j]);
 #pragma unroll
     for (int bb = 0; bb < kBlk; ++bb) {
-      float d, m;
-      block_scales<FMT>(R.sc[j], R.mn[j], bb, d, m);
+      const uint32_t dsh = FMT == MOE_W_Q2B32 ? 16u * uint32_t(bb) : 0u;
+      const float d = f16_to_f32(uint16_t((R.sc[j] >> dsh) & 0xFFFFu));
+      const float m = f16_to_f32(uint16_t((R.mn[j] >> dsh) & 0xFFFFu)) - 1024.f * d;
       uint32_t pr[16];
-      unpack_block<FMT>(w, bb, pr);
+      unpack_block_f16<FMT>(w, bb, pr);
 #pragma unroll
       for (int v = 0; v < NG; ++v) {
         if (v >= nv) continue;
-        const int t2 = 2 * (v0 + v);
-        const u32x4* h4 = reinterpret_cast<const u32x4*>(xd + t2 * vs + c * Fmt<FMT>::kCS) + 4 * bb;
-        const u32x4* l4 = reinterpret_cast<const u32x4*>(xd + (t2 + 1) * vs + c * Fmt<FMT>::kCS) + 4 * bb;
-        const float sx = sd[t2 * ss + kBlk * c + bb] + sd[(t2 + 1) * ss + kBlk * c + bb];
-        o[v] += d * (block_dot(pr, h4) + block_dot(pr, l4)) + m * sx;
+        const int t = v0 + v, blk = kBlk * c + bb;
+        const u32x4* h4 = reinterpret_cast<const u32x4*>(xd + t * vs + c * Fmt<FMT>::kCS) + 4 * bb;
+        o[v] += bsc[t * ss + blk] * (d * block_dot_f16(pr, h4) + m * sd[t * ss + blk]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1391,7 +1379,6 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
 
   // ---- C: the first down unit's loads, then routed gate/up
   const int Kd = a.I;
-  constexpr int kVPP = FMT == MOE_W_F32 ? 1 : 2;
   const int vs_d = FMT == MOE_W_F32 ? Kd : (Kd / Fmt<FMT>::kWPC) * Fmt<FMT>::kCS;
   const int ss_d = Kd / 32;
   const int nch_d = chunks_of<FMT>(Kd) / kLprD;
@@ -1514,8 +1501,9 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   // ---- D: down units (expert or shared, block of rows), y += gate * D h
   {
     uint32_t* xd = smem;                                    // reuses the token area
-    float* sd = reinterpret_cast<float*>(xd + kVPP * kTMax * vs_d);
-    float* pd = sd + kVPP * kTMax * ss_d;
+    float* sd = reinterpret_cast<float*>(xd + kTMax * vs_d);
+    float* pd = sd + kTMax * ss_d;
+    float* bsc = pd + kTMax * (Kd / 16);
     if (TB > 1 && d_first < d_end) load_down(d_first, rd);
     int staged = -1;   // bucket whose activations are in the LDS
     for (int unit = d_first; unit < d_end; unit += d_step) {
@@ -1532,16 +1520,16 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
           srcs[tid] = shared ? region_h_sh(a) + int64_t(tid) * Kd
                              : region_h(a) + int64_t(L.bpair[st + tid]) * Kd;
         __syncthreads();
-        stage_h<FMT>(srcs, n, Kd, xd, sd, pd, vs_d, epoch);
+        stage_h<FMT>(srcs, n, Kd, xd, sd, pd, bsc, vs_d, epoch);
         __syncthreads();
         staged = u;
       }
       for (int v0 = 0; v0 < n; v0 += kNG) {
         const int nv = min(kNG, n - v0);
         float o[kNG];
-        if constexpr (kVPP == 2) {
-          row_vecs_dot_hl<FMT, kNChD, kNG>(rd, nch_d, lane_gd, kLprD, xd, sd, vs_d, ss_d, v0, nv,
-                                             o);
+        if constexpr (FMT != MOE_W_F32) {
+          row_vecs_dot_f16<FMT, kNChD, kNG>(rd, nch_d, lane_gd, kLprD, xd, sd, bsc, vs_d, ss_d, v0,
+                                            nv, o);
         } else {
 #pragma unroll
           for (int v = 0; v < kNG; ++v)
@@ -1627,9 +1615,8 @@ size_t layer_fused_lds(int fmt, int T, int E, int H, int I) {
   // A-C: tokens, block sums, group sums, logits
   const size_t a = size_t(T) * (vec_bytes(fmt, H) + (H / 32) * 4 + (H / 16) * 4) +
                    size_t(T) * E * 4;
-  // D: 2 vectors per token (hi, lo), block sums, group sums (sized for 16 tokens)
-  const int vpp = fmt == MOE_W_F32 ? 1 : 2;
-  const size_t d = size_t(vpp) * kTMax * (vec_bytes(fmt, I) + (I / 32) * 4 + (I / 16) * 4);
+  // D: a vector per token, block sums, group sums, block scales (16 tokens)
+  const size_t d = size_t(kTMax) * (vec_bytes(fmt, I) + (I / 32) * 4 + (I / 16) * 4 + (I / 32) * 4);
   return a > d ? a : d;
 }
 
