@@ -47,6 +47,79 @@ def test_small_layer(name, path):
             assert rowwise_rel_err(host(o["shared_out"]), ref["shared_out"]) <= TOL
 
 
+# Shapes that take the fused launch (gate/up rows of whole 16-lane chunk
+# sets, down rows of whole 4- or 8-lane sets), for every token-count bucket
+# of the kernel, with and without the shared expert.
+FUSED = {
+    "q2_T1": small_cfg(E=64, k=8, H=1024, I=256, T=1, bias="zipf", seed=81),
+    "q2_T3": small_cfg(E=64, k=8, H=1024, I=256, T=3, bias="zipf", seed=82),
+    "q2_T9": small_cfg(E=96, k=6, H=1024, I=256, T=9, bias="zipf", seed=83),
+    "q4_T16": small_cfg(E=64, k=10, H=1024, I=256, T=16, wfmt="q4", bias="zipf", seed=84),
+    "q2_T16_no_shared": small_cfg(E=48, k=10, H=1024, I=256, T=16, shared=False, seed=85),
+}
+
+
+@pytest.mark.parametrize("name", list(FUSED))
+def test_fused_small(name):
+    cfg = FUSED[name]
+    say(f"[gpu] fused small {name}: E={cfg.E} k={cfg.k} H={cfg.H} I={cfg.I} T={cfg.T}")
+    x, _ = oracle.margin_x(cfg, 0)
+    L = DeviceLayer(cfg, 0, x=x)
+    o = L.run_layer()
+    ref = L.oracle()
+    check_routing(o, ref, cfg.k)
+    assert rowwise_rel_err(host(o["y"]), ref["y"]) <= TOL
+
+
+def test_fused_large_activations():
+    """Activations 2^8 times larger (h near 10^5, beyond the fp16 range):
+    the down projection's per-block scaling keeps the outputs within
+    tolerance.  Routing comes from the bias alone (zero router weights), so
+    the large activations do not reach the logits."""
+    import torch
+    cfg = small_cfg(E=64, k=8, H=1024, I=256, T=3, bias="zipf", seed=86)
+    say("[gpu] fused layer, large activations")
+    x, _ = oracle.margin_x(cfg, 0)
+    f = (x.astype(np.uint32) << 16).view(np.float32) * np.float32(256.0)
+    x = (f.view(np.uint32) >> 16).astype(np.uint16)          # exact: a power of two
+    L = DeviceLayer(cfg, 0, x=x)
+    bias = (np.random.default_rng(4).permutation(cfg.E) * 0.01).astype(np.float32)
+    L.inp["router_w"].zero_()
+    L.inp["bias"].copy_(torch.from_numpy(bias))
+    o = L.run_layer()
+    logits = oracle.router(x, np.zeros((cfg.E, cfg.H), np.uint16), cfg.router_fmt, bias)
+    idx, gate = oracle.topk(logits, cfg.k)
+    slot_idx, me, mt, mg, moff = oracle.resolve(idx, gate, cfg.E)
+    route = {"logits": logits, "idx": idx, "gate": gate, "slot_idx": slot_idx,
+             "miss_expert": me, "miss_token": mt, "miss_gate": mg, "miss_off": moff}
+    ref = oracle.layer_from_synth(cfg, 0, x, route=route)
+    check_routing(o, ref, cfg.k)
+    y = host(o["y"])
+    assert np.isfinite(y).all() and np.abs(ref["y"]).max() > 65504
+    assert rowwise_rel_err(y, ref["y"]) <= TOL
+
+
+def test_fused_tiered_small_with_misses():
+    """The fused launch on a partial slot table: misses listed bit-exactly,
+    y holds the hits."""
+    cfg = small_cfg(E=64, k=6, H=1024, I=256, T=5, bias="zipf", seed=87)
+    say("[gpu] fused tiered small layer with misses")
+    x, _ = oracle.margin_x(cfg, 0)
+    rng = np.random.default_rng(3)
+    resident = np.sort(rng.choice(cfg.E, 24, replace=False))
+    slot_of = np.full(cfg.E, -1, np.int32)
+    slot_of[resident] = np.arange(len(resident))[::-1]
+    from synth import device as sdev
+    pool = sdev.expert_pool(cfg, [0] * len(resident),
+                            [int(resident[len(resident) - 1 - s]) for s in range(len(resident))])
+    L = DeviceLayer(cfg, 0, x=x, pool=pool, slot_of=slot_of, num_slots=len(resident))
+    o = L.run_layer()
+    ref = L.oracle()
+    assert len(ref["miss_expert"]) > 0
+    check_routing(o, ref, cfg.k)
+    assert rowwise_rel_err(host(o["y"]), ref["y"]) <= TOL
+
+
 def _tie_bias(pattern, E, seed):
     e = np.arange(E)
     if pattern == "levels":      # four values, ~E/4 experts each
