@@ -1457,11 +1457,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     load_row<FMT, kNChD>(rd, D.codes + slot * a.mat_bytes + rr_ * row_bytes_d, D.scale + blk,
                            D.mn + blk, nch_d, lane_gd, kLprD);
   };
-  // one token: the first down unit's rows load during gate/up; several
-  // tokens keep those registers for the gate/up prefetch instead
-  if (TB == 1 && d_first < d_end) load_down(d_first, rd);
   uint64_t arr = 0;
-  if (b == 0 && tid < G) arr = ld_dev(region_arrive(a) + tid);
   {
     // each wave's tasks in turn, the next task's rows loading while the
     // current one computes
@@ -1476,6 +1472,10 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     RowRegs<FMT, nch_gu<FMT>()> ng, nu;
     if (task < c_end) load_task(task, rg, ru);
     if (kAhead == 2 && task + c_step < c_end) load_task(task + c_step, ng, nu);
+    // one token: the first down unit's rows load during gate/up (after its
+    // rows, which are needed first); several tokens keep those registers for
+    // the gate/up prefetch instead
+    if (TB == 1 && d_first < d_end) load_down(d_first, rd);
     for (; task < c_end; task += c_step) {
       const int ahead = task + kAhead * c_step;
       RowRegs<FMT, nch_gu<FMT>()> mg, mu;
@@ -1505,6 +1505,9 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     float* pd = sd + kTMax * ss_d;
     float* bsc = pd + kTMax * (Kd / 16);
     if (TB > 1 && d_first < d_end) load_down(d_first, rd);
+    // the arrival words, read while the first unit's activations are polled
+    // for (issued here, no later register reuse has to wait for them)
+    if (b == 0 && tid < G) arr = ld_dev(region_arrive(a) + tid);
     int staged = -1;   // bucket whose activations are in the LDS
     for (int unit = d_first; unit < d_end; unit += d_step) {
       RowRegs<FMT, kNChD> nd;   // the next unit's rows load meanwhile
