@@ -268,7 +268,7 @@ struct Lds {
   alignas(16) uint64_t rkey[kThreads + 8];   // segment maxima, then candidates (top-k)
   uint64_t tau[kTMax];       // per-token thresholds
   int ncand[kTMax];          // per-token candidate counts
-  uint32_t tmp[32];
+  alignas(16) uint32_t tmp[32];
   int cstart[kWaves + 1];   // this workgroup's waves' gate/up task ranges
   int dstart[2];            // this workgroup's down unit range
   int n_act;
@@ -1149,6 +1149,157 @@ __device__ __forceinline__ void resolve_one(const LayerArgs& a, Lds& L, int e, f
   }
 }
 
+// Orders this wave's LDS accesses across its lanes (LDS operations of one
+// wave complete in order; this keeps the compiler from moving them).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Routing of one token, two barriers in all.  Thread j polls the logits of
+// experts j and j + kThreads; the 32 segments of 16 neighbouring threads
+// publish the logit bits of their largest key.  Then every wave, for itself:
+//  - tau = the k-th largest of those 32 values: k segment maxima reach it,
+//    so the k best keys all do (lane l counts the values above value l % 32
+//    in half l / 32 of the list; the two halves are added);
+//  - the wave's candidates, the keys whose logit bits reach tau, take slots
+//    of one list through one LDS add per wave;
+// and after the second barrier, again every wave for itself (the tables it
+// writes are the same in every wave, so no further barrier is needed):
+//  - a candidate's rank is the number of larger candidate keys (keys are
+//    unique), and the candidate of rank r < k is choice r;
+//  - the gates (softmax over the k chosen logits) and the resolution.
+// More than 64 candidates (many equal logits) or k > kTopkListMax: the
+// per-wave selection instead.  lg receives the logits.  Only wave 0 of a
+// writer workgroup stores the outputs.
+__device__ __forceinline__ void route_token(const LayerArgs& a, float* lg, int E, int k, Lds& L,
+                                            uint32_t epoch, bool writer) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int kR = kEMax / kThreads;
+  uint64_t w[kR];
+#pragma unroll
+  for (int r = 0; r < kR; ++r)
+    if (tid + r * kThreads < E) w[r] = ld_dev(region_lg(a) + tid + r * kThreads);
+  for (;;) {
+    bool ok = true;
+#pragma unroll
+    for (int r = 0; r < kR; ++r) ok = ok && (tid + r * kThreads >= E || tag_ok(w[r], epoch));
+    if (ok) break;
+    __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int r = 0; r < kR; ++r)
+      if (tid + r * kThreads < E && !tag_ok(w[r], epoch))
+        w[r] = ld_dev(region_lg(a) + tid + r * kThreads);
+  }
+  uint64_t key[kR];   // 0: no expert
+  uint32_t m = 0u;    // largest logit bits of the thread
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    const int e = tid + r * kThreads;
+    key[r] = 0ull;
+    if (e < E) {
+      const float v = tag_val(w[r]);
+      lg[e] = v;
+      const uint32_t ob = ordered_bits(v);
+      key[r] = (uint64_t(ob) << 32) | uint64_t(~uint32_t(e));
+      m = max(m, ob);
+    }
+  }
+  m = max(m, dpp_u32<0xB1>(m));    // quad_perm [1,0,3,2]
+  m = max(m, dpp_u32<0x4E>(m));    // quad_perm [2,3,0,1]
+  m = max(m, dpp_u32<0x141>(m));   // row_half_mirror
+  m = max(m, dpp_u32<0x140>(m));   // row_mirror
+  if ((tid & 15) == 0) L.tmp[tid >> 4] = m;
+  if (tid < 64) L.rkey[tid] = 0ull;   // the candidate list's empty slots
+  __syncthreads();
+  const bool thresh = k <= kTopkListMax;
+  if (thresh) {
+    const uint32_t my = L.tmp[lane & 31];
+    const u32x4* half = reinterpret_cast<const u32x4*>(L.tmp) + 4 * (lane >> 5);
+    int gt = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 o = half[q];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) gt += o[c] > my ? 1 : 0;
+    }
+    gt += __shfl_xor(gt, 32, 64);
+    // the smallest value with fewer than k larger ones (as ~max of ~value)
+    const uint32_t tau = ~wave_max_u32(gt <= k - 1 ? ~my : 0u);
+    uint64_t cm[kR];
+    int cnt = 0;
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      cm[r] = __ballot(key[r] != 0ull && uint32_t(key[r] >> 32) >= tau);
+      cnt += __popcll(cm[r]);
+    }
+    int base = 0;
+    if (cnt > 0) {
+      if (lane == 0) base = atomicAdd(&L.ncand[0], cnt);
+      base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        const int pos = base + lanes_below(cm[r]);
+        if (((cm[r] >> lane) & 1ull) && pos < 64) L.rkey[pos] = key[r];
+        base += __popcll(cm[r]);
+      }
+    }
+  }
+  __syncthreads();
+  // The count, this lane's candidate and the first eight candidates are
+  // read together; list slots past the count hold key 0 (zeroed before the
+  // first barrier), which is below every key.
+  const int n = thresh ? L.ncand[0] : 65;
+  const uint64_t ck = L.rkey[lane];
+  auto rank_step = [&](int j0, int r) {   // candidates j0 .. j0 + 7 above ck
+    u32x4 q[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) q[h] = reinterpret_cast<const u32x4*>(L.rkey + j0)[h];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      r += ((uint64_t(q[h][1]) << 32) | q[h][0]) > ck ? 1 : 0;
+      r += ((uint64_t(q[h][3]) << 32) | q[h][2]) > ck ? 1 : 0;
+    }
+    return r;
+  };
+  int r = rank_step(0, 0);
+  int my_e;
+  float my_v;
+  if (n <= 64) {
+    for (int j0 = 8; j0 < n; j0 += 8) r = rank_step(j0, r);
+    // choice r moves to lane r (k <= 16 < 63, the lane that takes the rest)
+    const int to = 4 * ((lane < n && r < k) ? r : 63);
+    const uint32_t hi = uint32_t(__builtin_amdgcn_ds_permute(to, int(uint32_t(ck >> 32))));
+    const uint32_t lo = uint32_t(__builtin_amdgcn_ds_permute(to, int(uint32_t(ck))));
+    my_e = int(~lo);
+    my_v = key_value(hi);
+  } else if (E <= 512) {
+    wave_topk<8>(lg, E, k, lane, &my_e, &my_v);
+  } else {
+    wave_topk<16>(lg, E, k, lane, &my_e, &my_v);
+  }
+  // gates: softmax over the k chosen logits (choice 0 is the largest)
+  if (lane >= k) {
+    my_e = 0;
+    my_v = 0.f;
+  }
+  const float vmax = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_v), 0));
+  const float ex = lane < k ? __expf(my_v - vmax) : 0.f;
+  const float g = ex * __frcp_rn(wave_sum_f32(ex));
+  const bool out = writer && wave == 0;
+  if (lane < k) {
+    L.idx[lane] = my_e;
+    L.gate[lane] = g;
+    if (out) {
+      *gmem_w(a.idx + lane) = my_e;
+      *gmem_w(a.gate + lane) = g;
+    }
+  }
+  resolve_one(a, L, my_e, g, lane, out);
+  wave_lds_sync();
+}
+
 // Resolution of the P = T*k pairs of T >= 2 tokens (thread p = pair p).
 // Misses keep pair order (a ballot scan).  Hits are bucketed by expert, the
 // buckets in ascending expert order, each bucket's pairs in token order (a
@@ -1302,7 +1453,9 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   if (tid == 0) st_dev(region_arrive(a) + b, tag_word(0.f, epoch));
 
   // ---- B: every logit of this call, then routing
-  {
+  if constexpr (TB == 1) {
+    route_token(a, lg, E, k, L, epoch, b == 0);
+  } else {
     const int n_lg = T * E;
     constexpr int kR = TB * kEMax / kThreads > 16 ? 16 : TB * kEMax / kThreads;
     for (int base = 0; base < n_lg; base += kR * kThreads) {
@@ -1333,7 +1486,6 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
         if (i < n_lg) lg[i] = tag_val(w[r]);
       }
     }
-  }
   __syncthreads();
   const bool thresh = k <= kTopkListMax;
   if (thresh) topk_threshold<TB>(lg, T, E, k, L);
@@ -1365,13 +1517,11 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
         *gmem_w(a.gate + t * k + lane) = g;
       }
     }
-    if (T == 1) resolve_one(a, L, my_e, g, lane, b == 0);
-  }
-  if (T > 1) {
-    __syncthreads();
-    resolve_multi(a, L, P, b == 0);
   }
   __syncthreads();
+  resolve_multi(a, L, P, b == 0);   // T >= 2 here
+  __syncthreads();
+  }
   const int n_act = L.n_act;
   if (b == 0 && a.usage && tid < P)
     __hip_atomic_fetch_add(gmem_w(a.usage + L.idx[tid]), 1u, __ATOMIC_RELAXED,

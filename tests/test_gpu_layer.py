@@ -52,6 +52,8 @@ def test_small_layer(name, path):
 # of the kernel, with and without the shared expert.
 FUSED = {
     "q2_T1": small_cfg(E=64, k=8, H=1024, I=256, T=1, bias="zipf", seed=81),
+    "q2_T1_E1024": small_cfg(E=1024, k=16, H=1024, I=256, T=1, bias="zipf", seed=88),
+    "q4_T1_E300_k20": small_cfg(E=300, k=20, H=1024, I=256, T=1, wfmt="q4", seed=89),
     "q2_T3": small_cfg(E=64, k=8, H=1024, I=256, T=3, bias="zipf", seed=82),
     "q2_T9": small_cfg(E=96, k=6, H=1024, I=256, T=9, bias="zipf", seed=83),
     "q4_T16": small_cfg(E=64, k=10, H=1024, I=256, T=16, wfmt="q4", bias="zipf", seed=84),
@@ -140,6 +142,14 @@ TIES = {
     "T3_crowd": dict(E=1024, k=8, T=3, pattern="crowd128"),
     "T9_crowd": dict(E=1024, k=10, T=9, pattern="crowd32"),
     "T4_k20": dict(E=64, k=20, T=4, pattern="levels"),
+    # one token in the fused launch (H = 1024, I = 256): ties at the
+    # threshold within 64 candidates, more than 64 candidates, k above the
+    # threshold selection's limit, two logits per thread (E > 512)
+    "T1_fused_crowd32": dict(E=1024, k=10, T=1, pattern="crowd32", H=1024, I=256),
+    "T1_fused_crowd128": dict(E=1024, k=8, T=1, pattern="crowd128", H=1024, I=256),
+    "T1_fused_levels": dict(E=512, k=10, T=1, pattern="levels", H=1024, I=256),
+    "T1_fused_equal": dict(E=256, k=8, T=1, pattern="equal", H=1024, I=256),
+    "T1_fused_k20": dict(E=64, k=20, T=1, pattern="levels", H=1024, I=256),
 }
 
 
@@ -150,7 +160,8 @@ def test_tied_logits(name, path):
     lower expert id wins every tie, bit for bit."""
     import torch
     c = TIES[name]
-    cfg = small_cfg(E=c["E"], k=c["k"], H=128, I=64, T=c["T"], bias="zipf", seed=41)
+    cfg = small_cfg(E=c["E"], k=c["k"], H=c.get("H", 128), I=c.get("I", 64), T=c["T"],
+                    bias="zipf", seed=41)
     say(f"[gpu] tied logits {name} via {path}: E={cfg.E} k={cfg.k} T={cfg.T}")
     L = DeviceLayer(cfg, 0)
     bias = _tie_bias(c["pattern"], cfg.E, 5)
