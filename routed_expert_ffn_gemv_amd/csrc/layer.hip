@@ -1527,7 +1527,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     __hip_atomic_fetch_add(gmem_w(a.usage + L.idx[tid]), 1u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
 
-  // ---- C: the first down unit's loads, then routed gate/up
+  // ---- C: routed gate/up
   const int Kd = a.I;
   const int vs_d = FMT == MOE_W_F32 ? Kd : (Kd / Fmt<FMT>::kWPC) * Fmt<FMT>::kCS;
   const int ss_d = Kd / 32;
@@ -1607,6 +1607,38 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     load_row<FMT, kNChD>(rd, D.codes + slot * a.mat_bytes + rr_ * row_bytes_d, D.scale + blk,
                            D.mn + blk, nch_d, lane_gd, kLprD);
   };
+  // One load per 128-byte line of this wave's share of a unit's rows (codes,
+  // then scales and minima), whose values are not used: it brings the lines
+  // into this XCD's L2 for one address-unit slot per wave instead of one per
+  // row chunk.  Lines past the wave's 64 lanes are left out.  Every lane
+  // loads (spare lanes and unit < 0 read the hand-off region), so that the
+  // load is issued on every path and waits for earlier loads need not wait
+  // for it.
+  auto prefetch_down = [&](int unit) -> uint32_t {
+    uintptr_t p = reinterpret_cast<uintptr_t>(a.region);
+    if (unit >= 0) {
+      const int u = unit / nrb, rb = unit % nrb;
+      const bool shared = u >= n_act;
+      const Planes D = shared ? a.sd : a.d;
+      const int slot = shared ? 0 : L.act_slot[u];
+      const int r0 = rb * kRowsD + wave * (64 / kLprD);
+      const int nr = max(0, min(64 / kLprD, a.H - r0));
+      const int nl_c = int((nr * row_bytes_d + 127) / 128);
+      const uintptr_t c0 = reinterpret_cast<uintptr_t>(D.codes + slot * a.mat_bytes + r0 * row_bytes_d);
+      p = lane < nl_c ? c0 + uintptr_t(lane) * 128 : p;
+      if constexpr (FMT != MOE_W_F32) {
+        const int64_t blk = int64_t(slot) * a.mat_blocks + int64_t(r0) * ss_d;
+        const int nl_s = (nr * ss_d * 2 + 127) / 128;
+        const int l = lane - nl_c;
+        const uintptr_t s0 = reinterpret_cast<uintptr_t>(D.scale + blk);
+        const uintptr_t m0 = reinterpret_cast<uintptr_t>(D.mn + blk);
+        p = (l >= 0 && l < nl_s) ? s0 + uintptr_t(l) * 128 : p;
+        p = (l >= nl_s && l < 2 * nl_s) ? m0 + uintptr_t(l - nl_s) * 128 : p;
+      }
+    }
+    return *gmem(reinterpret_cast<const uint32_t*>(p & ~uintptr_t(3)));
+  };
+  uint32_t pf = 0u;
   uint64_t arr = 0;
   {
     // each wave's tasks in turn, the next task's rows loading while the
@@ -1622,20 +1654,29 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     RowRegs<FMT, nch_gu<FMT>()> ng, nu;
     if (task < c_end) load_task(task, rg, ru);
     if (kAhead == 2 && task + c_step < c_end) load_task(task + c_step, ng, nu);
-    // one token: the first down unit's rows load during gate/up (after its
-    // rows, which are needed first); several tokens keep those registers for
-    // the gate/up prefetch instead
-    if (TB == 1 && d_first < d_end) load_down(d_first, rd);
+    // one token: the first down unit's lines head for the L2 meanwhile
+    if constexpr (TB == 1) pf = prefetch_down(d_first < d_end ? d_first : -1);
+    auto compute_task = [&](int t, const RowRegs<FMT, nch_gu<FMT>()>& g,
+                            const RowRegs<FMT, nch_gu<FMT>()>& up) {
+      const int u = t / tpe;
+      const int i = (t % tpe) * kRowsGU + lane / kLprGU;
+      const int st = L.act_start[u];
+      const int n = L.act_start[u + 1] - st;
+      gateup_compute<FMT, kNGC>(g, up, a, i, n, L.tok + st, L.bpair + st, 0, region_h(a), xs,
+                                xsum, vstride, lane_gu, epoch);
+    };
+    // At most one task (one token, the usual case): no loop, so no load is
+    // issued on one path and not on another, which would make the waits
+    // for the rows also wait for the prefetch.
+    if (TB == 1 && task + c_step >= c_end) {
+      if (task < c_end) compute_task(task, rg, ru);
+      task = c_end;
+    }
     for (; task < c_end; task += c_step) {
       const int ahead = task + kAhead * c_step;
       RowRegs<FMT, nch_gu<FMT>()> mg, mu;
       if (ahead < c_end) load_task(ahead, mg, mu);
-      const int u = task / tpe;
-      const int i = (task % tpe) * kRowsGU + lane / kLprGU;
-      const int st = L.act_start[u];
-      const int n = L.act_start[u + 1] - st;
-      gateup_compute<FMT, kNGC>(rg, ru, a, i, n, L.tok + st, L.bpair + st, 0, region_h(a), xs, xsum, vstride,
-                          lane_gu, epoch);
+      compute_task(task, rg, ru);
       if constexpr (kAhead == 2) {
         rg = ng;
         ru = nu;
@@ -1654,7 +1695,10 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     float* sd = reinterpret_cast<float*>(xd + kTMax * vs_d);
     float* pd = sd + kTMax * ss_d;
     float* bsc = pd + kTMax * (Kd / 16);
-    if (TB > 1 && d_first < d_end) load_down(d_first, rd);
+    // The first unit's rows load here, not during gate/up: there they would
+    // queue ahead of other waves' gate/up rows in the CU's address unit,
+    // which would then finish later.
+    if (d_first < d_end) load_down(d_first, rd);
     // the arrival words, read while the first unit's activations are polled
     // for (issued here, no later register reuse has to wait for them)
     if (b == 0 && tid < G) arr = ld_dev(region_arrive(a) + tid);
@@ -1714,6 +1758,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     __syncthreads();
     if (tid == 0) st_dev(region_calls(a), epoch);
   }
+  asm volatile("" ::"v"(pf));   // the prefetch's value counts as used
 }
 
 struct Occ {
