@@ -50,8 +50,8 @@ KERNEL_SOURCES = {
 TRAFFIC = {
     # workload: {"sha256": ..., "bytes": fetched + written per launch}
     # c2: the moe_layer kernel (profiles/c2_decode_layer_hbm_traffic.md)
-    "c2_decode_layer_q2": {"sha256": "6730b2f0037e187e91142fd06e5a65a9c375b8783eb6f3127bf2f971c130edc3",
-                           "bytes": 23236681},
+    "c2_decode_layer_q2": {"sha256": "5eff0de9bb5b25e098f0c7a102e724b526f5894b1227b36e30f7f922aa7f563a",
+                           "bytes": 23111717},
     # c5: the kernels of one moe_expert_ffn call (active list, schedule, x16,
     # gate/up and down GEMMs; profiles/c5_prefill_hbm_traffic.md)
     "c5_prefill_q4": {"sha256": "7c6bdd3262b01a17d99ffe4afdcbba63256ab541f07cc2173512ad1b72967401",
