@@ -221,6 +221,8 @@ def bench_decode(args, cfg_name):
                      "kernel": "moe_layer (whole call)", "bytes_per_launch": int(bytes_call),
                      "launch_ms": round(ms_call, 5), "distinct_experts_per_layer": round(u, 2)},
     }
+    if args.host_tier and cfg.slots == "tiered":
+        out["host_tier"] = host_tier_leg(cfg, layers, ws, ms)
     if not args.no_cpu_baseline:
         n = args.cpu_tokens
         log(f"[bench] cpu baseline: oracle on {n} tokens")
@@ -230,6 +232,68 @@ def bench_decode(args, cfg_name):
                                "sample": f"{n} single-token decode layers of {cfg.name} "
                                          f"(router..combine, fp64, one thread, {el:.1f}s)"}
     return out
+
+
+def host_tier_leg(cfg, layers, ws, gpu_ms):
+    """The misses of one step of a tiered stack, computed by the host tier
+    (moe_host_miss_ffn) from host copies of the missed experts' weights.
+    One extra GPU step keeps every layer's miss list; the host then runs the
+    48 layers' lists in turn (each call multi-threaded), timed as a whole."""
+    import torch
+    import routed_expert_ffn_gemv_amd as moe
+    from synth import device as sdev
+    dev = torch.device("cuda", 0)
+    T, k, H = cfg.T, cfg.k, cfg.H
+    lists = []
+    for l, (desc, inp, _, _) in enumerate(layers):
+        y = torch.empty((T, H), dtype=torch.float32, device=dev)
+        idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        gate = torch.empty((T, k), dtype=torch.float32, device=dev)
+        slot_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        miss = torch.empty((T * k * 3,), dtype=torch.int32, device=dev)
+        miss_off = torch.empty((T + 1,), dtype=torch.int32, device=dev)
+        moe.moe_layer(desc, inp["x"], T, y, idx, gate, slot_idx, miss, miss_off, ws)
+        lists.append((miss, miss_off))
+    torch.cuda.synchronize()
+    work = []   # per layer: host store of the missed experts, remapped list, x
+    n_miss = n_uniq = 0
+    for l, ((miss, miss_off), (desc, inp, _, _)) in enumerate(zip(lists, layers)):
+        moff = miss_off.cpu().numpy().astype(np.int32)
+        m = miss.cpu().numpy()[: 3 * moff[-1]].reshape(-1, 3).copy()
+        experts = np.unique(m[:, 0])
+        n_miss += len(m)
+        n_uniq += len(experts)
+        if len(m) == 0:
+            continue
+        m[:, 0] = np.searchsorted(experts, m[:, 0])
+        pool = sdev.expert_pool(cfg, [l] * len(experts), experts.tolist(), dev)
+        store = {name: tuple(t.cpu().numpy() for t in pool[name]) for name in ("gate", "up", "down")}
+        del pool
+        work.append((len(experts), store, m.ravel().copy(), moff, inp["x"].cpu().numpy()))
+    torch.cuda.empty_cache()
+    threads = min(16, os.cpu_count() or 1)
+    ys = np.zeros((T, H), np.float32)
+
+    def one_step():
+        for n_e, store, m, moff, x in work:
+            moe.moe_host_miss_ffn(n_e, H, cfg.I, cfg.wfmt, store["gate"], store["up"],
+                                  store["down"], x, T, m, moff, ys, threads)
+    one_step()   # first touch of the host copies
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        one_step()
+        times.append(time.perf_counter() - t0)
+    ms = float(np.median(times)) * 1e3
+    import synth
+    gb = n_uniq * synth.expert_bytes(cfg) / 1e9
+    return {"ms_per_step": round(ms, 3), "misses_per_step": int(n_miss),
+            "distinct_missed_experts": int(n_uniq), "weight_gb_per_step": round(gb, 3),
+            "gbs": round(gb / (ms * 1e-3), 1), "threads": threads,
+            "isa": "avx512" if moe.moe_host_isa() else "generic",
+            "gpu_ms_per_step": round(gpu_ms, 4),
+            "note": "host tier (CPU) computing the step's misses from host-memory weights; "
+                    "the GPU figure is the same step's hits and shared expert"}
 
 
 def bench_adaptive(args):
@@ -517,6 +581,8 @@ def main():
     ap.add_argument("--layers", type=int, default=48)
     ap.add_argument("--cpu-tokens", type=int, default=12)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--host-tier", action="store_true",
+                    help="c4: also time the host tier on one step's misses")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="first run a plain device-to-device copy of MIB MiB (3 times): the "
                          "known-size kernel that scales the HBM byte counters of a profile")

@@ -229,6 +229,36 @@ moe_status moe_slot_refresh_workspace_size(const moe_slot_pool* pool, size_t* by
 moe_status moe_slot_refresh(const moe_slot_pool* pool, int32_t max_swaps, int32_t* swaps,
                             int32_t* n_swaps, void* ws, size_t ws_bytes, void* stream);
 
+/* Host tier: the listed misses computed on the CPU ([MD] "1 トークン、三者の
+ *分担": experts that are not on the card are computed by the CPU next to the
+ * RAM that holds them, and the results are summed with the card's).
+ * Unlike the calls above, every pointer here is a HOST pointer and the call
+ * is synchronous; it uses no GPU.
+ *  gate, up [n][I][H] and down [n][H][I]: the layer's experts indexed by
+ *    expert id (n >= E), one format (F32, Q2B32 or Q4B32; layouts as for
+ *    moe_mat, in host memory).
+ *  x: bf16 bits [T][H], the layer input.  miss, miss_off: a miss list as
+ *    moe_layer / moe_resolve_slots write it (host copies): token t's misses
+ *    are miss[miss_off[t] .. miss_off[t+1]), each with token t, an expert in
+ *    [0, E) named at most once per token, and its gate weight.
+ *  y [T][H] fp32, accumulated: y[t] += gate * D_e(silu(G_e x_t) * U_e x_t)
+ *    for every miss, in fp32.  With y holding moe_layer's output for a
+ *    partial slot table, y becomes the layer's output with every expert
+ *    resident (up to rounding).
+ * Each missed expert's weights are read once for all of its tokens.  The
+ * additions into each element of y happen in one fixed order (experts by
+ * ascending id), so the result does not depend on n_threads (<= 0: the
+ * hardware concurrency).  Invalid arguments or list: MOE_ERR_INVALID and y
+ * untouched.  The dot products use AVX-512 when the CPU has it; the
+ * environment variable MOE_HOST_ISA=generic, read at the first call,
+ * selects plain C++ instead. */
+moe_status moe_host_miss_ffn(int32_t E, int32_t H, int32_t I, moe_mat gate, moe_mat up,
+                             moe_mat down, const uint16_t* x, int32_t T, const moe_miss* miss,
+                             const int32_t* miss_off, float* y, int32_t n_threads);
+
+/* Which code moe_host_miss_ffn runs: 1 = AVX-512, 0 = plain C++. */
+int32_t moe_host_isa(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,8 @@ FORMATS = {"f32": MOE_W_F32, "bf16": MOE_W_BF16, "q2": MOE_W_Q2B32, "q4": MOE_W_
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_status_string", "moe_version", "moe_workspace_size", "moe_route",
            "moe_resolve_slots", "moe_expert_ffn", "moe_combine", "moe_layer",
-           "moe_slot_refresh_workspace_size", "moe_slot_refresh")
+           "moe_slot_refresh_workspace_size", "moe_slot_refresh", "moe_host_miss_ffn",
+           "moe_host_isa")
 MOE_REFRESH_MAX_SWAPS = 1024
 
 
@@ -93,6 +94,11 @@ def _load():
     lib.moe_slot_refresh_workspace_size.argtypes = [SP, ctypes.POINTER(SZ)]
     lib.moe_slot_refresh.restype = I32
     lib.moe_slot_refresh.argtypes = [SP, I32, P, P, P, SZ, P]
+    lib.moe_host_isa.restype = I32
+    lib.moe_host_isa.argtypes = []
+    lib.moe_host_miss_ffn.restype = I32
+    lib.moe_host_miss_ffn.argtypes = [I32, I32, I32, moe_mat, moe_mat, moe_mat, P, I32, P, P, P,
+                                      I32]
     return lib
 
 
@@ -241,6 +247,50 @@ def moe_slot_refresh(pool, max_swaps, swaps, n_swaps, stream=None):
     """swaps: int32 device tensor [>= max_swaps * 3]; n_swaps: int32 [1]."""
     _check(lib.moe_slot_refresh(pool.ref, int(max_swaps), _ptr(swaps), _ptr(n_swaps), None, 0,
                                 _stream(stream)), "moe_slot_refresh")
+
+
+def _hptr(a, dtype):
+    """Address of a C-contiguous host array (numpy, or a CPU torch tensor)."""
+    import numpy as np
+    if a is None:
+        return None
+    if isinstance(a, np.ndarray):
+        want = np.dtype(dtype)
+        same_bits = (a.dtype.kind in "iu" and want.kind in "iu" and a.dtype.itemsize == want.itemsize)
+        if not a.flags["C_CONTIGUOUS"] or not (a.dtype == want or same_bits):
+            raise ValueError(f"host array must be C-contiguous {want}")
+        return a.ctypes.data
+    if getattr(a, "is_cuda", False) or not a.is_contiguous():
+        raise ValueError("host tensor must be a contiguous CPU tensor")
+    return a.data_ptr()
+
+
+def moe_host_miss_ffn(E, H, I, wfmt, gate, up, down, x, T, miss, miss_off, y, n_threads=0):
+    """Host tier: y [T][H] float32 += each listed miss's expert output, on
+    the CPU.  gate/up/down: the layer's experts by id in host memory, f32
+    arrays [n][rows][cols] or (codes uint8, scale uint16, min uint16) tuples;
+    x: uint16 bf16 bits [T][H]; miss: int32 words of moe_miss records;
+    miss_off: int32 [T+1].  Host arrays only; synchronous."""
+    import numpy as np
+    fmt = FORMATS[wfmt] if isinstance(wfmt, str) else wfmt
+
+    def mat(p):
+        m = moe_mat()
+        m.fmt = fmt
+        if fmt == MOE_W_F32:
+            m.data = _hptr(p, np.float32)
+        else:
+            m.data, m.scale, m.min = _hptr(p[0], np.uint8), _hptr(p[1], np.uint16), _hptr(p[2], np.uint16)
+        return m
+    mats = [mat(gate), mat(up), mat(down)]
+    _check(lib.moe_host_miss_ffn(int(E), int(H), int(I), *mats, _hptr(x, np.uint16), int(T),
+                                 _hptr(miss, np.int32), _hptr(miss_off, np.int32),
+                                 _hptr(y, np.float32), int(n_threads)), "moe_host_miss_ffn")
+
+
+def moe_host_isa():
+    """1: the host tier runs AVX-512 code; 0: plain C++."""
+    return lib.moe_host_isa()
 
 
 def unpack_miss(miss_tensor, n):

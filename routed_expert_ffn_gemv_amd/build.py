@@ -19,6 +19,9 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-mcode-object-
          "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
 
 
+HOST_ONLY = {"host_tier.cpp"}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
                   if f.endswith(".hip") or f.endswith(".cpp"))
@@ -30,7 +33,10 @@ def build(verbose=False):
 
     def compile_one(src):
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
-        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        # .hip: device and host code; host_tier.cpp: plain C++ (the CPU
+        # tier, no device pass); other .cpp: host code that calls HIP
+        name = os.path.basename(src)
+        lang = ["-x", "hip"] if src.endswith(".hip") else (["-x", "c++"] if name in HOST_ONLY else [])
         cmd = [HIPCC] + FLAGS + lang + ["-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
