@@ -46,7 +46,7 @@ def lib():
         L.oracle_f16.argtypes = [ctypes.c_uint16]
         for name in ("oracle_dequant", "oracle_router", "oracle_topk", "oracle_resolve",
                      "oracle_bucket", "oracle_ffn", "oracle_combine", "oracle_layer",
-                     "oracle_count_usage", "oracle_slot_refresh"):
+                     "oracle_count_usage", "oracle_slot_refresh", "oracle_verify_accept"):
             getattr(L, name).restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -101,6 +101,19 @@ def topk(logits, k):
     gate = np.empty((T, k), np.float64)
     _check(lib().oracle_topk(T, E, k, _ptr(logits), _ptr(idx), _ptr(gate)), "topk")
     return idx, gate
+
+
+def verify_accept(logits, draft):
+    """Tokens kept by a verify pass: the model's greedy tokens g_0 .. g_a,
+    where the first a drafts equal g_0 .. g_{a-1} (oracle_verify_accept)."""
+    logits = _c(logits, np.float64)
+    T, V = logits.shape
+    draft = np.zeros(max(T - 1, 1), np.int32) if T == 1 else _c(draft, np.int32)
+    out = np.empty(T, np.int32)
+    n = np.zeros(1, np.int32)
+    _check(lib().oracle_verify_accept(T, V, _ptr(logits), _ptr(draft), _ptr(out), _ptr(n)),
+           "verify_accept")
+    return out[: int(n[0])].copy()
 
 
 def resolve(idx, gate, E, slot_of=None):

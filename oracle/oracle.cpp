@@ -382,4 +382,32 @@ int oracle_layer(int T, int E, int k, int H, int I, int S, const uint16_t* x, in
                         shg ? shared.data() : nullptr, y);
 }
 
+// Acceptance of a verify pass ([MD] "予測してから検証する": a draft layer
+// proposes up to 3 next tokens, one pass of the model checks them all, keeps
+// the ones the model agrees with and adds one token of its own, so the
+// output equals plain greedy decoding).  Row i of logits [T][V] is the
+// model's prediction after input i of the verify batch (input 0 = the last
+// accepted token, input i = draft token i); draft [T-1].  The model's greedy
+// token after input i is g_i = the index of the largest logit of row i, the
+// lowest index on equal values.  Draft i+1 is kept while it equals g_i; with
+// a drafts kept, the output is g_0 .. g_a (the kept drafts, then the model's
+// own token), n_out = a + 1.
+int oracle_verify_accept(int T, int V, const double* logits, const int32_t* draft, int32_t* out,
+                         int32_t* n_out) {
+  if (T < 1 || V < 1) return 1;
+  std::vector<int32_t> g(T);
+  for (int i = 0; i < T; ++i) {
+    const double* l = logits + int64_t(i) * V;
+    int best = 0;
+    for (int v = 1; v < V; ++v)
+      if (l[v] > l[best]) best = v;
+    g[i] = best;
+  }
+  int a = 0;
+  while (a < T - 1 && draft[a] == g[a]) ++a;
+  for (int i = 0; i <= a; ++i) out[i] = g[i];
+  *n_out = a + 1;
+  return 0;
+}
+
 }  // extern "C"

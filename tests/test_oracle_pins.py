@@ -483,3 +483,49 @@ def test_refresh_bounded_takes_the_best_first():
     np.testing.assert_array_equal(swaps[:, 1], outs)
     np.testing.assert_array_equal(swaps[:, 0], vics)
     np.testing.assert_array_equal(swaps[:, 2], vics)
+
+
+# ---- verify acceptance ([MD] "予測してから検証する")
+
+def test_verify_accept_hand_cases():
+    V = 5
+    rows = np.full((4, V), -1.0)
+    for i, g in enumerate([2, 0, 4, 1]):
+        rows[i, g] = 3.0
+    assert oracle.verify_accept(rows, [2, 0, 3]).tolist() == [2, 0, 4]     # third draft rejected
+    assert oracle.verify_accept(rows, [2, 0, 4]).tolist() == [2, 0, 4, 1]  # all kept + own token
+    assert oracle.verify_accept(rows, [1, 0, 4]).tolist() == [2]           # first draft rejected
+    assert oracle.verify_accept(rows, [2, 1, 4]).tolist() == [2, 0]        # a later match is not kept
+    assert oracle.verify_accept(rows[:1], []).tolist() == [2]              # no drafts: one token
+
+
+def test_verify_accept_ties_take_the_lowest_index():
+    rows = np.array([[0.0, 7.0, 1.0, 7.0, 7.0],
+                     [-0.0, 0.0, -1.0, -2.0, -3.0],
+                     [0.0, -0.0, 0.0, -5.0, -5.0]])
+    out = oracle.verify_accept(rows, [1, 0])
+    assert out.tolist() == [1, 0, 0]
+
+
+def test_verify_accept_equals_greedy_decoding():
+    """A bigram 'model' (next-token logits depend on the last token) decoded
+    greedily, and the same model run as drafts + verify passes with a drafter
+    that is right about two times in three: the two token streams are equal."""
+    rng = np.random.default_rng(7)
+    V, steps = 11, 60
+    table = rng.standard_normal((V, V))
+    table[:, 3] = table[:, 5] = table.max(axis=1)   # exact ties everywhere
+    greedy = [4]
+    while len(greedy) < steps + 1:
+        greedy.append(int(np.argmax(table[greedy[-1]])))
+    spec = [4]
+    while len(spec) < steps + 1:
+        D = int(rng.integers(0, 4))
+        drafts, last = [], spec[-1]
+        for _ in range(D):   # the drafter: the model's token, or a wrong one
+            nxt = int(np.argmax(table[last])) if rng.random() < 0.67 else int(rng.integers(0, V))
+            drafts.append(nxt)
+            last = nxt
+        inputs = [spec[-1]] + drafts
+        spec += oracle.verify_accept(table[inputs], drafts).tolist()
+    assert spec[: steps + 1] == greedy
