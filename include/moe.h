@@ -229,6 +229,24 @@ moe_status moe_slot_refresh_workspace_size(const moe_slot_pool* pool, size_t* by
 moe_status moe_slot_refresh(const moe_slot_pool* pool, int32_t max_swaps, int32_t* swaps,
                             int32_t* n_swaps, void* ws, size_t ws_bytes, void* stream);
 
+/* Acceptance of a verify pass ([MD] "予測してから検証する": a draft layer
+ * proposes up to 3 next tokens, one pass of the model checks them all, keeps
+ * the drafts the model agrees with and adds one token of its own, so the
+ * output equals greedy decoding token for token).
+ *  logits [T][V] fp32: row i is the model's prediction after input i of the
+ *    verify batch (input 0 = the last accepted token, input i = draft i).
+ *  draft [T-1] int32: the draft tokens (may be NULL when T = 1).
+ * With g_i = the index of the largest logit of row i (the lowest index on
+ * equal logits; -0.0 equals +0.0), drafts are kept while draft[i] == g_i;
+ * with a kept, out_tokens[0 .. a] = g_0 .. g_a (the kept drafts, then the
+ * model's own token) and *n_out = a + 1 (device int32).  out_tokens [T]:
+ * entries past a receive g_i too.  Limits: 1 <= T <= 64, 1 <= V <= 2^26.
+ * ws: moe_verify_workspace_size bytes, 256-byte aligned.  Async on stream. */
+moe_status moe_verify_workspace_size(int32_t T, int32_t V, size_t* bytes);
+moe_status moe_verify_accept(const float* logits, int32_t T, int32_t V, const int32_t* draft,
+                             int32_t* out_tokens, int32_t* n_out, void* ws, size_t ws_bytes,
+                             void* stream);
+
 /* Host tier: the listed misses computed on the CPU ([MD] "1 トークン、三者の
  *分担": experts that are not on the card are computed by the CPU next to the
  * RAM that holds them, and the results are summed with the card's).

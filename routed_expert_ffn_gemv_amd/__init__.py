@@ -25,7 +25,7 @@ FORMATS = {"f32": MOE_W_F32, "bf16": MOE_W_BF16, "q2": MOE_W_Q2B32, "q4": MOE_W_
 EXPORTS = ("moe_status_string", "moe_version", "moe_workspace_size", "moe_route",
            "moe_resolve_slots", "moe_expert_ffn", "moe_combine", "moe_layer",
            "moe_slot_refresh_workspace_size", "moe_slot_refresh", "moe_host_miss_ffn",
-           "moe_host_isa")
+           "moe_host_isa", "moe_verify_workspace_size", "moe_verify_accept")
 MOE_REFRESH_MAX_SWAPS = 1024
 
 
@@ -94,6 +94,10 @@ def _load():
     lib.moe_slot_refresh_workspace_size.argtypes = [SP, ctypes.POINTER(SZ)]
     lib.moe_slot_refresh.restype = I32
     lib.moe_slot_refresh.argtypes = [SP, I32, P, P, P, SZ, P]
+    lib.moe_verify_workspace_size.restype = I32
+    lib.moe_verify_workspace_size.argtypes = [I32, I32, ctypes.POINTER(SZ)]
+    lib.moe_verify_accept.restype = I32
+    lib.moe_verify_accept.argtypes = [P, I32, I32, P, P, P, P, SZ, P]
     lib.moe_host_isa.restype = I32
     lib.moe_host_isa.argtypes = []
     lib.moe_host_miss_ffn.restype = I32
@@ -247,6 +251,22 @@ def moe_slot_refresh(pool, max_swaps, swaps, n_swaps, stream=None):
     """swaps: int32 device tensor [>= max_swaps * 3]; n_swaps: int32 [1]."""
     _check(lib.moe_slot_refresh(pool.ref, int(max_swaps), _ptr(swaps), _ptr(n_swaps), None, 0,
                                 _stream(stream)), "moe_slot_refresh")
+
+
+def moe_verify_workspace_size(T, V):
+    n = ctypes.c_size_t(0)
+    _check(lib.moe_verify_workspace_size(int(T), int(V), ctypes.byref(n)),
+           "moe_verify_workspace_size")
+    return n.value
+
+
+def moe_verify_accept(logits, T, V, draft, out_tokens, n_out, ws, stream=None):
+    """logits: fp32 device [T][V]; draft: int32 [T-1] (None when T = 1);
+    out_tokens: int32 [T]; n_out: int32 [1]; ws: uint8 device tensor of at
+    least moe_verify_workspace_size(T, V) bytes."""
+    _check(lib.moe_verify_accept(_ptr(logits), int(T), int(V), _ptr(draft), _ptr(out_tokens),
+                                 _ptr(n_out), _ptr(ws), ws.numel() if ws is not None else 0,
+                                 _stream(stream)), "moe_verify_accept")
 
 
 def _hptr(a, dtype):

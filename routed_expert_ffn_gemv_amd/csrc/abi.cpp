@@ -17,6 +17,8 @@ constexpr int kMaxK = 32;
 constexpr int kMaxH = 8192;
 constexpr int kMaxI = 4096;
 constexpr int kMaxSlots = 16384;
+constexpr int kMaxVerifyT = 64;        // rows of one verify pass
+constexpr int kMaxVocab = 1 << 26;
 constexpr int64_t kMaxT = int64_t(1) << 22;
 constexpr size_t kAlign = 256;
 constexpr int kRouterGemmMinT = 256;       // tokens from which the router runs on MFMA
@@ -426,6 +428,26 @@ moe_status moe_slot_refresh(const moe_slot_pool* pool, int32_t max_swaps, int32_
     r.mat_blocks = f32 ? 0 : v.mat_blocks;
   }
   return device_status(launch_slot_refresh(a, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_verify_workspace_size(int32_t T, int32_t V, size_t* bytes) {
+  if (!bytes || T < 1 || V < 1) return MOE_ERR_INVALID;
+  if (T > kMaxVerifyT || V > kMaxVocab) return MOE_ERR_UNSUPPORTED;
+  *bytes = up(size_t(T) * verify_parts(T, V) * 8);
+  return MOE_OK;
+}
+
+moe_status moe_verify_accept(const float* logits, int32_t T, int32_t V, const int32_t* draft,
+                             int32_t* out_tokens, int32_t* n_out, void* ws, size_t ws_bytes,
+                             void* stream) {
+  size_t need = 0;
+  const moe_status s = moe_verify_workspace_size(T, V, &need);
+  if (s != MOE_OK) return s;
+  if (!logits || !out_tokens || !n_out || (T > 1 && !draft)) return MOE_ERR_INVALID;
+  if (!ws || !aligned(ws, kAlign)) return MOE_ERR_INVALID;
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  return device_status(launch_verify_accept(logits, T, V, T > 1 ? draft : out_tokens, out_tokens,
+                                            n_out, ws, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -5,6 +5,11 @@
 
 namespace moe {
 
+// verify-pass acceptance: partial argmax blocks per row, then one block
+int verify_parts(int T, int V);
+hipError_t launch_verify_accept(const float* logits, int T, int V, const int32_t* draft,
+                                int32_t* out, int32_t* n_out, void* ws, hipStream_t st);
+
 // router
 constexpr int kRouterNT = 8;              // tokens per router block
 constexpr int kRouterLdsBytes = 64 * 1024;

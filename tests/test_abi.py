@@ -156,3 +156,25 @@ def test_slot_refresh_validates_before_launch():
     p = _pool()
     p.store_down.fmt = moe.MOE_W_Q4B32                      # store and pool differ
     assert L.moe_slot_refresh(ctypes.byref(p), 96, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_INVALID
+
+
+def test_verify_accept_validation():
+    """Shapes and pointers are checked on the host before any launch."""
+    import ctypes
+    import routed_expert_ffn_gemv_amd as moe
+    n = ctypes.c_size_t(0)
+    assert moe.lib.moe_verify_workspace_size(0, 10, ctypes.byref(n)) == moe.MOE_ERR_INVALID
+    assert moe.lib.moe_verify_workspace_size(4, 0, ctypes.byref(n)) == moe.MOE_ERR_INVALID
+    assert moe.lib.moe_verify_workspace_size(65, 10, ctypes.byref(n)) == moe.MOE_ERR_UNSUPPORTED
+    assert moe.lib.moe_verify_workspace_size(4, 151936, None) == moe.MOE_ERR_INVALID
+    assert moe.lib.moe_verify_workspace_size(4, 151936, ctypes.byref(n)) == moe.MOE_OK
+    assert n.value > 0 and n.value % 256 == 0
+    fake = 1 << 20   # never dereferenced: every call below fails validation
+    assert moe.lib.moe_verify_accept(None, 4, 100, fake, fake, fake, fake, 1 << 20,
+                                     None) == moe.MOE_ERR_INVALID
+    assert moe.lib.moe_verify_accept(fake, 4, 100, None, fake, fake, fake, 1 << 20,
+                                     None) == moe.MOE_ERR_INVALID
+    assert moe.lib.moe_verify_accept(fake, 4, 100, fake, fake, fake, fake + 8, 1 << 20,
+                                     None) == moe.MOE_ERR_INVALID
+    assert moe.lib.moe_verify_accept(fake, 4, 100, fake, fake, fake, fake, 8,
+                                     None) == moe.MOE_ERR_WORKSPACE
