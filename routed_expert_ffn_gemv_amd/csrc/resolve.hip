@@ -105,28 +105,35 @@ hipError_t launch_resolve_small(int T, int k, int E, int S, const int32_t* idx,
 // Pairs are cut into chunks of kResolveChunk consecutive pairs.
 //  1. count:   per chunk, slot of each pair, per-slot counts (slot-major
 //              table cnt[s][chunk]) and the chunk's miss count;
-//  2. scan:    one block scans cnt in slot-major order (giving each chunk's
-//              first position inside each bucket), the chunk miss counts,
-//              bucket_off and the active list;
+//  2. scan:    (a) per slot, the exclusive prefix of its counts over the
+//              chunks (each chunk's first position inside the bucket,
+//              relative to the bucket's start) and the slot's total, slots
+//              and chunk ranges spread over blocks and waves; (b) one block
+//              scans the chunk miss counts and the slot totals (bucket
+//              starts, bucket_off, the active list);
 //  3. scatter: per chunk, a pair's rank among the chunk's earlier pairs of
 //              the same slot (or among its earlier misses) places it.
 
 struct LargeWs {
   int32_t* cnt;        // [nchunk][S]: chunk-major, so a pass over slots is coalesced
   int32_t* cmiss;      // [nchunk + 1]
+  int32_t* stot;       // [S] pairs per slot
+  int32_t* sbase;      // [S] first position of the slot's bucket
 };
 
 static inline LargeWs large_ws_layout(void* ws, int nchunk, int S) {
   LargeWs w;
   w.cnt = static_cast<int32_t*>(ws);
   w.cmiss = w.cnt + size_t(S) * nchunk;
+  w.stot = w.cmiss + nchunk + 1;
+  w.sbase = w.stot + S;
   return w;
 }
 
 size_t resolve_large_ws(int T, int k, int S) {
   const int64_t P = int64_t(T) * k;
   const int64_t nchunk = (P + kResolveChunk - 1) / kResolveChunk;
-  return size_t((int64_t(S) * nchunk + nchunk + 1) * 4);
+  return size_t((int64_t(S) * nchunk + nchunk + 1 + 2 * int64_t(S)) * 4);
 }
 
 __global__ __launch_bounds__(256) void resolve_count_kernel(int P, int E, int S, int nchunk,
@@ -155,13 +162,43 @@ __global__ __launch_bounds__(256) void resolve_count_kernel(int P, int E, int S,
   if (threadIdx.x == 0) w.cmiss[c] = nm;
 }
 
-// One block of 1024 threads: exclusive scans in place.
+// 2a. 64 slots per block (a lane each), the chunks split among the 16
+// waves: each wave sums its range, the ranges before it give its start, and
+// a second pass writes the exclusive prefixes in place.
+constexpr int kColWaves = 16;
+__global__ __launch_bounds__(64 * kColWaves) void resolve_colscan_kernel(int S, int nchunk,
+                                                                         LargeWs w) {
+  __shared__ int part[kColWaves][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int s = blockIdx.x * 64 + lane;
+  const int per = (nchunk + kColWaves - 1) / kColWaves;
+  const int c0 = min(nchunk, wv * per), c1 = min(nchunk, c0 + per);
+  int sum = 0;
+  if (s < S) {
+#pragma unroll 8
+    for (int c = c0; c < c1; ++c) sum += w.cnt[int64_t(c) * S + s];
+  }
+  part[wv][lane] = sum;
+  __syncthreads();
+  int r = 0;
+  for (int q = 0; q < wv; ++q) r += part[q][lane];
+  if (s < S) {
+#pragma unroll 8
+    for (int c = c0; c < c1; ++c) {
+      const int v = w.cnt[int64_t(c) * S + s];
+      w.cnt[int64_t(c) * S + s] = r;
+      r += v;
+    }
+    if (wv == kColWaves - 1) w.stot[s] = r;
+  }
+}
+
+// 2b. One block of 1024 threads: chunk miss counts and slot totals.
 __global__ __launch_bounds__(1024) void resolve_scan_kernel(int T, int S, int nchunk, LargeWs w,
                                                             int32_t* __restrict__ bucket_off,
                                                             int32_t* __restrict__ miss_off,
                                                             ActiveList act) {
   __shared__ int tmp[32];
-  // chunk miss counts
   int run = 0;
   for (int base = 0; base < nchunk; base += blockDim.x) {
     const int i = base + threadIdx.x;
@@ -175,27 +212,15 @@ __global__ __launch_bounds__(1024) void resolve_scan_kernel(int T, int S, int nc
     w.cmiss[nchunk] = run;
     if (miss_off) miss_off[T] = run;
   }
-  // per-slot, per-chunk counts in slot-major order; one thread per slot
-  // sums its row, a block scan over slots gives bucket_off.
   int hits_before = 0, act_before = 0;
   for (int base = 0; base < S; base += blockDim.x) {
     const int s = base + threadIdx.x;
-    int tot_s = 0;
-    if (s < S) {
-#pragma unroll 16
-      for (int c = 0; c < nchunk; ++c) tot_s += w.cnt[int64_t(c) * S + s];
-    }
+    const int tot_s = s < S ? w.stot[s] : 0;
     int tot_all;
     const int off = hits_before + block_exclusive_scan(tot_s, tmp, &tot_all);
     if (s < S) {
+      w.sbase[s] = off;
       if (bucket_off) bucket_off[s] = off;
-      int r = off;
-#pragma unroll 16
-      for (int c = 0; c < nchunk; ++c) {
-        const int v = w.cnt[int64_t(c) * S + s];
-        w.cnt[int64_t(c) * S + s] = r;
-        r += v;
-      }
     }
     const int nonempty = (s < S && tot_s > 0) ? 1 : 0;
     int n_ne;
@@ -237,7 +262,7 @@ __global__ __launch_bounds__(256) void resolve_scatter_kernel(
     }
     const int p = p0 + i;
     if (s >= 0) {
-      if (bucket_pair) bucket_pair[w.cnt[int64_t(c) * S + s] + r] = p;
+      if (bucket_pair) bucket_pair[w.sbase[s] + w.cnt[int64_t(c) * S + s] + r] = p;
     } else if (miss) {
       moe_miss m;
       m.expert = idx[p];
@@ -258,6 +283,8 @@ hipError_t launch_resolve_large(int T, int k, int E, int S, const int32_t* idx,
   LargeWs w = large_ws_layout(ws, nchunk, S);
   hipLaunchKernelGGL(resolve_count_kernel, dim3(nchunk), dim3(256), size_t(S) * 4, st, P, E, S,
                      nchunk, idx, slot_of, slot_idx, w);
+  hipLaunchKernelGGL(resolve_colscan_kernel, dim3((S + 63) / 64), dim3(64 * kColWaves), 0, st, S,
+                     nchunk, w);
   hipLaunchKernelGGL(resolve_scan_kernel, dim3(1), dim3(1024), 0, st, T, S, nchunk, w,
                      bucket_off, miss_off, act);
   hipLaunchKernelGGL(resolve_scatter_kernel, dim3(nchunk), dim3(256), 0, st, P, k, S, nchunk, idx,
