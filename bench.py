@@ -548,6 +548,31 @@ def bench_prefill(args, cfg_name):
                      "kernel": "moe_expert_ffn (grouped gate/up + down GEMMs)",
                      "flops_per_launch": int(flops)},
     }
+    if args.prefill_chunks:
+        out["prefill_layer"] = []
+        aux = torch.cuda.Stream()
+        for c in [int(v) for v in args.prefill_chunks.split(",")]:
+            for use_aux in (False, True):
+                wsp = torch.zeros(moe.moe_prefill_workspace_size(desc, T, c), dtype=torch.uint8,
+                                  device=dev)
+
+                def run():
+                    moe.moe_prefill_layer(desc, x, T, c, y, idx, gate, slot_idx, wsp, stream,
+                                          aux if use_aux else None)
+                for _ in range(2):
+                    run()
+                torch.cuda.synchronize()
+                e0.record(stream)
+                n = max(3, args.steps // 2)
+                for _ in range(n):
+                    run()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                out["prefill_layer"].append({"chunk": c, "aux_stream": use_aux,
+                                             "ms": round(e0.elapsed_time(e1) / n, 4)})
+                del wsp
+                torch.cuda.empty_cache()
+        log(f"[bench] prefill layer: {out['prefill_layer']}")
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline: oracle on a sample")
         tps, el = cpu_baseline_prefill(cfg, 512, 4)
@@ -581,6 +606,9 @@ def main():
     ap.add_argument("--layers", type=int, default=48)
     ap.add_argument("--cpu-tokens", type=int, default=12)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-chunks", default="", metavar="C1,C2,...",
+                    help="c5: also time moe_prefill_layer at these chunk sizes, with and "
+                         "without a second stream")
     ap.add_argument("--host-tier", action="store_true",
                     help="c4: also time the host tier on one step's misses")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",

@@ -229,6 +229,32 @@ moe_status moe_slot_refresh_workspace_size(const moe_slot_pool* pool, size_t* by
 moe_status moe_slot_refresh(const moe_slot_pool* pool, int32_t max_swaps, int32_t* swaps,
                             int32_t* n_swaps, void* ws, size_t ws_bytes, void* stream);
 
+/* Prefill layer in chunks ([MD] "長いプロンプトを読む": a long prompt is read
+ * in chunks, up to 8,192 tokens by default and more when configured, and the
+ * transfers of one step overlap the computation of another, each expert
+ * serving a whole chunk).  Here the overlap is within the layer: the routing
+ * of the next chunk runs beside the expert work of the current one.  The
+ * prompt's T tokens
+ * are cut into chunks of `chunk` tokens (the last one shorter; chunk >= T:
+ * one chunk).  For each chunk: moe_route + moe_resolve_slots on aux_stream,
+ * then moe_expert_ffn + moe_combine on stream, so chunk c + 1 is routed
+ * while chunk c's experts run.  aux_stream NULL: everything on stream.  The
+ * call orders itself after work already queued on stream, and on return
+ * every launch is ordered before later work on stream.  Outputs: y [T][H]
+ * fp32 (misses, if the slot table has any, contribute nothing, as in
+ * moe_combine); topk_idx, topk_gate and slot_idx [T][k] of every token.  No
+ * miss list (moe_resolve_slots gives one).  ws: moe_prefill_workspace_size
+ * bytes (one full workspace plus the chunk's buckets, pair and shared
+ * outputs, twice when there are several chunks), 256-byte aligned.  Events
+ * are made once per device and host thread; calls on one device from
+ * several host threads at once are not supported. */
+moe_status moe_prefill_workspace_size(const moe_layer_desc* desc, int32_t T, int32_t chunk,
+                                      size_t* bytes);
+moe_status moe_prefill_layer(const moe_layer_desc* desc, const uint16_t* x, int32_t T,
+                             int32_t chunk, float* y, int32_t* topk_idx, float* topk_gate,
+                             int32_t* slot_idx, void* ws, size_t ws_bytes, void* stream,
+                             void* aux_stream);
+
 /* Acceptance of a verify pass ([MD] "予測してから検証する": a draft layer
  * proposes up to 3 next tokens, one pass of the model checks them all, keeps
  * the drafts the model agrees with and adds one token of its own, so the

@@ -25,7 +25,8 @@ FORMATS = {"f32": MOE_W_F32, "bf16": MOE_W_BF16, "q2": MOE_W_Q2B32, "q4": MOE_W_
 EXPORTS = ("moe_status_string", "moe_version", "moe_workspace_size", "moe_route",
            "moe_resolve_slots", "moe_expert_ffn", "moe_combine", "moe_layer",
            "moe_slot_refresh_workspace_size", "moe_slot_refresh", "moe_host_miss_ffn",
-           "moe_host_isa", "moe_verify_workspace_size", "moe_verify_accept")
+           "moe_host_isa", "moe_verify_workspace_size", "moe_verify_accept",
+           "moe_prefill_workspace_size", "moe_prefill_layer")
 MOE_REFRESH_MAX_SWAPS = 1024
 
 
@@ -94,6 +95,10 @@ def _load():
     lib.moe_slot_refresh_workspace_size.argtypes = [SP, ctypes.POINTER(SZ)]
     lib.moe_slot_refresh.restype = I32
     lib.moe_slot_refresh.argtypes = [SP, I32, P, P, P, SZ, P]
+    lib.moe_prefill_workspace_size.restype = I32
+    lib.moe_prefill_workspace_size.argtypes = [D, I32, I32, ctypes.POINTER(SZ)]
+    lib.moe_prefill_layer.restype = I32
+    lib.moe_prefill_layer.argtypes = [D, P, I32, I32, P, P, P, P, P, SZ, P, P]
     lib.moe_verify_workspace_size.restype = I32
     lib.moe_verify_workspace_size.argtypes = [I32, I32, ctypes.POINTER(SZ)]
     lib.moe_verify_accept.restype = I32
@@ -251,6 +256,24 @@ def moe_slot_refresh(pool, max_swaps, swaps, n_swaps, stream=None):
     """swaps: int32 device tensor [>= max_swaps * 3]; n_swaps: int32 [1]."""
     _check(lib.moe_slot_refresh(pool.ref, int(max_swaps), _ptr(swaps), _ptr(n_swaps), None, 0,
                                 _stream(stream)), "moe_slot_refresh")
+
+
+def moe_prefill_workspace_size(desc, T, chunk):
+    n = ctypes.c_size_t(0)
+    _check(lib.moe_prefill_workspace_size(desc.ref, int(T), int(chunk), ctypes.byref(n)),
+           "moe_prefill_workspace_size")
+    return n.value
+
+
+def moe_prefill_layer(desc, x, T, chunk, y, topk_idx, topk_gate, slot_idx, ws, stream=None,
+                      aux_stream=None):
+    """aux_stream: a second torch.cuda.Stream (or None: everything on stream)."""
+    aux = None if aux_stream is None else (aux_stream if isinstance(aux_stream, int)
+                                           else aux_stream.cuda_stream)
+    _check(lib.moe_prefill_layer(desc.ref, _ptr(x), int(T), int(chunk), _ptr(y), _ptr(topk_idx),
+                                 _ptr(topk_gate), _ptr(slot_idx), _ptr(ws),
+                                 ws.numel() if ws is not None else 0, _stream(stream), aux),
+           "moe_prefill_layer")
 
 
 def moe_verify_workspace_size(T, V):

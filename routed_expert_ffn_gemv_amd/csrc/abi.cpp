@@ -207,6 +207,76 @@ moe_status run_resolve(const moe_layer_desc* d, const int32_t* idx, const float*
   return device_status(e);
 }
 
+// The expert FFN of one bucketed batch (the body of moe_expert_ffn).
+moe_status run_ffn(const moe_layer_desc* d, const uint16_t* x, int T, const int32_t* bucket_off,
+                   const int32_t* bucket_pair, float* pair_out, float* shared_out, void* ws,
+                   const WsLayout& w, hipStream_t st) {
+  FfnArgs a = ffn_args(d, x, T);
+  a.act = active_at(ws, w);
+  a.active_cap = w.cap;
+  a.bucket_pair = bucket_pair;
+  a.h = at<float>(ws, w.h);
+  a.h_sh = a.h + size_t(T) * d->k * d->I;
+  a.pair_out = pair_out;
+  a.shared_out = shared_out;
+  hipError_t e = launch_active_from_offsets(d->num_slots, bucket_off, a.act, st);
+  if (e == hipSuccess) {
+    if (int64_t(T) * d->k >= kFfnGemmMinPairs && ffn_gemm_ok(a.fmt, d->H, d->I) &&
+        planes_16b_aligned(d))
+      e = launch_ffn_gemm(a, d->num_slots, bucket_off, at<void>(ws, w.h), st);
+    else
+      e = launch_ffn_gemv(a, st);
+  }
+  return device_status(e);
+}
+
+// Workspace of the chunked prefill: one or two halves, each a full
+// workspace for `chunk` tokens followed by the chunk's buckets, pair outputs
+// and shared-expert outputs.
+struct PrefillHalf {
+  WsLayout w;
+  size_t boff, bpair, pair_out, shared_out, total;
+};
+
+PrefillHalf prefill_half(const moe_layer_desc* d, int chunk) {
+  PrefillHalf h;
+  h.w = layout(d, chunk);
+  size_t o = h.w.total;
+  h.boff = o;
+  o += up(size_t(d->num_slots + 1) * 4);
+  h.bpair = o;
+  o += up(size_t(chunk) * d->k * 4);
+  h.pair_out = o;
+  o += up(size_t(chunk) * d->k * d->H * 4);
+  h.shared_out = o;
+  o += up(size_t(chunk) * d->H * 4);
+  h.total = o;
+  return h;
+}
+
+// Events of the prefill pipeline, made once per device and host thread.
+struct PrefillEvents {
+  hipEvent_t fork = nullptr, routed[2] = {nullptr, nullptr}, done[2] = {nullptr, nullptr};
+  bool ok = false;
+};
+
+PrefillEvents* prefill_events() {
+  static thread_local PrefillEvents ev[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  PrefillEvents& e = ev[dev];
+  if (!e.ok) {
+    if (hipEventCreateWithFlags(&e.fork, hipEventDisableTiming) != hipSuccess) return nullptr;
+    for (int i = 0; i < 2; ++i) {
+      if (hipEventCreateWithFlags(&e.routed[i], hipEventDisableTiming) != hipSuccess ||
+          hipEventCreateWithFlags(&e.done[i], hipEventDisableTiming) != hipSuccess)
+        return nullptr;
+    }
+    e.ok = true;
+  }
+  return &e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -275,25 +345,8 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const uint16_t* x, int32_t
     return MOE_ERR_INVALID;
   if (!aligned(pair_out, 16) || (shared_out && !aligned(shared_out, 16))) return MOE_ERR_INVALID;
   if ((s = check_ws(desc, T, ws, ws_bytes)) != MOE_OK) return s;
-  const WsLayout w = layout(desc, T);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  FfnArgs a = ffn_args(desc, x, T);
-  a.act = active_at(ws, w);
-  a.active_cap = w.cap;
-  a.bucket_pair = bucket_pair;
-  a.h = at<float>(ws, w.h);
-  a.h_sh = a.h + size_t(T) * desc->k * desc->I;
-  a.pair_out = pair_out;
-  a.shared_out = shared_out;
-  hipError_t e = launch_active_from_offsets(desc->num_slots, bucket_off, a.act, st);
-  if (e == hipSuccess) {
-    if (int64_t(T) * desc->k >= kFfnGemmMinPairs && ffn_gemm_ok(a.fmt, desc->H, desc->I) &&
-        planes_16b_aligned(desc))
-      e = launch_ffn_gemm(a, desc->num_slots, bucket_off, at<void>(ws, w.h), st);
-    else
-      e = launch_ffn_gemv(a, st);
-  }
-  return device_status(e);
+  return run_ffn(desc, x, T, bucket_off, bucket_pair, pair_out, shared_out, ws, layout(desc, T),
+                 static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_combine(const moe_layer_desc* desc, int32_t T, const int32_t* slot_idx,
@@ -428,6 +481,72 @@ moe_status moe_slot_refresh(const moe_slot_pool* pool, int32_t max_swaps, int32_
     r.mat_blocks = f32 ? 0 : v.mat_blocks;
   }
   return device_status(launch_slot_refresh(a, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_prefill_workspace_size(const moe_layer_desc* desc, int32_t T, int32_t chunk,
+                                      size_t* bytes) {
+  const moe_status s = check_desc(desc);
+  if (s != MOE_OK) return s;
+  if (!bytes || T < 0 || chunk < 1) return MOE_ERR_INVALID;
+  if (T > kMaxT) return MOE_ERR_UNSUPPORTED;
+  const int c = T < chunk ? (T > 0 ? T : 1) : chunk;
+  *bytes = prefill_half(desc, c).total * (T > c ? 2 : 1);
+  return MOE_OK;
+}
+
+moe_status moe_prefill_layer(const moe_layer_desc* desc, const uint16_t* x, int32_t T,
+                             int32_t chunk, float* y, int32_t* topk_idx, float* topk_gate,
+                             int32_t* slot_idx, void* ws, size_t ws_bytes, void* stream,
+                             void* aux_stream) {
+  size_t need = 0;
+  moe_status s = moe_prefill_workspace_size(desc, T, chunk, &need);
+  if (s != MOE_OK) return s;
+  if (T == 0) return MOE_OK;
+  if (!x || !aligned(x, 16) || !y || !aligned(y, 16) || !topk_idx || !topk_gate || !slot_idx)
+    return MOE_ERR_INVALID;
+  if (!ws || !aligned(ws, kAlign)) return MOE_ERR_INVALID;
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  const int C = T < chunk ? T : chunk;
+  const int n_chunks = (T + C - 1) / C;
+  const PrefillHalf ph = prefill_half(desc, C);
+  hipStream_t main = static_cast<hipStream_t>(stream);
+  hipStream_t aux = aux_stream ? static_cast<hipStream_t>(aux_stream) : main;
+  PrefillEvents* ev = n_chunks > 1 || aux != main ? prefill_events() : nullptr;
+  if ((n_chunks > 1 || aux != main) && !ev) return MOE_ERR_DEVICE;
+  // the aux stream starts after the work already queued on the main stream
+  if (aux != main && (hipEventRecord(ev->fork, main) != hipSuccess ||
+                      hipStreamWaitEvent(aux, ev->fork, 0) != hipSuccess))
+    return MOE_ERR_DEVICE;
+  const int k = desc->k, H = desc->H;
+  for (int c = 0; c < n_chunks; ++c) {
+    const int t0 = c * C, Tc = T - t0 < C ? T - t0 : C, h = c & 1;
+    void* half = static_cast<char*>(ws) + size_t(h) * ph.total;
+    int32_t* boff = at<int32_t>(half, ph.boff);
+    int32_t* bpair = at<int32_t>(half, ph.bpair);
+    float* pair_out = at<float>(half, ph.pair_out);
+    float* sh_out = has_shared(desc) ? at<float>(half, ph.shared_out) : nullptr;
+    const uint16_t* xc = x + size_t(t0) * H;
+    int32_t* idx = topk_idx + size_t(t0) * k;
+    float* gate = topk_gate + size_t(t0) * k;
+    int32_t* sl = slot_idx + size_t(t0) * k;
+    // routing of chunk c (after chunk c - 2, the last user of this half, is done)
+    if (c >= 2 && hipStreamWaitEvent(aux, ev->done[h], 0) != hipSuccess) return MOE_ERR_DEVICE;
+    if ((s = run_route(desc, xc, Tc, idx, gate, half, ph.w, aux)) != MOE_OK) return s;
+    if ((s = run_resolve(desc, idx, gate, Tc, sl, boff, bpair, nullptr, nullptr, half, ph.w,
+                         aux)) != MOE_OK)
+      return s;
+    if (ev && (hipEventRecord(ev->routed[h], aux) != hipSuccess ||
+               hipStreamWaitEvent(main, ev->routed[h], 0) != hipSuccess))
+      return MOE_ERR_DEVICE;
+    // experts and combine of chunk c, while chunk c + 1 is routed
+    if ((s = run_ffn(desc, xc, Tc, boff, bpair, pair_out, sh_out, half, ph.w, main)) != MOE_OK)
+      return s;
+    if ((s = device_status(launch_combine(Tc, k, H, sl, gate, pair_out, sh_out,
+                                          y + size_t(t0) * H, main))) != MOE_OK)
+      return s;
+    if (ev && hipEventRecord(ev->done[h], main) != hipSuccess) return MOE_ERR_DEVICE;
+  }
+  return MOE_OK;
 }
 
 moe_status moe_verify_workspace_size(int32_t T, int32_t V, size_t* bytes) {

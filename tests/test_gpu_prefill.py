@@ -87,3 +87,50 @@ def test_c5_prefill_full_size():
     err = rowwise_rel_err(host(o["y"])[tokens], ref["y"][tokens])
     say(f"  sampled {len(tokens)} tokens: rel err {err:.2e}")
     assert err <= TOL
+
+
+CHUNKED = {
+    # name: (config, chunk, aux stream)
+    "q4_T600_chunk256_aux": (MID["q4_T600"], 256, True),
+    "q2_T517_chunk100_aux": (MID["q2_T517"], 100, True),
+    "q4_T700_noshared_chunk700": (MID["q4_T700_noshared"], 700, False),
+    "q4_T600_chunk7_main": (MID["q4_T600"], 7, False),
+}
+
+
+@pytest.mark.parametrize("name", list(CHUNKED))
+def test_prefill_layer_chunked(name):
+    """moe_prefill_layer (routing of chunk c + 1 on a second stream while
+    chunk c's experts run) against the oracle: routing bit-exact for every
+    token, y within tolerance, and the same as the one-chunk call."""
+    import torch
+    import routed_expert_ffn_gemv_amd as moe
+    cfg, chunk, use_aux = CHUNKED[name]
+    say(f"[gpu] prefill layer {name}: T={cfg.T} chunk={chunk} aux={use_aux}")
+    x, _ = oracle.margin_x(cfg, 0)
+    L = DeviceLayer(cfg, 0, x=x)
+    T, k, H = cfg.T, cfg.k, cfg.H
+    dev = "cuda"
+
+    def run(c, aux):
+        ws = torch.zeros(moe.moe_prefill_workspace_size(L.desc, T, c), dtype=torch.uint8,
+                         device=dev)
+        y = torch.full((T, H), float("nan"), dtype=torch.float32, device=dev)
+        idx = torch.full((T, k), -3, dtype=torch.int32, device=dev)
+        gate = torch.full((T, k), -3.0, dtype=torch.float32, device=dev)
+        sl = torch.full((T, k), -3, dtype=torch.int32, device=dev)
+        moe.moe_prefill_layer(L.desc, L.inp["x"], T, c, y, idx, gate, sl, ws,
+                              aux_stream=torch.cuda.Stream() if aux else None)
+        torch.cuda.synchronize()
+        return {"y": y, "idx": idx, "gate": gate, "slot_idx": sl}
+
+    o = run(chunk, use_aux)
+    ref = L.oracle()
+    np.testing.assert_array_equal(host(o["idx"]), ref["idx"])
+    np.testing.assert_array_equal(host(o["slot_idx"]), ref["slot_idx"])
+    g = host(o["gate"]).astype(np.float64)
+    assert np.all(np.abs(g - ref["gate"]) <= TOL * np.abs(ref["gate"]))
+    assert rowwise_rel_err(host(o["y"]), ref["y"]) <= TOL
+    whole = run(T, False)
+    np.testing.assert_array_equal(host(whole["idx"]), host(o["idx"]))
+    assert rowwise_rel_err(host(o["y"]), host(whole["y"]).astype(np.float64)) <= TOL
