@@ -54,8 +54,8 @@ TRAFFIC = {
                            "bytes": 23111717},
     # c5: the kernels of one moe_expert_ffn call (active list, schedule, x16,
     # gate/up and down GEMMs; profiles/c5_prefill_hbm_traffic.md)
-    "c5_prefill_q4": {"sha256": "7c6bdd3262b01a17d99ffe4afdcbba63256ab541f07cc2173512ad1b72967401",
-                      "bytes": 8913486161},
+    "c5_prefill_q4": {"sha256": "ec3d59190fb602334b9f173b2a13d05b47ef5a3d8fddbf5b8f55b59b44f780e4",
+                      "bytes": 8951866931},
 }
 
 
@@ -604,7 +604,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c4a", "c5"])
     ap.add_argument("--layers", type=int, default=48)
-    ap.add_argument("--cpu-tokens", type=int, default=12)
+    ap.add_argument("--cpu-tokens", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-chunks", default="", metavar="C1,C2,...",
                     help="c5: also time moe_prefill_layer at these chunk sizes, with and "
