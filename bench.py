@@ -50,8 +50,8 @@ KERNEL_SOURCES = {
 TRAFFIC = {
     # workload: {"sha256": ..., "bytes": fetched + written per launch}
     # c2: the moe_layer kernel (profiles/c2_decode_layer_hbm_traffic.md)
-    "c2_decode_layer_q2": {"sha256": "5eff0de9bb5b25e098f0c7a102e724b526f5894b1227b36e30f7f922aa7f563a",
-                           "bytes": 23111717},
+    "c2_decode_layer_q2": {"sha256": "a09f1cfdb1ce71a73052009e9a2899f7e3a06d92a6b9d6d179ed163407d11d8f",
+                           "bytes": 23112298},
     # c5: the kernels of one moe_expert_ffn call (active list, schedule, x16,
     # gate/up and down GEMMs; profiles/c5_prefill_hbm_traffic.md)
     "c5_prefill_q4": {"sha256": "ec3d59190fb602334b9f173b2a13d05b47ef5a3d8fddbf5b8f55b59b44f780e4",

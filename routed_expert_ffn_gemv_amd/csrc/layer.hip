@@ -1548,7 +1548,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   int c_first = b + wave * G, c_end = n_tasks, c_step = kWaves * G;
   int d_first = b, d_end = n_units, d_step = G;
   if constexpr (TB > 1) {
-    constexpr int kCostC = 1, kCostD = 2;
+    constexpr int kCostC = 2, kCostD = 1;
     const int n_db = n_act + (a.has_sh ? 1 : 0);
     // (costs stay below 2^20; a bound's exact quotient a * tot / W comes from
     // double arithmetic: the product is exact and no quotient lies within a
