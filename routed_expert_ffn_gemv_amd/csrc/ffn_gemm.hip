@@ -222,7 +222,7 @@ constexpr int kMT = kQM / 32;     // MFMA row tiles per wave
 template <int FMT, bool GU>
 __global__ __launch_bounds__(256, 2) void qgemm_kernel(GemmArgs a, int n_ntiles) {
   constexpr int kCW = FMT == MOE_W_Q4B32 ? 4 : 2;   // code dwords of one block
-  __shared__ uint16_t As[2][kQM * kLdsRow];
+  __shared__ __align__(16) uint16_t As[2][kQM * kLdsRow];
   __shared__ uint32_t Sd[2][kBN * kSdRow];   // d | m << 16 per (weight row, block of the group)
   __shared__ int arow[kQM];
   __shared__ int orow[kQM];      // down: pair_out row of each tile row
@@ -268,12 +268,10 @@ __global__ __launch_bounds__(256, 2) void qgemm_kernel(GemmArgs a, int n_ntiles)
   const int col = lane & 31, bh = lane >> 5;
   const int64_t row_bytes = int64_t(K) * fmt_bits(FMT) / 8;
   const uint8_t* cw[2];
-  int wrow0 = 0;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const MatView* Wm;
     const int r = weight_row(wave * 64 + j * 32 + col, Wm);
-    if (j == 0) wrow0 = r;
     cw[j] = Wm->codes + slot * Wm->mat_bytes + r * row_bytes;
   }
   // scale group staging: thread tid loads weight row tid's 8 scales and mins
@@ -286,17 +284,24 @@ __global__ __launch_bounds__(256, 2) void qgemm_kernel(GemmArgs a, int n_ntiles)
     sg_mn = Wm->mn + b;
   }
 
-  u32x4 ra1[kMT], ra2[kMT];      // A of K steps kt+1, kt+2 in flight
-  uint32_t wc[3][2][kCW];        // codes of K steps kt, kt+1, kt+2
+  // Registers in flight are indexed by K-step parity and the K loop is
+  // unrolled over one scale group, so no register copy ever forces a wait
+  // for loads issued in the same step: A of step kt + 2 and its codes are
+  // loaded into the parity-kt buffers at the start of step kt; A of step
+  // kt + 1 (loaded one step earlier) goes to LDS at its end.  Loads past the
+  // last step repeat the last step (in bounds, unused), so every step issues
+  // the same loads and the wait counts stay exact.
+  u32x4 ra[2][kMT];              // A of K steps kt + 1 and kt + 2
+  uint32_t wc[2][2][kCW];        // codes of K steps kt + 1 and kt + 2
   u32x4 gsc, gmn;                // scales / mins of the next group in flight
-  auto load_a = [&](int kt, u32x4* ra) {
+  auto load_a = [&](int kt, u32x4* r) {
 #pragma unroll
-    for (int q = 0; q < kMT; ++q) ra[q] = *reinterpret_cast<const u32x4*>(abase + aoff[q] + kt * kBK);
+    for (int q = 0; q < kMT; ++q) r[q] = *reinterpret_cast<const u32x4*>(abase + aoff[q] + kt * kBK);
   };
-  auto store_a = [&](const u32x4* ra, int buf) {
+  auto store_a = [&](const u32x4* r, int buf) {
 #pragma unroll
     for (int q = 0; q < kMT; ++q)
-      *reinterpret_cast<u32x4*>(&As[buf][(q * 32 + (tid >> 3)) * kLdsRow + achunk * 8]) = ra[q];
+      *reinterpret_cast<u32x4*>(&As[buf][(q * 32 + (tid >> 3)) * kLdsRow + achunk * 8]) = r[q];
   };
   auto load_codes = [&](int kt, uint32_t (*c)[kCW]) {
     const int blk = 2 * kt + bh;
@@ -330,7 +335,8 @@ __global__ __launch_bounds__(256, 2) void qgemm_kernel(GemmArgs a, int n_ntiles)
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
   // Scale group g sits in Sd[g & 1] from the K step before its first one
-  // on; its loads are issued three K steps before that.
+  // on; its loads are issued three K steps before that (the last group's
+  // loads are repeated past the end, into a buffer nothing reads again).
   const int ngroups = nk / kGroup;
   auto scales = [&](int kt, int j, f16x2& d2, f16x2& m2) {
     const uint32_t dm = Sd[(kt / kGroup) & 1][(wave * 64 + j * 32 + col) * kSdRow + 2 * (kt % kGroup) + bh];
@@ -338,17 +344,13 @@ __global__ __launch_bounds__(256, 2) void qgemm_kernel(GemmArgs a, int n_ntiles)
     m2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(dm, dm, 0x03020302u));
   };
   load_group(0);
-  load_a(0, ra1);
+  load_a(0, ra[0]);
   load_codes(0, wc[0]);
-  if (nk > 1) {
-    load_a(1, ra2);
-    load_codes(1, wc[1]);
-  }
+  load_a(min(1, nk - 1), ra[1]);
+  load_codes(min(1, nk - 1), wc[1]);
   store_group(0);
-  if (ngroups > 1) load_group(1);
-  store_a(ra1, 0);
-#pragma unroll
-  for (int q = 0; q < kMT; ++q) ra1[q] = ra2[q];
+  load_group(min(1, ngroups - 1));
+  store_a(ra[0], 0);
   __syncthreads();
   // weight operands of K step 0
   f16x8 bv[2][4];
@@ -359,50 +361,42 @@ __global__ __launch_bounds__(256, 2) void qgemm_kernel(GemmArgs a, int n_ntiles)
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) bv[j][kk] = w_operand<FMT>(wc[0][j], kk, d2, m2);
   }
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 2 < nk) {
-      load_a(kt + 2, ra2);
-      load_codes(kt + 2, wc[2]);
-    }
-    const bool more = kt + 1 < nk;
-    f16x2 dn[2], mn[2];   // scales of the next K step
+  for (int kt0 = 0; kt0 < nk; kt0 += kGroup) {
+    const int g = kt0 / kGroup;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) scales(more ? kt + 1 : kt, j, dn[j], mn[j]);
-    const uint16_t* Ab = As[kt & 1];
-    // the next K step's weight operand kk is built while the MFMAs of kk
-    // run, in the registers those MFMAs have just read
+    for (int s = 0; s < kGroup; ++s) {
+      const int kt = kt0 + s, p = s & 1;   // kt0 is even: p is the parity of kt
+      const int kl = min(kt + 2, nk - 1), kn = min(kt + 1, nk - 1);
+      load_a(kl, ra[p]);
+      load_codes(kl, wc[p]);
+      f16x2 dn[2], mn[2];   // scales of the next K step
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      f16x8 av[kMT];
+      for (int j = 0; j < 2; ++j) scales(kn, j, dn[j], mn[j]);
+      const uint16_t* Ab = As[p];
+      // the next K step's weight operand kk is built while the MFMAs of kk
+      // run, in the registers those MFMAs have just read (after the last
+      // step the build repeats the last step's operands, unused)
 #pragma unroll
-      for (int i = 0; i < kMT; ++i)
-        av[i] = *reinterpret_cast<const f16x8*>(Ab + (i * 32 + col) * kLdsRow + bh * 32 + kk * 8);
+      for (int kk = 0; kk < 4; ++kk) {
+        f16x8 av[kMT];
 #pragma unroll
-      for (int i = 0; i < kMT; ++i)
+        for (int i = 0; i < kMT; ++i)
+          av[i] = *reinterpret_cast<const f16x8*>(Ab + (i * 32 + col) * kLdsRow + bh * 32 + kk * 8);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j][kk], acc[i][j], 0, 0, 0);
-      if (more) {
+        for (int i = 0; i < kMT; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) bv[j][kk] = w_operand<FMT>(wc[1][j], kk, dn[j], mn[j]);
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j][kk], acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) bv[j][kk] = w_operand<FMT>(wc[p ^ 1][j], kk, dn[j], mn[j]);
       }
-    }
-    const int g = kt / kGroup, ks = kt % kGroup;
-    if (more) store_a(ra1, (kt + 1) & 1);
-    if (ks == kGroup - 2 && g + 1 < ngroups) {
-      store_group((g + 1) & 1);
-      if (g + 2 < ngroups) load_group(g + 2);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < kMT; ++q) ra1[q] = ra2[q];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int c = 0; c < kCW; ++c) {
-        wc[0][j][c] = wc[1][j][c];
-        wc[1][j][c] = wc[2][j][c];
+      store_a(ra[p ^ 1], p ^ 1);
+      if (s == kGroup - 2) {
+        store_group((g + 1) & 1);
+        load_group(min(g + 2, ngroups - 1));
       }
+      __syncthreads();
+    }
   }
   // epilogue: element v of lane l is row 8 (v / 4) + 4 (l / 32) + v % 4 of
   // the 32 x 32 tile, column l % 32
@@ -432,18 +426,31 @@ __global__ __launch_bounds__(256, 2) void qgemm_kernel(GemmArgs a, int n_ntiles)
             *reinterpret_cast<const u32x4*>(ht + row * kHRow + ch * 8);
     }
   } else {
-    float* out = rm.shared ? a.shared_out : a.pair_out;
+    // the fp32 tile in 32-row slabs through LDS, then whole 1 KB row pieces
+    // to pair_out, 16 bytes per lane
+    constexpr int kORow = kBN + 4;   // floats per LDS row
+    static_assert(32 * kORow * 4 <= int(sizeof(As)), "an output slab fits in the A buffers");
+    float* ot = reinterpret_cast<float*>(&As[0][0]);
+    float* out = (rm.shared ? a.shared_out : a.pair_out) + nt * kBN;
+    const int ocol = wave * 64 + col;
 #pragma unroll
-    for (int i = 0; i < kMT; ++i)
+    for (int i = 0; i < kMT; ++i) {
+      if (i > 0) __syncthreads();   // the previous slab has been read
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = i * 32 + 8 * (v >> 2) + 4 * bh + (v & 3);
-        if (row < rm.rows) {
-          const int64_t o = int64_t(orow[row]) * a.H + wrow0;
+        const int r = 8 * (v >> 2) + 4 * bh + (v & 3);
 #pragma unroll
-          for (int j = 0; j < 2; ++j) out[o + 32 * j] = acc[i][j][v];
-        }
+        for (int j = 0; j < 2; ++j) ot[r * kORow + ocol + 32 * j] = acc[i][j][v];
       }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 32 / 4; ++q) {
+        const int r = q * 4 + (tid >> 6), c4 = tid & 63;
+        if (i * 32 + r < rm.rows)
+          *reinterpret_cast<float4*>(out + int64_t(orow[i * 32 + r]) * a.H + 4 * c4) =
+              *reinterpret_cast<const float4*>(ot + r * kORow + 4 * c4);
+      }
+    }
   }
 }
 
