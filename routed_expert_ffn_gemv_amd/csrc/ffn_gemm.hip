@@ -217,41 +217,26 @@ __global__ __launch_bounds__(256) void x16_kernel(const uint16_t* __restrict__ x
 constexpr int kBN = 256;          // weight rows per tile
 constexpr int kSdRow = 9;         // dwords per weight row in the scale table (8 + pad)
 constexpr int kGroup = 4;         // K steps per scale group (8 blocks)
-constexpr int kMT = kQM / 32;     // MFMA row tiles per wave
 
-template <int FMT, bool GU>
-__global__ __launch_bounds__(256, 2) void qgemm_kernel(GemmArgs a, int n_ntiles) {
+typedef uint16_t ATile[kQM * kLdsRow];
+typedef uint32_t STable[kBN * kSdRow];
+
+// One tile whose rows fit in MT MFMA row tiles (MT * 32 >= rows): the
+// waves skip the row tiles of a bucket's last, partly filled tile.
+template <int FMT, bool GU, int MT>
+__device__ __forceinline__ void qgemm_tile(const GemmArgs& a, const RowMap& rm, int nt, ATile* As,
+                                           STable* Sd, const int* arow, const int* orow) {
   constexpr int kCW = FMT == MOE_W_Q4B32 ? 4 : 2;   // code dwords of one block
-  __shared__ __align__(16) uint16_t As[2][kQM * kLdsRow];
-  __shared__ uint32_t Sd[2][kBN * kSdRow];   // d | m << 16 per (weight row, block of the group)
-  __shared__ int arow[kQM];
-  __shared__ int orow[kQM];      // down: pair_out row of each tile row
-  const int w = xcd_item();
-  const int total = *a.n_tiles * n_ntiles;
-  if (w >= total) return;
-  const int n_act = *a.act.count;
-  const int2 tinfo = a.tiles[w / n_ntiles];
-  const int nt = w % n_ntiles;
-  const RowMap rm = row_map(a, tinfo, n_act);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = GU ? a.H : a.I;
   const int nk = K / kBK, nb = K / 32;
-  // A source rows: gate/up gathers token rows of x16; down reads h rows at
-  // the bucket positions.  Rows past the bucket read row 0 of the tile.
-  if (tid < kQM) {
-    const int r = tid < rm.rows ? tid : 0;
-    const int p = rm.shared ? rm.pos0 + r : a.bucket_pair[rm.pos0 + r];
-    arow[tid] = GU ? (rm.shared ? p : p / a.k) : rm.pos0 + r;
-    orow[tid] = p;
-  }
-  __syncthreads();
   const uint16_t* abase = GU ? a.x16 : (rm.shared ? a.h_sh : a.h);
   // A staging: 8 lanes per row (16 bytes each, a whole 128-byte K step);
   // this thread's rows q * 32 + tid / 8, q = 0..3
   const int achunk = tid & 7;
-  uint32_t aoff[kMT];
+  uint32_t aoff[MT];
 #pragma unroll
-  for (int q = 0; q < kMT; ++q) aoff[q] = uint32_t(arow[q * 32 + (tid >> 3)]) * uint32_t(K) + achunk * 8;
+  for (int q = 0; q < MT; ++q) aoff[q] = uint32_t(arow[q * 32 + (tid >> 3)]) * uint32_t(K) + achunk * 8;
   // weight rows: tile row R = wave * 64 + j * 32 + col (j = MFMA column tile)
   const MatView W0 = GU ? (rm.shared ? a.sg : a.g) : (rm.shared ? a.sd : a.d);
   const MatView W1 = GU ? (rm.shared ? a.su : a.u) : W0;
@@ -291,16 +276,16 @@ __global__ __launch_bounds__(256, 2) void qgemm_kernel(GemmArgs a, int n_ntiles)
   // kt + 1 (loaded one step earlier) goes to LDS at its end.  Loads past the
   // last step repeat the last step (in bounds, unused), so every step issues
   // the same loads and the wait counts stay exact.
-  u32x4 ra[2][kMT];              // A of K steps kt + 1 and kt + 2
+  u32x4 ra[2][MT];              // A of K steps kt + 1 and kt + 2
   uint32_t wc[2][2][kCW];        // codes of K steps kt + 1 and kt + 2
   u32x4 gsc, gmn;                // scales / mins of the next group in flight
   auto load_a = [&](int kt, u32x4* r) {
 #pragma unroll
-    for (int q = 0; q < kMT; ++q) r[q] = *reinterpret_cast<const u32x4*>(abase + aoff[q] + kt * kBK);
+    for (int q = 0; q < MT; ++q) r[q] = *reinterpret_cast<const u32x4*>(abase + aoff[q] + kt * kBK);
   };
   auto store_a = [&](const u32x4* r, int buf) {
 #pragma unroll
-    for (int q = 0; q < kMT; ++q)
+    for (int q = 0; q < MT; ++q)
       *reinterpret_cast<u32x4*>(&As[buf][(q * 32 + (tid >> 3)) * kLdsRow + achunk * 8]) = r[q];
   };
   auto load_codes = [&](int kt, uint32_t (*c)[kCW]) {
@@ -328,9 +313,9 @@ __global__ __launch_bounds__(256, 2) void qgemm_kernel(GemmArgs a, int n_ntiles)
       d[2 * q + 1] = (gsc[q] >> 16) | (gmn[q] & 0xFFFF0000u);
     }
   };
-  f32x16 acc[kMT][2];
+  f32x16 acc[MT][2];
 #pragma unroll
-  for (int i = 0; i < kMT; ++i)
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
@@ -378,12 +363,12 @@ __global__ __launch_bounds__(256, 2) void qgemm_kernel(GemmArgs a, int n_ntiles)
       // step the build repeats the last step's operands, unused)
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        f16x8 av[kMT];
+        f16x8 av[MT];
 #pragma unroll
-        for (int i = 0; i < kMT; ++i)
+        for (int i = 0; i < MT; ++i)
           av[i] = *reinterpret_cast<const f16x8*>(Ab + (i * 32 + col) * kLdsRow + bh * 32 + kk * 8);
 #pragma unroll
-        for (int i = 0; i < kMT; ++i)
+        for (int i = 0; i < MT; ++i)
 #pragma unroll
           for (int j = 0; j < 2; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j][kk], acc[i][j], 0, 0, 0);
@@ -409,7 +394,7 @@ __global__ __launch_bounds__(256, 2) void qgemm_kernel(GemmArgs a, int n_ntiles)
     const int fl = wave * 32 + col;  // feature within the tile
     const int fcol = (fl & ~31) + perm_pos<FMT>(fl & 31);
 #pragma unroll
-    for (int i = 0; i < kMT; ++i)
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = i * 32 + 8 * (v >> 2) + 4 * bh + (v & 3);
@@ -429,12 +414,12 @@ __global__ __launch_bounds__(256, 2) void qgemm_kernel(GemmArgs a, int n_ntiles)
     // the fp32 tile in 32-row slabs through LDS, then whole 1 KB row pieces
     // to pair_out, 16 bytes per lane
     constexpr int kORow = kBN + 4;   // floats per LDS row
-    static_assert(32 * kORow * 4 <= int(sizeof(As)), "an output slab fits in the A buffers");
+    static_assert(32 * kORow * 4 <= int(2 * sizeof(ATile)), "an output slab fits in the A buffers");
     float* ot = reinterpret_cast<float*>(&As[0][0]);
     float* out = (rm.shared ? a.shared_out : a.pair_out) + nt * kBN;
     const int ocol = wave * 64 + col;
 #pragma unroll
-    for (int i = 0; i < kMT; ++i) {
+    for (int i = 0; i < MT; ++i) {
       if (i > 0) __syncthreads();   // the previous slab has been read
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -452,6 +437,40 @@ __global__ __launch_bounds__(256, 2) void qgemm_kernel(GemmArgs a, int n_ntiles)
       }
     }
   }
+}
+
+template <int FMT, bool GU>
+__global__ __launch_bounds__(256, 2) void qgemm_kernel(GemmArgs a, int n_ntiles) {
+  __shared__ __align__(16) ATile As[2];
+  __shared__ STable Sd[2];   // d | m << 16 per (weight row, block of the group)
+  __shared__ int arow[kQM];
+  __shared__ int orow[kQM];  // down: pair_out row of each tile row
+  const int w = xcd_item();
+  const int total = *a.n_tiles * n_ntiles;
+  if (w >= total) return;
+  const int n_act = *a.act.count;
+  const int2 tinfo = a.tiles[w / n_ntiles];
+  const int nt = w % n_ntiles;
+  const RowMap rm = row_map(a, tinfo, n_act);
+  const int tid = threadIdx.x;
+  // A source rows: gate/up gathers token rows of x16; down reads h rows at
+  // the bucket positions.  Rows past the bucket read row 0 of the tile.
+  if (tid < kQM) {
+    const int r = tid < rm.rows ? tid : 0;
+    const int p = rm.shared ? rm.pos0 + r : a.bucket_pair[rm.pos0 + r];
+    arow[tid] = GU ? (rm.shared ? p : p / a.k) : rm.pos0 + r;
+    orow[tid] = p;
+  }
+  __syncthreads();
+  const int mt = (rm.rows + 31) >> 5;   // wave-uniform
+  if (mt >= 4)
+    qgemm_tile<FMT, GU, 4>(a, rm, nt, As, Sd, arow, orow);
+  else if (mt == 3)
+    qgemm_tile<FMT, GU, 3>(a, rm, nt, As, Sd, arow, orow);
+  else if (mt == 2)
+    qgemm_tile<FMT, GU, 2>(a, rm, nt, As, Sd, arow, orow);
+  else
+    qgemm_tile<FMT, GU, 1>(a, rm, nt, As, Sd, arow, orow);
 }
 
 // MFMA on one K step from LDS (bf16 router): wave tile = (MT x 32 rows) x
