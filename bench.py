@@ -54,8 +54,8 @@ TRAFFIC = {
                            "bytes": 23112298},
     # c5: the kernels of one moe_expert_ffn call (active list, schedule, x16,
     # gate/up and down GEMMs; profiles/c5_prefill_hbm_traffic.md)
-    "c5_prefill_q4": {"sha256": "ec3d59190fb602334b9f173b2a13d05b47ef5a3d8fddbf5b8f55b59b44f780e4",
-                      "bytes": 8951866931},
+    "c5_prefill_q4": {"sha256": "0b53cc97298df40d52ade8aef92e830a2d07a033ace74591eede48596940131a",
+                      "bytes": 9143742838},
 }
 
 
