@@ -15,7 +15,17 @@ MID = {
     "q2_T517": small_cfg(E=48, k=5, H=256, I=192, T=517, wfmt="q2", bias="zipf", seed=42),
     "q4_T700_noshared": small_cfg(E=32, k=4, H=384, I=64, T=700, wfmt="q4", shared=False,
                                   seed=43),
+    # grouped-GEMM shapes (H and I multiples of 256, at least 2048 pairs):
+    # buckets of several row tiles with last tiles of 1-4 MFMA row tiles,
+    # K loops of one scale group (K = 256) and of two (K = 512)
+    "gemm_q2_T1100": small_cfg(E=32, k=4, H=512, I=256, T=1100, wfmt="q2", bias="zipf", seed=45),
+    "gemm_q4_T900_noshared": small_cfg(E=24, k=3, H=256, I=512, T=900, wfmt="q4", shared=False,
+                                       bias="zipf", seed=46),
 }
+
+
+def _uses_gemm(cfg):
+    return cfg.T * cfg.k >= 2048 and cfg.H % 256 == 0 and cfg.I % 256 == 0
 
 
 @pytest.mark.parametrize("name", list(MID))
@@ -29,6 +39,12 @@ def test_prefill_mid(name):
     check_routing(o, ref, cfg.k)
     np.testing.assert_array_equal(host(o["bucket_off"]), ref["bucket_off"])
     np.testing.assert_array_equal(host(o["bucket_pair"]), ref["bucket_pair"])
+    if name.startswith("gemm"):
+        assert _uses_gemm(cfg)
+        sizes = np.diff(ref["bucket_off"])
+        tails = {int((n - 1) % 128) // 32 + 1 for n in sizes if n > 0}
+        say(f"  bucket sizes {sizes.min()}..{sizes.max()}, last-tile row tiles {sorted(tails)}")
+        assert sizes.max() > 128 and len(tails) >= 3
     hit = ref["slot_idx"].ravel() >= 0
     assert rowwise_rel_err(host(o["pair_out"])[hit], ref["pair_out"][hit]) <= TOL
     if cfg.shared:
@@ -36,10 +52,19 @@ def test_prefill_mid(name):
     assert rowwise_rel_err(host(o["y"]), ref["y"]) <= TOL
 
 
-def test_prefill_mid_partial_slots():
-    """Large-T resolution with misses: bit-exact miss list and offsets."""
-    cfg = small_cfg(E=64, k=6, H=256, I=128, T=450, wfmt="q4", bias="zipf", seed=44)
-    say("[gpu] prefill with a partial slot table")
+PARTIAL = {
+    "gemv": small_cfg(E=64, k=6, H=256, I=128, T=450, wfmt="q4", bias="zipf", seed=44),
+    "gemm": small_cfg(E=64, k=6, H=256, I=256, T=800, wfmt="q4", bias="zipf", seed=47),
+}
+
+
+@pytest.mark.parametrize("name", list(PARTIAL))
+def test_prefill_mid_partial_slots(name):
+    """Large-T resolution with misses: bit-exact miss list and offsets; the
+    expert FFN of the hits by GEMV or by grouped GEMM."""
+    cfg = PARTIAL[name]
+    assert _uses_gemm(cfg) == (name == "gemm")
+    say(f"[gpu] prefill with a partial slot table ({name})")
     x, _ = oracle.margin_x(cfg, 0)
     rank = synth.popularity_rank(cfg, 0)
     resident = np.sort(np.argsort(rank)[:40])
@@ -95,6 +120,9 @@ CHUNKED = {
     "q2_T517_chunk100_aux": (MID["q2_T517"], 100, True),
     "q4_T700_noshared_chunk700": (MID["q4_T700_noshared"], 700, False),
     "q4_T600_chunk7_main": (MID["q4_T600"], 7, False),
+    # first chunk through the grouped GEMMs (2,400 pairs), last through the
+    # GEMVs (2,000 pairs)
+    "gemm_q2_T1100_chunk600_aux": (MID["gemm_q2_T1100"], 600, True),
 }
 
 
