@@ -39,6 +39,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 128;          // rows per router tile
 constexpr int kQM = 128;          // rows per grouped-GEMM tile
@@ -412,7 +413,9 @@ __device__ __forceinline__ void qgemm_tile(const GemmArgs& a, const RowMap& rm, 
     }
   } else {
     // the fp32 tile in 32-row slabs through LDS, then whole 1 KB row pieces
-    // to pair_out, 16 bytes per lane
+    // to pair_out, 16 bytes per lane, as non-temporal stores (the combine
+    // reads them much later; they would only displace weights and tokens
+    // from the L2)
     constexpr int kORow = kBN + 4;   // floats per LDS row
     static_assert(32 * kORow * 4 <= int(2 * sizeof(ATile)), "an output slab fits in the A buffers");
     float* ot = reinterpret_cast<float*>(&As[0][0]);
@@ -432,8 +435,8 @@ __device__ __forceinline__ void qgemm_tile(const GemmArgs& a, const RowMap& rm, 
       for (int q = 0; q < 32 / 4; ++q) {
         const int r = q * 4 + (tid >> 6), c4 = tid & 63;
         if (i * 32 + r < rm.rows)
-          *reinterpret_cast<float4*>(out + int64_t(orow[i * 32 + r]) * a.H + 4 * c4) =
-              *reinterpret_cast<const float4*>(ot + r * kORow + 4 * c4);
+          __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(ot + r * kORow + 4 * c4),
+                                      reinterpret_cast<f32x4*>(out + int64_t(orow[i * 32 + r]) * a.H + 4 * c4));
       }
     }
   }
