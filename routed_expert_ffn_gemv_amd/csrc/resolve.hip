@@ -241,36 +241,55 @@ __global__ __launch_bounds__(1024) void resolve_scan_kernel(int T, int S, int nc
   }
 }
 
-__global__ __launch_bounds__(256) void resolve_scatter_kernel(
+// 3. One wave per chunk, 64 pairs at a time in pair order.  A pair's place
+// among the chunk's pairs of its slot is the slot's running count plus the
+// earlier lanes with the same slot; the lanes with equal slots are found by
+// one ballot per key bit (misses take the key S).  Misses are ranked by
+// their own ballot.
+__global__ __launch_bounds__(64) void resolve_scatter_kernel(
     int P, int k, int S, int nchunk, const int32_t* __restrict__ idx, const float* __restrict__ gate,
     const int32_t* __restrict__ slot_idx, LargeWs w, int32_t* __restrict__ bucket_pair,
     moe_miss* __restrict__ miss, int32_t* __restrict__ miss_off) {
-  __shared__ int sl[kResolveChunk];
-  const int c = blockIdx.x;
+  extern __shared__ int run[];   // [S] pairs of each slot placed so far in the chunk
+  const int c = blockIdx.x, lane = threadIdx.x;
   const int p0 = c * kResolveChunk;
   const int n = min(kResolveChunk, P - p0);
-  for (int i = threadIdx.x; i < kResolveChunk; i += blockDim.x)
-    sl[i] = i < n ? slot_idx[p0 + i] : -2;
+  for (int q = lane; q < S; q += 64) run[q] = 0;
   __syncthreads();
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    const int s = sl[i];
-    int r = 0, rm = 0;
-    for (int q = 0; q < i; ++q) {
-      const int sq = sl[q];
-      r += (sq == s) ? 1 : 0;
-      rm += (sq < 0) ? 1 : 0;
-    }
+  const int nbits = 32 - __clz(S);   // keys 0 .. S
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  const int cmiss = w.cmiss[c];
+  int mbase = 0;                     // misses in the earlier groups
+  for (int g = 0; g < n; g += 64) {
+    const int i = g + lane;
+    const bool valid = i < n;
     const int p = p0 + i;
-    if (s >= 0) {
-      if (bucket_pair) bucket_pair[w.sbase[s] + w.cnt[int64_t(c) * S + s] + r] = p;
-    } else if (miss) {
+    const int sl = valid ? slot_idx[p] : -1;
+    const int key = sl >= 0 ? sl : S;
+    uint64_t same = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (key >> b) & 1;
+      const uint64_t set = __ballot(bit);
+      same &= bit ? set : ~set;
+    }
+    const uint64_t missm = __ballot(valid && sl < 0);
+    const int rm = mbase + __popcll(missm & below);
+    if (valid && sl >= 0) {
+      const int within = __popcll(same & below);
+      const int base = run[sl];
+      // every lane has read its count before the first lane of each slot
+      // (program order within the wave) adds the group's pairs
+      if (within == 0) run[sl] = base + __popcll(same);
+      if (bucket_pair) bucket_pair[w.sbase[sl] + w.cnt[int64_t(c) * S + sl] + base + within] = p;
+    } else if (valid && miss) {
       moe_miss m;
       m.expert = idx[p];
       m.token = p / k;
       m.gate = gate[p];
-      miss[w.cmiss[c] + rm] = m;
+      miss[cmiss + rm] = m;
     }
-    if (miss_off && p % k == 0) miss_off[p / k] = w.cmiss[c] + rm;
+    if (valid && miss_off && p % k == 0) miss_off[p / k] = cmiss + rm;
+    mbase += __popcll(missm);
   }
 }
 
@@ -287,8 +306,8 @@ hipError_t launch_resolve_large(int T, int k, int E, int S, const int32_t* idx,
                      nchunk, w);
   hipLaunchKernelGGL(resolve_scan_kernel, dim3(1), dim3(1024), 0, st, T, S, nchunk, w,
                      bucket_off, miss_off, act);
-  hipLaunchKernelGGL(resolve_scatter_kernel, dim3(nchunk), dim3(256), 0, st, P, k, S, nchunk, idx,
-                     gate, slot_idx, w, bucket_pair, miss, miss_off);
+  hipLaunchKernelGGL(resolve_scatter_kernel, dim3(nchunk), dim3(64), size_t(S) * 4, st, P, k, S,
+                     nchunk, idx, gate, slot_idx, w, bucket_pair, miss, miss_off);
   return hipGetLastError();
 }
 
