@@ -54,8 +54,8 @@ TRAFFIC = {
                            "bytes": 23112298},
     # c5: the kernels of one moe_expert_ffn call (active list, schedule, x16,
     # gate/up and down GEMMs; profiles/c5_prefill_hbm_traffic.md)
-    "c5_prefill_q4": {"sha256": "0b53cc97298df40d52ade8aef92e830a2d07a033ace74591eede48596940131a",
-                      "bytes": 9143742838},
+    "c5_prefill_q4": {"sha256": "67aa3636541855a722f39743215ff6fd385952b0aafd99a214db0f3579eb9f33",
+                      "bytes": 9005277735},
 }
 
 
