@@ -52,6 +52,12 @@ TRAFFIC = {
     # c2: the moe_layer kernel (profiles/c2_decode_layer_hbm_traffic.md)
     "c2_decode_layer_q2": {"sha256": "a09f1cfdb1ce71a73052009e9a2899f7e3a06d92a6b9d6d179ed163407d11d8f",
                            "bytes": 23112298},
+    # c3: the moe_layer kernel (profiles/c3_verify_stack_hbm_traffic.md)
+    "c3_verify_stack_q2": {"sha256": "a09f1cfdb1ce71a73052009e9a2899f7e3a06d92a6b9d6d179ed163407d11d8f",
+                           "bytes": 70396353},
+    # c4: the moe_layer kernel (profiles/c4_slot_tiering_hbm_traffic.md)
+    "c4_slot_tiering_q2": {"sha256": "a09f1cfdb1ce71a73052009e9a2899f7e3a06d92a6b9d6d179ed163407d11d8f",
+                           "bytes": 121756325},
     # c5: the kernels of one moe_expert_ffn call (active list, schedule, x16,
     # gate/up and down GEMMs; profiles/c5_prefill_hbm_traffic.md)
     "c5_prefill_q4": {"sha256": "67aa3636541855a722f39743215ff6fd385952b0aafd99a214db0f3579eb9f33",
