@@ -60,7 +60,7 @@ TRAFFIC = {
                            "bytes": 121756325},
     # c5: the kernels of one moe_expert_ffn call (active list, schedule, x16,
     # gate/up and down GEMMs; profiles/c5_prefill_hbm_traffic.md)
-    "c5_prefill_q4": {"sha256": "67aa3636541855a722f39743215ff6fd385952b0aafd99a214db0f3579eb9f33",
+    "c5_prefill_q4": {"sha256": "e81bd10e36a2fd50e8b60b7b019701087c68047e42b7222585b7bccc4b3a984e",
                       "bytes": 9005277735},
 }
 

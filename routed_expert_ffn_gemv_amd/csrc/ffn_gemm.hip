@@ -25,7 +25,12 @@
 //    (4 x 2 MFMA 32x32x16 tiles, fp32 accumulation).  gate/up waves hold 32
 //    gate rows and the 32 up rows of the same features, so SwiGLU happens in
 //    registers; h goes through LDS and leaves as whole fp16 rows.  Down waves
-//    hold 64 output columns and write fp32 rows to pair_out by pair id.
+//    hold 64 output columns; their fp32 rows go through LDS in 32-row slabs
+//    and leave as whole row pieces to pair_out by pair id.
+//  - A bucket's last tile runs only the 32-row MFMA tiles its rows fill (the
+//    body is compiled for 1-4 row tiles and chosen once per tile).
+//  - The K loop is unrolled over one scale group with the registers in
+//    flight indexed by K-step parity: no register copy forces a wait.
 //  - Tiles are ordered so that consecutive tiles of one expert run on the
 //    same XCD and share its weights in that XCD's L2.
 #include "gemv_core.h"
