@@ -15,6 +15,9 @@ MID = {
     "q2_T517": small_cfg(E=48, k=5, H=256, I=192, T=517, wfmt="q2", bias="zipf", seed=42),
     "q4_T700_noshared": small_cfg(E=32, k=4, H=384, I=64, T=700, wfmt="q4", shared=False,
                                   seed=43),
+    # MFMA router over several ragged expert tiles (E = 600) and a ragged
+    # token tile, with the 16-keys-per-lane top-k
+    "q2_T300_E600_k12": small_cfg(E=600, k=12, H=256, I=64, T=300, wfmt="q2", bias="zipf", seed=48),
     # grouped-GEMM shapes (H and I multiples of 256, at least 2048 pairs):
     # buckets of several row tiles with last tiles of 1-4 MFMA row tiles,
     # K loops of one scale group (K = 256) and of two (K = 512)
