@@ -216,22 +216,22 @@ __global__ __launch_bounds__(256) void x16_kernel(const uint16_t* __restrict__ x
 }
 
 // ---------------------------------------------------------------- GEMM
-// One grouped-GEMM tile: 128 rows of one bucket x 256 weight rows (gate/up:
-// 128 gate + 128 up rows of 128 features; down: 256 output columns).  Each
-// wave holds all 128 rows x 64 columns (4 x 2 MFMA tiles), so every
-// dequantised weight feeds 4 MFMAs; two workgroups share a CU.
-constexpr int kBN = 256;          // weight rows per tile
+// One grouped-GEMM tile: 128 rows of one bucket x 128 * NJ weight rows
+// (gate/up, NJ = 2: 128 gate + 128 up rows of 128 features; down: 128 * NJ
+// output columns).  Each wave holds all 128 rows x 32 * NJ columns (4 x NJ
+// MFMA tiles), so every dequantised weight feeds 4 MFMAs.
 constexpr int kSdRow = 9;         // dwords per weight row in the scale table (8 + pad)
 constexpr int kGroup = 4;         // K steps per scale group (8 blocks)
 
 typedef uint16_t ATile[kQM * kLdsRow];
-typedef uint32_t STable[kBN * kSdRow];
 
 // One tile whose rows fit in MT MFMA row tiles (MT * 32 >= rows): the
 // waves skip the row tiles of a bucket's last, partly filled tile.
-template <int FMT, bool GU, int MT>
+template <int FMT, bool GU, int MT, int NJ>
 __device__ __forceinline__ void qgemm_tile(const GemmArgs& a, const RowMap& rm, int nt, ATile* As,
-                                           STable* Sd, const int* arow, const int* orow) {
+                                           uint32_t* Sd0, const int* arow, const int* orow) {
+  constexpr int kBNt = 128 * NJ;   // weight rows of the tile (32 * NJ per wave)
+  auto Sd = [&](int buf) { return Sd0 + buf * (kBNt * kSdRow); };
   constexpr int kCW = FMT == MOE_W_Q4B32 ? 4 : 2;   // code dwords of one block
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = GU ? a.H : a.I;
@@ -248,28 +248,28 @@ __device__ __forceinline__ void qgemm_tile(const GemmArgs& a, const RowMap& rm, 
   const MatView W1 = GU ? (rm.shared ? a.su : a.u) : W0;
   const int slot = rm.shared ? 0 : rm.slot;
   auto weight_row = [&](int R, const MatView*& Wm) {
-    const int wv = R >> 6, j = (R >> 5) & 1, c = R & 31;
+    const int wv = R / (32 * NJ), j = (R >> 5) % NJ, c = R & 31;
     if (GU) {
       Wm = j ? &W1 : &W0;
       return nt * 128 + wv * 32 + c;
     }
     Wm = &W0;
-    return nt * 256 + wv * 64 + j * 32 + c;
+    return nt * kBNt + R;
   };
   const int col = lane & 31, bh = lane >> 5;
   const int64_t row_bytes = int64_t(K) * fmt_bits(FMT) / 8;
-  const uint8_t* cw[2];
+  const uint8_t* cw[NJ];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < NJ; ++j) {
     const MatView* Wm;
-    const int r = weight_row(wave * 64 + j * 32 + col, Wm);
+    const int r = weight_row(wave * 32 * NJ + j * 32 + col, Wm);
     cw[j] = Wm->codes + slot * Wm->mat_bytes + r * row_bytes;
   }
   // scale group staging: thread tid loads weight row tid's 8 scales and mins
   const uint16_t *sg_sc, *sg_mn;
   {
     const MatView* Wm;
-    const int r = weight_row(tid, Wm);
+    const int r = weight_row(tid < kBNt ? tid : 0, Wm);
     const int64_t b = int64_t(slot) * Wm->mat_blocks + int64_t(r) * nb;
     sg_sc = Wm->scale + b;
     sg_mn = Wm->mn + b;
@@ -283,7 +283,7 @@ __device__ __forceinline__ void qgemm_tile(const GemmArgs& a, const RowMap& rm, 
   // last step repeat the last step (in bounds, unused), so every step issues
   // the same loads and the wait counts stay exact.
   u32x4 ra[2][MT];              // A of K steps kt + 1 and kt + 2
-  uint32_t wc[2][2][kCW];        // codes of K steps kt + 1 and kt + 2
+  uint32_t wc[2][NJ][kCW];       // codes of K steps kt + 1 and kt + 2
   u32x4 gsc, gmn;                // scales / mins of the next group in flight
   auto load_a = [&](int kt, u32x4* r) {
 #pragma unroll
@@ -297,7 +297,7 @@ __device__ __forceinline__ void qgemm_tile(const GemmArgs& a, const RowMap& rm, 
   auto load_codes = [&](int kt, uint32_t (*c)[kCW]) {
     const int blk = 2 * kt + bh;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       if constexpr (FMT == MOE_W_Q4B32) {
         const u32x4 v = *reinterpret_cast<const u32x4*>(cw[j] + blk * 16);
         c[j][0] = v[0]; c[j][1] = v[1]; c[j][2] = v[2]; c[j][3] = v[3];
@@ -312,25 +312,26 @@ __device__ __forceinline__ void qgemm_tile(const GemmArgs& a, const RowMap& rm, 
     gmn = *reinterpret_cast<const u32x4*>(sg_mn + 8 * g);
   };
   auto store_group = [&](int buf) {
-    uint32_t* d = &Sd[buf][tid * kSdRow];
+    if (tid >= kBNt) return;
+    uint32_t* d = Sd(buf) + tid * kSdRow;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       d[2 * q] = (gsc[q] & 0xFFFFu) | (gmn[q] << 16);
       d[2 * q + 1] = (gsc[q] >> 16) | (gmn[q] & 0xFFFF0000u);
     }
   };
-  f32x16 acc[MT][2];
+  f32x16 acc[MT][NJ];
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
 
   // Scale group g sits in Sd[g & 1] from the K step before its first one
   // on; its loads are issued three K steps before that (the last group's
   // loads are repeated past the end, into a buffer nothing reads again).
   const int ngroups = nk / kGroup;
   auto scales = [&](int kt, int j, f16x2& d2, f16x2& m2) {
-    const uint32_t dm = Sd[(kt / kGroup) & 1][(wave * 64 + j * 32 + col) * kSdRow + 2 * (kt % kGroup) + bh];
+    const uint32_t dm = Sd((kt / kGroup) & 1)[(wave * 32 * NJ + j * 32 + col) * kSdRow + 2 * (kt % kGroup) + bh];
     d2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(dm, dm, 0x01000100u));
     m2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(dm, dm, 0x03020302u));
   };
@@ -344,9 +345,9 @@ __device__ __forceinline__ void qgemm_tile(const GemmArgs& a, const RowMap& rm, 
   store_a(ra[0], 0);
   __syncthreads();
   // weight operands of K step 0
-  f16x8 bv[2][4];
+  f16x8 bv[NJ][4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < NJ; ++j) {
     f16x2 d2, m2;
     scales(0, j, d2, m2);
 #pragma unroll
@@ -360,9 +361,9 @@ __device__ __forceinline__ void qgemm_tile(const GemmArgs& a, const RowMap& rm, 
       const int kl = min(kt + 2, nk - 1), kn = min(kt + 1, nk - 1);
       load_a(kl, ra[p]);
       load_codes(kl, wc[p]);
-      f16x2 dn[2], mn[2];   // scales of the next K step
+      f16x2 dn[NJ], mn[NJ];   // scales of the next K step
 #pragma unroll
-      for (int j = 0; j < 2; ++j) scales(kn, j, dn[j], mn[j]);
+      for (int j = 0; j < NJ; ++j) scales(kn, j, dn[j], mn[j]);
       const uint16_t* Ab = As[p];
       // the next K step's weight operand kk is built while the MFMAs of kk
       // run, in the registers those MFMAs have just read (after the last
@@ -376,10 +377,10 @@ __device__ __forceinline__ void qgemm_tile(const GemmArgs& a, const RowMap& rm, 
 #pragma unroll
         for (int i = 0; i < MT; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
+          for (int j = 0; j < NJ; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j][kk], acc[i][j], 0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) bv[j][kk] = w_operand<FMT>(wc[p ^ 1][j], kk, dn[j], mn[j]);
+        for (int j = 0; j < NJ; ++j) bv[j][kk] = w_operand<FMT>(wc[p ^ 1][j], kk, dn[j], mn[j]);
       }
       store_a(ra[p ^ 1], p ^ 1);
       if (s == kGroup - 2) {
@@ -421,11 +422,11 @@ __device__ __forceinline__ void qgemm_tile(const GemmArgs& a, const RowMap& rm, 
     // to pair_out, 16 bytes per lane, as non-temporal stores (the combine
     // reads them much later; they would only displace weights and tokens
     // from the L2)
-    constexpr int kORow = kBN + 4;   // floats per LDS row
+    constexpr int kORow = kBNt + 4;   // floats per LDS row
     static_assert(32 * kORow * 4 <= int(2 * sizeof(ATile)), "an output slab fits in the A buffers");
     float* ot = reinterpret_cast<float*>(&As[0][0]);
-    float* out = (rm.shared ? a.shared_out : a.pair_out) + nt * kBN;
-    const int ocol = wave * 64 + col;
+    float* out = (rm.shared ? a.shared_out : a.pair_out) + nt * kBNt;
+    const int ocol = wave * 32 * NJ + col;
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
       if (i > 0) __syncthreads();   // the previous slab has been read
@@ -433,12 +434,12 @@ __device__ __forceinline__ void qgemm_tile(const GemmArgs& a, const RowMap& rm, 
       for (int v = 0; v < 16; ++v) {
         const int r = 8 * (v >> 2) + 4 * bh + (v & 3);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) ot[r * kORow + ocol + 32 * j] = acc[i][j][v];
+        for (int j = 0; j < NJ; ++j) ot[r * kORow + ocol + 32 * j] = acc[i][j][v];
       }
       __syncthreads();
 #pragma unroll
-      for (int q = 0; q < 32 / 4; ++q) {
-        const int r = q * 4 + (tid >> 6), c4 = tid & 63;
+      for (int q = 0; q < 32 / (1024 / kBNt); ++q) {
+        const int r = q * (1024 / kBNt) + tid / (kBNt / 4), c4 = tid % (kBNt / 4);
         if (i * 32 + r < rm.rows)
           __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(ot + r * kORow + 4 * c4),
                                       reinterpret_cast<f32x4*>(out + int64_t(orow[i * 32 + r]) * a.H + 4 * c4));
@@ -447,10 +448,10 @@ __device__ __forceinline__ void qgemm_tile(const GemmArgs& a, const RowMap& rm, 
   }
 }
 
-template <int FMT, bool GU>
-__global__ __launch_bounds__(256, 2) void qgemm_kernel(GemmArgs a, int n_ntiles) {
+template <int FMT, bool GU, int NJ>
+__global__ __launch_bounds__(256, NJ == 1 ? 3 : 2) void qgemm_kernel(GemmArgs a, int n_ntiles) {
   __shared__ __align__(16) ATile As[2];
-  __shared__ STable Sd[2];   // d | m << 16 per (weight row, block of the group)
+  __shared__ uint32_t Sd[2 * 128 * NJ * kSdRow];   // d | m << 16 per (weight row, block of the group)
   __shared__ int arow[kQM];
   __shared__ int orow[kQM];  // down: pair_out row of each tile row
   const int w = xcd_item();
@@ -472,13 +473,13 @@ __global__ __launch_bounds__(256, 2) void qgemm_kernel(GemmArgs a, int n_ntiles)
   __syncthreads();
   const int mt = (rm.rows + 31) >> 5;   // wave-uniform
   if (mt >= 4)
-    qgemm_tile<FMT, GU, 4>(a, rm, nt, As, Sd, arow, orow);
+    qgemm_tile<FMT, GU, 4, NJ>(a, rm, nt, As, Sd, arow, orow);
   else if (mt == 3)
-    qgemm_tile<FMT, GU, 3>(a, rm, nt, As, Sd, arow, orow);
+    qgemm_tile<FMT, GU, 3, NJ>(a, rm, nt, As, Sd, arow, orow);
   else if (mt == 2)
-    qgemm_tile<FMT, GU, 2>(a, rm, nt, As, Sd, arow, orow);
+    qgemm_tile<FMT, GU, 2, NJ>(a, rm, nt, As, Sd, arow, orow);
   else
-    qgemm_tile<FMT, GU, 1>(a, rm, nt, As, Sd, arow, orow);
+    qgemm_tile<FMT, GU, 1, NJ>(a, rm, nt, As, Sd, arow, orow);
 }
 
 // MFMA on one K step from LDS (bf16 router): wave tile = (MT x 32 rows) x
@@ -572,11 +573,14 @@ hipError_t launch_gemm_fmt(const GemmArgs& ga, const uint16_t* x, int max_tiles,
   const int64_t n_blocks = int64_t(ga.T) * ga.H / 32;
   hipLaunchKernelGGL(x16_kernel<FMT>, dim3(unsigned((n_blocks + 255) / 256)), dim3(256), 0, st, x,
                      n_blocks, const_cast<uint16_t*>(ga.x16));
-  const int nt_gu = ga.I / 128, nt_d = ga.H / 256;
-  hipLaunchKernelGGL((qgemm_kernel<FMT, true>), dim3(round_xcd(max_tiles * nt_gu)), dim3(256), 0, st,
+  // down tiles of 256 columns (2 MFMA column tiles per wave); 128-column
+  // tiles (1 per wave, 160 registers, three workgroups per CU) measured slower
+  constexpr int kNJD = 2;
+  const int nt_gu = ga.I / 128, nt_d = ga.H / (128 * kNJD);
+  hipLaunchKernelGGL((qgemm_kernel<FMT, true, 2>), dim3(round_xcd(max_tiles * nt_gu)), dim3(256), 0, st,
                      ga, nt_gu);
-  hipLaunchKernelGGL((qgemm_kernel<FMT, false>), dim3(round_xcd(max_tiles * nt_d)), dim3(256), 0, st,
-                     ga, nt_d);
+  hipLaunchKernelGGL((qgemm_kernel<FMT, false, kNJD>), dim3(round_xcd(max_tiles * nt_d)), dim3(256), 0,
+                     st, ga, nt_d);
   return hipGetLastError();
 }
 
