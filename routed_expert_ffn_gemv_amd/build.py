@@ -20,6 +20,10 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-mcode-object-
 
 
 HOST_ONLY = {"host_tier.cpp"}
+# Per-file device flags.  The fused decode layer kernel is built with the
+# ILP-first machine scheduler: measured 19.9 -> 19.0 us per one-token layer,
+# unchanged for four tokens.
+FILE_FLAGS = {"layer.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
 def sources():
@@ -37,7 +41,7 @@ def build(verbose=False):
         # tier, no device pass); other .cpp: host code that calls HIP
         name = os.path.basename(src)
         lang = ["-x", "hip"] if src.endswith(".hip") else (["-x", "c++"] if name in HOST_ONLY else [])
-        cmd = [HIPCC] + FLAGS + lang + ["-c", src, "-o", obj]
+        cmd = [HIPCC] + FLAGS + FILE_FLAGS.get(name, []) + lang + ["-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
