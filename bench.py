@@ -43,25 +43,27 @@ def log(msg):
 # (their SHA-256 below); otherwise traffic is null.
 KERNEL_SOURCES = {
     "decode": ["routed_expert_ffn_gemv_amd/csrc/layer.hip", "routed_expert_ffn_gemv_amd/csrc/layer.h",
-               "routed_expert_ffn_gemv_amd/csrc/gemv_core.h", "routed_expert_ffn_gemv_amd/csrc/common.h"],
+               "routed_expert_ffn_gemv_amd/csrc/gemv_core.h", "routed_expert_ffn_gemv_amd/csrc/common.h",
+               "routed_expert_ffn_gemv_amd/build.py"],
     "prefill": ["routed_expert_ffn_gemv_amd/csrc/ffn_gemm.hip", "routed_expert_ffn_gemv_amd/csrc/resolve.hip",
-                "routed_expert_ffn_gemv_amd/csrc/gemv_core.h", "routed_expert_ffn_gemv_amd/csrc/common.h"],
+                "routed_expert_ffn_gemv_amd/csrc/gemv_core.h", "routed_expert_ffn_gemv_amd/csrc/common.h",
+                "routed_expert_ffn_gemv_amd/build.py"],
 }
 TRAFFIC = {
     # workload: {"sha256": ..., "bytes": fetched + written per launch}
     # c2: the moe_layer kernel (profiles/c2_decode_layer_hbm_traffic.md)
-    "c2_decode_layer_q2": {"sha256": "a09f1cfdb1ce71a73052009e9a2899f7e3a06d92a6b9d6d179ed163407d11d8f",
-                           "bytes": 23112298},
+    "c2_decode_layer_q2": {"sha256": "db5185917d45e81081095f882b301ed45d09b455db45cd31576b6e00926fd23d",
+                           "bytes": 23067169},
     # c3: the moe_layer kernel (profiles/c3_verify_stack_hbm_traffic.md)
-    "c3_verify_stack_q2": {"sha256": "a09f1cfdb1ce71a73052009e9a2899f7e3a06d92a6b9d6d179ed163407d11d8f",
-                           "bytes": 70396353},
+    "c3_verify_stack_q2": {"sha256": "db5185917d45e81081095f882b301ed45d09b455db45cd31576b6e00926fd23d",
+                           "bytes": 70405233},
     # c4: the moe_layer kernel (profiles/c4_slot_tiering_hbm_traffic.md)
-    "c4_slot_tiering_q2": {"sha256": "a09f1cfdb1ce71a73052009e9a2899f7e3a06d92a6b9d6d179ed163407d11d8f",
-                           "bytes": 121756325},
+    "c4_slot_tiering_q2": {"sha256": "db5185917d45e81081095f882b301ed45d09b455db45cd31576b6e00926fd23d",
+                           "bytes": 121783097},
     # c5: the kernels of one moe_expert_ffn call (active list, schedule, x16,
     # gate/up and down GEMMs; profiles/c5_prefill_hbm_traffic.md)
-    "c5_prefill_q4": {"sha256": "d2b2ade25556bef7a72e5aa45d8a11619a3cd512e842d65bc09557add14e60c8",
-                      "bytes": 9042670850},
+    "c5_prefill_q4": {"sha256": "ed4532c0745965cfcfdc61cbd5ad814dc11098223b6c3f4667070ff1b330e8a0",
+                      "bytes": 8957782439},
 }
 
 
