@@ -46,7 +46,7 @@ typedef enum {
   MOE_ERR_INVALID = 1,      /* bad shape, null pointer, misalignment, k > E ... */
   MOE_ERR_UNSUPPORTED = 2,  /* valid but not implemented (format, T too large) */
   MOE_ERR_WORKSPACE = 3,    /* ws_bytes smaller than moe_workspace_size() */
-  MOE_ERR_DEVICE = 4        /* a HIP launch failed (hipGetLastError) */
+  MOE_ERR_DEVICE = 4        /* a HIP call failed, or a fused launch gave up (moe_layer_check) */
 } moe_status;
 
 /* Weight formats.  Q2B32 / Q4B32: blocks of 32 consecutive weights along K
@@ -178,11 +178,44 @@ moe_status moe_combine(const moe_layer_desc* desc, int32_t T, const int32_t* slo
  * device-scope float atomics, so y can differ between runs in the last bits
  * (the gate-weighted terms are added in no fixed order).  A workspace serves one moe_layer call at a time,
  * and the launch sizes its grid to the workgroups the device holds at once,
- * so it must not share the GPU with a kernel that would keep some of them
- * from running.  Other shapes run the separate steps in sequence. */
+ * so it should not share the GPU with a kernel that keeps some of them
+ * from running: every wait of the launch is bounded (moe_set_wait_budget),
+ * and a launch that runs out of it gives up instead of hanging -- see
+ * moe_layer_check.  Other shapes run the separate steps in sequence. */
 moe_status moe_layer(const moe_layer_desc* desc, const uint16_t* x, int32_t T, float* y,
                      int32_t* topk_idx, float* topk_gate, int32_t* slot_idx, moe_miss* miss,
                      int32_t* miss_off, void* ws, size_t ws_bytes, void* stream);
+
+/* Whether the fused moe_layer calls made on workspace ws completed: MOE_OK,
+ * or MOE_ERR_DEVICE when one of them gave up a bounded wait (for example
+ * because another kernel kept some of its workgroups from running for
+ * longer than the budget).  Such a call's outputs are unspecified (it never
+ * accesses memory out of bounds), and every later moe_layer call on the
+ * same workspace returns at once without writing anything, until the caller
+ * zeroes the workspace again.  This call waits for the work queued on
+ * `stream` and reads 8 bytes of ws: a host synchronisation, meant for
+ * checks outside the hot path.  ws NULL or ws_bytes < 256: MOE_ERR_INVALID. */
+moe_status moe_layer_check(const void* ws, size_t ws_bytes, void* stream);
+
+/* Budget of every wait of the fused moe_layer launch, in nanoseconds of the
+ * GPU's real-time counter, counted from each workgroup's start (0 restores
+ * the default of 100 ms).  hold != 0 is a test hook: workgroup 0 of every
+ * later fused launch first waits on a word that nothing writes, so the
+ * launch runs out of its budget, marks its workspace failed, and every
+ * workgroup still exits normally.  Process-wide, read when a call is
+ * issued. */
+void moe_set_wait_budget(uint64_t ns, int32_t hold);
+
+/* Diagnostics: phase stamps of later fused moe_layer launches.  trace is a
+ * device buffer of 16 uint64 words per workgroup of the launch (one per
+ * compute unit; 1024 rows always suffice), or NULL to stop.  Row b holds
+ * workgroup b's real-time counter stamps (100 MHz) at: 0 start, 2 tokens
+ * staged, 3 router/shared tasks of wave 0 done, 4 every logit seen,
+ * 5 routing done, 6 wave 0's gate/up done, 7 the last wave's gate/up done,
+ * 8 first h staged, 9 down done, 10 end; word 1 is the XCD it ran on.
+ * Every launch overwrites the rows it writes.  Process-wide, read when a
+ * call is issued. */
+void moe_set_trace(uint64_t* trace);
 
 /* ---- Adaptive slot table ([MD] section "粗から細へ" and its placement
  * figure: each card fills its expert slots by a usage ranking, and an

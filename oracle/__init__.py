@@ -271,15 +271,17 @@ def layer_from_synth(cfg, layer_id, x, slot_of=None, num_slots=None, tokens=None
     Routing covers every token of x; the FFN and combine cover `tokens`
     (default: all).  Each expert's weights are regenerated by synth on the
     host.  with_misses also returns y_full, where missed experts are added
-    as if they were resident.  route: a result of route_from_synth to reuse."""
+    as if they were resident.  route: a result of route_from_synth to reuse.
+    threads > 1 runs the router rows and the experts' FFN calls in threads;
+    every call is still the single-threaded oracle and each expert's rows
+    land at fixed places, so the result does not depend on the thread
+    count."""
     import synth
     r = dict(route) if route is not None else route_from_synth(cfg, layer_id, x, slot_of,
                                                                 num_slots, threads)
     T = x.shape[0]
     k, H, I = cfg.k, cfg.H, cfg.I
     tokens = np.arange(T) if tokens is None else np.asarray(tokens)
-    sel = np.zeros(T, bool)
-    sel[tokens] = True
     pair_out = np.zeros((T * k, H), np.float64)
     by_expert = {}
     for t in tokens.tolist():
@@ -287,16 +289,29 @@ def layer_from_synth(cfg, layer_id, x, slot_of=None, num_slots=None, tokens=None
             p = t * k + j
             if r["slot_idx"].ravel()[p] >= 0 or with_misses:
                 by_expert.setdefault(int(r["idx"].ravel()[p]), []).append(p)
-    for e, ps in sorted(by_expert.items()):
-        ex = synth.gen_expert(cfg, layer_id, e)
-        toks = np.array([p // k for p in ps])
-        o = ffn(cfg.wfmt, H, I, ex, x[toks])
-        pair_out[np.array(ps)] = o
-    shared = None
+    jobs = [(e, np.array(ps)) for e, ps in sorted(by_expert.items())]
     if cfg.shared:
-        shared = np.zeros((T, H), np.float64)
-        ex = synth.gen_expert(cfg, layer_id, synth.SHARED_ID)
-        shared[tokens] = ffn(cfg.wfmt, H, I, ex, x[tokens])
+        jobs.append((synth.SHARED_ID, None))
+
+    def one(job):
+        e, ps = job
+        ex = synth.gen_expert(cfg, layer_id, e)
+        toks = tokens if ps is None else ps // k
+        return ffn(cfg.wfmt, H, I, ex, x[toks])
+
+    if threads > 1 and len(jobs) > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(min(threads, len(jobs))) as pool:
+            outs = list(pool.map(one, jobs))
+    else:
+        outs = [one(j) for j in jobs]
+    shared = None
+    for (e, ps), o in zip(jobs, outs):
+        if ps is None:
+            shared = np.zeros((T, H), np.float64)
+            shared[tokens] = o
+        else:
+            pair_out[ps] = o
     y = combine(r["slot_idx"], r["gate"], pair_out, shared)
     r["y"] = y
     r["pair_out"] = pair_out

@@ -26,7 +26,8 @@ EXPORTS = ("moe_status_string", "moe_version", "moe_workspace_size", "moe_route"
            "moe_resolve_slots", "moe_expert_ffn", "moe_combine", "moe_layer",
            "moe_slot_refresh_workspace_size", "moe_slot_refresh", "moe_host_miss_ffn",
            "moe_host_isa", "moe_verify_workspace_size", "moe_verify_accept",
-           "moe_prefill_workspace_size", "moe_prefill_layer")
+           "moe_prefill_workspace_size", "moe_prefill_layer", "moe_layer_check",
+           "moe_set_wait_budget", "moe_set_trace")
 MOE_REFRESH_MAX_SWAPS = 1024
 
 
@@ -90,6 +91,12 @@ def _load():
     lib.moe_combine.argtypes = [D, I32, P, P, P, P, P, P]
     lib.moe_layer.restype = I32
     lib.moe_layer.argtypes = [D, P, I32, P, P, P, P, P, P, P, SZ, P]
+    lib.moe_layer_check.restype = I32
+    lib.moe_layer_check.argtypes = [P, SZ, P]
+    lib.moe_set_wait_budget.restype = None
+    lib.moe_set_wait_budget.argtypes = [ctypes.c_uint64, I32]
+    lib.moe_set_trace.restype = None
+    lib.moe_set_trace.argtypes = [P]
     SP = ctypes.POINTER(moe_slot_pool)
     lib.moe_slot_refresh_workspace_size.restype = I32
     lib.moe_slot_refresh_workspace_size.argtypes = [SP, ctypes.POINTER(SZ)]
@@ -229,6 +236,25 @@ def moe_layer(desc, x, T, y, topk_idx, topk_gate, slot_idx, miss, miss_off, ws, 
     _check(lib.moe_layer(desc.ref, _ptr(x), int(T), _ptr(y), _ptr(topk_idx), _ptr(topk_gate),
                          _ptr(slot_idx), _ptr(miss), _ptr(miss_off), _ptr(ws),
                          ws.numel() if ws is not None else 0, _stream(stream)), "moe_layer")
+
+
+def moe_layer_check(ws, stream=None):
+    """Raises MoEError(MOE_ERR_DEVICE) if a fused moe_layer call on ws gave
+    up a bounded wait (waits for the stream)."""
+    _check(lib.moe_layer_check(_ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)),
+           "moe_layer_check")
+
+
+def moe_set_wait_budget(ns=0, hold=False):
+    """Budget of the fused launch's waits in ns (0: the default, 100 ms);
+    hold=True makes later fused launches run out of it (test hook)."""
+    lib.moe_set_wait_budget(int(ns), 1 if hold else 0)
+
+
+def moe_set_trace(trace):
+    """Phase stamps of later fused moe_layer launches into trace (a uint64-
+    sized int64 device tensor of [1024][16] words), or None to stop."""
+    lib.moe_set_trace(_ptr(trace))
 
 
 class SlotPool:

@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "../../include/moe.h"
 #include "kernels.h"
 #include "layer.h"
@@ -23,6 +25,12 @@ constexpr int64_t kMaxT = int64_t(1) << 22;
 constexpr size_t kAlign = 256;
 constexpr int kRouterGemmMinT = 256;       // tokens from which the router runs on MFMA
 constexpr int64_t kFfnGemmMinPairs = 2048; // pairs from which the FFN runs as grouped GEMMs
+
+// Budget of the fused launch's waits (ns; 0 = the default) and the test hold.
+constexpr uint64_t kDefaultWaitNs = 100000000ull;
+std::atomic<uint64_t> g_wait_ns{0};
+std::atomic<int32_t> g_hold{0};
+std::atomic<uint64_t*> g_trace{nullptr};   // phase stamps of the fused launch (diagnostics)
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -222,7 +230,7 @@ moe_status run_ffn(const moe_layer_desc* d, const uint16_t* x, int T, const int3
   hipError_t e = launch_active_from_offsets(d->num_slots, bucket_off, a.act, st);
   if (e == hipSuccess) {
     if (int64_t(T) * d->k >= kFfnGemmMinPairs && ffn_gemm_ok(a.fmt, d->H, d->I) &&
-        planes_16b_aligned(d))
+        ffn_gemm_fits(T, d->k, d->H, d->I) && planes_16b_aligned(d))
       e = launch_ffn_gemm(a, d->num_slots, bucket_off, at<void>(ws, w.h), st);
     else
       e = launch_ffn_gemv(a, st);
@@ -275,6 +283,57 @@ PrefillEvents* prefill_events() {
     e.ok = true;
   }
   return &e;
+}
+
+// Whether moe_layer takes the fused launch for this layer and T.
+bool fused_shape(const moe_layer_desc* d, int T) {
+  const int fmt = d->gate.fmt;
+  return layer_fused_ok(fmt, T, d->k, d->E, d->H, d->I) &&
+         (fmt == MOE_W_F32 || d->router_fmt == MOE_W_BF16);
+}
+
+// Arguments of the fused launch (region: its hand-off region).
+LayerArgs layer_args(const moe_layer_desc* desc, const uint16_t* x, int T, float* y,
+                     int32_t* topk_idx, float* topk_gate, int32_t* slot_idx, moe_miss* miss,
+                     int32_t* miss_off, uint8_t* region) {
+  LayerArgs L;
+  memset(&L, 0, sizeof(L));
+  L.x = x;
+  L.T = T;
+  L.E = desc->E;
+  L.k = desc->k;
+  L.H = desc->H;
+  L.I = desc->I;
+  L.S = desc->num_slots;
+  L.rfmt = desc->router_fmt;
+  L.has_sh = has_shared(desc) ? 1 : 0;
+  L.W = desc->router_w;
+  L.bias = desc->router_bias;
+  L.slot_of = desc->slot_of_expert;
+  const FfnArgs f = ffn_args(desc, x, T);
+  auto planes = [](const MatView& v) { return Planes{v.codes, v.scale, v.mn}; };
+  L.g = planes(f.g);
+  L.u = planes(f.u);
+  L.d = planes(f.d);
+  L.sg = planes(f.sg);
+  L.su = planes(f.su);
+  L.sd = planes(f.sd);
+  L.mat_bytes = f.g.mat_bytes;     // the same for all six: I x H weights each
+  L.mat_blocks = f.g.mat_blocks;
+  L.y = y;
+  L.idx = topk_idx;
+  L.gate = topk_gate;
+  L.slot_idx = slot_idx;
+  L.miss = miss;
+  L.miss_off = miss_off;
+  L.usage = desc->usage_counts;
+  L.region = region;
+  const uint64_t ns = g_wait_ns.load(std::memory_order_relaxed);
+  L.wait_ticks = (ns ? ns : kDefaultWaitNs) / 10;   // the real-time counter runs at 100 MHz
+  if (L.wait_ticks == 0) L.wait_ticks = 1;
+  L.debug_hold = g_hold.load(std::memory_order_relaxed);
+  L.trace = g_trace.load(std::memory_order_relaxed);
+  return L;
 }
 
 }  // namespace
@@ -383,40 +442,9 @@ moe_status moe_layer(const moe_layer_desc* desc, const uint16_t* x, int32_t T, f
   float* pairbuf = at<float>(ws, w.pairbuf);
   float* shbuf = has_shared(desc) ? at<float>(ws, w.sharedbuf) : nullptr;
   const int fmt = desc->gate.fmt;
-  if (layer_fused_ok(fmt, T, desc->k, desc->E, desc->H, desc->I) &&
-      (fmt == MOE_W_F32 || desc->router_fmt == MOE_W_BF16)) {
-    LayerArgs L;
-    memset(&L, 0, sizeof(L));
-    L.x = x;
-    L.T = T;
-    L.E = desc->E;
-    L.k = desc->k;
-    L.H = desc->H;
-    L.I = desc->I;
-    L.S = desc->num_slots;
-    L.rfmt = desc->router_fmt;
-    L.has_sh = has_shared(desc) ? 1 : 0;
-    L.W = desc->router_w;
-    L.bias = desc->router_bias;
-    L.slot_of = desc->slot_of_expert;
-    const FfnArgs f = ffn_args(desc, x, T);
-    auto planes = [](const MatView& v) { return Planes{v.codes, v.scale, v.mn}; };
-    L.g = planes(f.g);
-    L.u = planes(f.u);
-    L.d = planes(f.d);
-    L.sg = planes(f.sg);
-    L.su = planes(f.su);
-    L.sd = planes(f.sd);
-    L.mat_bytes = f.g.mat_bytes;     // the same for all six: I x H weights each
-    L.mat_blocks = f.g.mat_blocks;
-    L.y = y;
-    L.idx = topk_idx;
-    L.gate = topk_gate;
-    L.slot_idx = slot_idx;
-    L.miss = miss;
-    L.miss_off = miss_off;
-    L.usage = desc->usage_counts;
-    L.region = at<uint8_t>(ws, w.layer);
+  if (fused_shape(desc, T)) {
+    const LayerArgs L = layer_args(desc, x, T, y, topk_idx, topk_gate, slot_idx, miss, miss_off,
+                                   at<uint8_t>(ws, w.layer));
     return device_status(launch_layer_fused(L, fmt, st, nullptr));
   }
   int32_t* sl = slot_idx ? slot_idx : at<int32_t>(ws, w.slotbuf);
@@ -437,6 +465,23 @@ moe_status moe_layer(const moe_layer_desc* desc, const uint16_t* x, int32_t T, f
     e = launch_combine(T, desc->k, desc->H, sl, topk_gate, pairbuf, shbuf, y, st);
   return device_status(e);
 }
+
+moe_status moe_layer_check(const void* ws, size_t ws_bytes, void* stream) {
+  if (!ws || !aligned(ws, kAlign) || ws_bytes < 256) return MOE_ERR_INVALID;
+  if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return MOE_ERR_DEVICE;
+  uint32_t err = 0;   // the error word of the hand-off region's header (region at offset 0)
+  if (hipMemcpy(&err, static_cast<const uint8_t*>(ws) + kRegionErr, 4, hipMemcpyDeviceToHost) !=
+      hipSuccess)
+    return MOE_ERR_DEVICE;
+  return err ? MOE_ERR_DEVICE : MOE_OK;
+}
+
+void moe_set_wait_budget(uint64_t ns, int32_t hold) {
+  g_wait_ns.store(ns, std::memory_order_relaxed);
+  g_hold.store(hold, std::memory_order_relaxed);
+}
+
+void moe_set_trace(uint64_t* trace) { g_trace.store(trace, std::memory_order_relaxed); }
 
 moe_status moe_slot_refresh_workspace_size(const moe_slot_pool* pool, size_t* bytes) {
   const moe_status s = check_pool(pool);

@@ -33,6 +33,16 @@
 //    flight indexed by K-step parity: no register copy forces a wait.
 //  - Tiles are ordered so that consecutive tiles of one expert run on the
 //    same XCD and share its weights in that XCD's L2.
+//  - fp16 range: a token row whose largest magnitude lies outside
+//    [2^-6, 2^16) is converted as x * 2^-e, with e chosen so that its largest
+//    magnitude lands in [2^14, 2^15); the gate/up epilogue multiplies that
+//    row's products by 2^e (exact).  Likewise each h row slab of 128
+//    features outside [2^-6, 2^15) is stored as h * 2^-e with its own e; a
+//    small pass brings the slabs of a row to the row's largest e (rescaling
+//    the others in place), and the down epilogue multiplies the row's
+//    outputs by 2^e.  In range every e is 0 and nothing is rescaled; inside
+//    the range every bf16 token value converts to fp16 exactly and h keeps
+//    11 significant bits relative to the slab's largest value.
 #include "gemv_core.h"
 #include "kernels.h"
 
@@ -68,6 +78,18 @@ __host__ __device__ __forceinline__ int perm_pos(int j) {
     const int i = j >> 4, r = j & 3, b = (j >> 2) & 3;
     return 8 * (2 * i + (r >> 1)) + 4 * (r & 1) + b;
   }
+}
+
+// Scale exponent of a row (or row slab) whose largest magnitude is amax:
+// 0 inside [lo, hi), else floor(log2 amax) - 14, which brings the largest
+// magnitude into [2^14, 2^15).  An all-zero slab gets kZeroSlab, which
+// takes no part in the row's common exponent.
+constexpr int kZeroSlab = -128;
+__device__ __forceinline__ int range_exp(float amax, float lo, float hi) {
+  if (amax == 0.f) return kZeroSlab;
+  if (amax >= lo && amax < hi) return 0;
+  const int e = __builtin_amdgcn_frexp_expf(amax) - 1 - 14;   // frexp: amax = m 2^f, m in [0.5, 1)
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
 __device__ __forceinline__ uint32_t f32x2_to_f16x2(float lo, float hi) {
@@ -160,6 +182,13 @@ struct GemmArgs {
   uint16_t* h_sh;           // fp16 [T][I]
   float* pair_out;          // [T*k][H]
   float* shared_out;        // [T][H]
+  // scale exponents (fp16 range): tokens [T]; h row slabs [P + T][I / 128]
+  // and h rows [P + T] (routed rows at their bucket position, the shared
+  // expert's rows at P + token)
+  int8_t* xe;
+  int8_t* he;
+  int8_t* hr;
+  int P;
 };
 
 // Rows of the tile: token (A source row) and output row id.
@@ -187,32 +216,59 @@ __device__ __forceinline__ RowMap row_map(const GemmArgs& a, int2 t, int n_act) 
 }
 
 // ---------------------------------------------------------------- tokens
-// x (bf16) -> x16 (fp16) with K permuted inside each 32-wide block.
+// x (bf16) -> x16 (fp16) with K permuted inside each 32-wide block, one wave
+// per token (H <= 8192: at most 4 blocks of 32 per lane).  xe[t] receives
+// the token's scale exponent (x16 = x * 2^-xe).
 template <int FMT>
-__global__ __launch_bounds__(256) void x16_kernel(const uint16_t* __restrict__ x, int64_t n_blocks,
-                                                  uint16_t* __restrict__ x16) {
-  const int64_t b = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (b >= n_blocks) return;
-  const u32x4* src = reinterpret_cast<const u32x4*>(x + b * 32);
-  uint32_t w[16];
+__global__ __launch_bounds__(256) void x16_kernel(const uint16_t* __restrict__ x, int T, int H,
+                                                  uint16_t* __restrict__ x16,
+                                                  int8_t* __restrict__ xe) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (t >= T) return;
+  const int nb = H / 32;
+  const uint16_t* row = x + int64_t(t) * H;
+  uint32_t w[4][16];
+  uint32_t mbits = 0;   // largest |x| of the lane as bf16 bits (monotonic for finite values)
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const u32x4 v = src[q];
-    w[4 * q] = v[0]; w[4 * q + 1] = v[1]; w[4 * q + 2] = v[2]; w[4 * q + 3] = v[3];
+  for (int j = 0; j < 4; ++j) {
+    const int b = lane + 64 * j;
+    if (b < nb) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(row + b * 32);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x4 v = src[q];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w[j][4 * q + e] = v[e];
+          mbits = max(mbits, max(v[e] & 0x7FFFu, (v[e] >> 16) & 0x7FFFu));
+        }
+      }
+    }
   }
-  uint16_t o[32];
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const uint32_t bits = (w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-    o[perm_pos<FMT>(j)] = __builtin_bit_cast(uint16_t, _Float16(__uint_as_float(bits << 16)));
+  for (int m = 1; m < 64; m <<= 1) mbits = max(mbits, uint32_t(__shfl_xor(int(mbits), m, 64)));
+  int e = range_exp(__uint_as_float(mbits << 16), 0x1p-6f, 0x1p16f);
+  e = e == kZeroSlab ? 0 : e;
+  if (lane == 0) xe[t] = int8_t(e);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int b = lane + 64 * j;
+    if (b >= nb) continue;
+    uint16_t o[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t bits = (w[j][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+      const float f = __uint_as_float(bits << 16);
+      o[perm_pos<FMT>(i)] = __builtin_bit_cast(uint16_t, _Float16(e ? ldexpf(f, -e) : f));
+    }
+    u32x4* dst = reinterpret_cast<u32x4*>(x16 + int64_t(t) * H + b * 32);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      dst[q] = u32x4{uint32_t(o[8 * q]) | (uint32_t(o[8 * q + 1]) << 16),
+                     uint32_t(o[8 * q + 2]) | (uint32_t(o[8 * q + 3]) << 16),
+                     uint32_t(o[8 * q + 4]) | (uint32_t(o[8 * q + 5]) << 16),
+                     uint32_t(o[8 * q + 6]) | (uint32_t(o[8 * q + 7]) << 16)};
   }
-  u32x4* dst = reinterpret_cast<u32x4*>(x16 + b * 32);
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    dst[q] = u32x4{uint32_t(o[8 * q]) | (uint32_t(o[8 * q + 1]) << 16),
-                   uint32_t(o[8 * q + 2]) | (uint32_t(o[8 * q + 3]) << 16),
-                   uint32_t(o[8 * q + 4]) | (uint32_t(o[8 * q + 5]) << 16),
-                   uint32_t(o[8 * q + 6]) | (uint32_t(o[8 * q + 7]) << 16)};
 }
 
 // ---------------------------------------------------------------- GEMM
@@ -229,7 +285,8 @@ typedef uint16_t ATile[kQM * kLdsRow];
 // waves skip the row tiles of a bucket's last, partly filled tile.
 template <int FMT, bool GU, int MT, int NJ>
 __device__ __forceinline__ void qgemm_tile(const GemmArgs& a, const RowMap& rm, int nt, ATile* As,
-                                           uint32_t* Sd0, const int* arow, const int* orow) {
+                                           uint32_t* Sd0, const int* arow, const int* orow,
+                                           const int* rsc, bool scaled) {
   constexpr int kBNt = 128 * NJ;   // weight rows of the tile (32 * NJ per wave)
   auto Sd = [&](int buf) { return Sd0 + buf * (kBNt * kSdRow); };
   constexpr int kCW = FMT == MOE_W_Q4B32 ? 4 : 2;   // code dwords of one block
@@ -400,18 +457,81 @@ __device__ __forceinline__ void qgemm_tile(const GemmArgs& a, const RowMap& rm, 
     uint16_t* ht = &As[0][0];        // the A buffers are free after the last K step
     const int fl = wave * 32 + col;  // feature within the tile
     const int fcol = (fl & ~31) + perm_pos<FMT>(fl & 31);
+    // h of element v of MFMA row tile i (the token's scale undone first)
+    auto h_of = [&](int i, int v) {
+      float ga = acc[i][0][v], ua = acc[i][1][v];
+      if (scaled) {
+        const int sc = rsc[i * 32 + 8 * (v >> 2) + 4 * bh + (v & 3)];
+        ga = ldexpf(ga, sc);
+        ua = ldexpf(ua, sc);
+      }
+      return silu_f32(ga) * ua;
+    };
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = i * 32 + 8 * (v >> 2) + 4 * bh + (v & 3);
-        const float hv = silu_f32(acc[i][0][v]) * acc[i][1][v];
-        ht[row * kHRow + fcol] = __builtin_bit_cast(uint16_t, _Float16(hv));
+        ht[row * kHRow + fcol] = __builtin_bit_cast(uint16_t, _Float16(h_of(i, v)));
       }
     __syncthreads();
+    // Range check of the slab: the 16 threads of a row (one 16-lane DPP row)
+    // take the largest |h| of their pieces as fp16 bits.  Inside [2^-6, 2^15)
+    // for every row of the tile: stored as is, exponent 0.
+    constexpr int kQ = kQM * 16 / 256;
+    bool off = false;
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      const int c = q * 256 + tid, row = c >> 4, ch = c & 15;
+      const u32x4 pc = *reinterpret_cast<const u32x4*>(ht + row * kHRow + ch * 8);
+      uint32_t m = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m = max(m, max(pc[e] & 0x7FFFu, (pc[e] >> 16) & 0x7FFFu));
+      m = max(m, uint32_t(__builtin_amdgcn_mov_dpp(int(m), 0xB1, 0xF, 0xF, true)));
+      m = max(m, uint32_t(__builtin_amdgcn_mov_dpp(int(m), 0x4E, 0xF, 0xF, true)));
+      m = max(m, uint32_t(__builtin_amdgcn_mov_dpp(int(m), 0x141, 0xF, 0xF, true)));
+      m = max(m, uint32_t(__builtin_amdgcn_mov_dpp(int(m), 0x140, 0xF, 0xF, true)));
+      // fp16 bits of 2^-6 and 2^15
+      off = off || (row < rm.rows && (m < 0x2400u || m >= 0x7800u));
+    }
+    const bool slow = __syncthreads_or(off) != 0;
+    int8_t* he = a.he + (int64_t(rm.shared ? a.P + rm.pos0 : rm.pos0)) * (a.I / 128) + nt;
+    if (slow) {
+      // exact per-row maxima of the fp32 h, then each row scaled into range
+      uint32_t* rmax = reinterpret_cast<uint32_t*>(Sd0);   // the scale tables are free too
+      if (tid < kQM) rmax[tid] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          atomicMax(&rmax[i * 32 + 8 * (v >> 2) + 4 * bh + (v & 3)],
+                    __float_as_uint(fabsf(h_of(i, v))));
+      __syncthreads();
+      int* rexp = reinterpret_cast<int*>(rmax) + kQM;
+      if (tid < kQM) {
+        const int e = range_exp(__uint_as_float(rmax[tid]), 0x1p-6f, 0x1p15f);
+        rexp[tid] = e;
+        if (tid < rm.rows) he[int64_t(tid) * (a.I / 128)] = int8_t(e);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = i * 32 + 8 * (v >> 2) + 4 * bh + (v & 3);
+          const int e = rexp[row];
+          const float hv = h_of(i, v);
+          ht[row * kHRow + fcol] =
+              __builtin_bit_cast(uint16_t, _Float16(e == kZeroSlab ? hv : ldexpf(hv, -e)));
+        }
+      __syncthreads();
+    } else if (tid < rm.rows) {
+      he[int64_t(tid) * (a.I / 128)] = 0;
+    }
     uint16_t* out = (rm.shared ? a.h_sh : a.h) + int64_t(rm.pos0) * a.I + nt * 128;
 #pragma unroll
-    for (int q = 0; q < kQM * 16 / 256; ++q) {
+    for (int q = 0; q < kQ; ++q) {
       const int c = q * 256 + tid, row = c >> 4, ch = c & 15;
       if (row < rm.rows)
         *reinterpret_cast<u32x4*>(out + int64_t(row) * a.I + ch * 8) =
@@ -440,12 +560,45 @@ __device__ __forceinline__ void qgemm_tile(const GemmArgs& a, const RowMap& rm, 
 #pragma unroll
       for (int q = 0; q < 32 / (1024 / kBNt); ++q) {
         const int r = q * (1024 / kBNt) + tid / (kBNt / 4), c4 = tid % (kBNt / 4);
-        if (i * 32 + r < rm.rows)
-          __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(ot + r * kORow + 4 * c4),
-                                      reinterpret_cast<f32x4*>(out + int64_t(orow[i * 32 + r]) * a.H + 4 * c4));
+        if (i * 32 + r < rm.rows) {
+          f32x4 o4 = *reinterpret_cast<const f32x4*>(ot + r * kORow + 4 * c4);
+          if (scaled) {   // the h row's scale undone
+            const int e = rsc[i * 32 + r];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) o4[c] = ldexpf(o4[c], e);
+          }
+          __builtin_nontemporal_store(o4, reinterpret_cast<f32x4*>(out + int64_t(orow[i * 32 + r]) * a.H + 4 * c4));
+        }
       }
     }
   }
+}
+
+// Between the two GEMMs: brings the slabs of each h row to one exponent,
+// the largest of the row's slabs (all-zero slabs take no part), rescaling
+// the slabs stored with a smaller one in place by a power of two below 1,
+// and records it in hr.  In range every slab has exponent 0 and the pass
+// only reads the exponents.  One thread per row: routed rows are the bucket
+// positions [0, n_hit), the shared expert's rows P + t.
+__global__ __launch_bounds__(256) void h_range_kernel(GemmArgs a, int has_sh) {
+  const int64_t r = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const bool shared = r >= a.P;
+  if (shared ? (!has_sh || r >= int64_t(a.P) + a.T) : r >= a.act.start[*a.act.count]) return;
+  const int ns = a.I / 128;
+  const int8_t* e = a.he + r * ns;
+  int emax = kZeroSlab;
+  for (int s = 0; s < ns; ++s) emax = max(emax, int(e[s]));
+  if (emax == kZeroSlab) emax = 0;
+  uint16_t* h = shared ? a.h_sh + (r - a.P) * a.I : a.h + r * a.I;
+  for (int s = 0; s < ns; ++s) {
+    const int es = e[s];
+    if (es == kZeroSlab || es == emax) continue;
+    for (int i = s * 128; i < (s + 1) * 128; ++i) {
+      const float f = float(__builtin_bit_cast(_Float16, h[i]));
+      h[i] = __builtin_bit_cast(uint16_t, _Float16(ldexpf(f, es - emax)));
+    }
+  }
+  a.hr[r] = int8_t(emax);
 }
 
 template <int FMT, bool GU, int NJ>
@@ -454,6 +607,7 @@ __global__ __launch_bounds__(256, NJ == 1 ? 3 : 2) void qgemm_kernel(GemmArgs a,
   __shared__ uint32_t Sd[2 * 128 * NJ * kSdRow];   // d | m << 16 per (weight row, block of the group)
   __shared__ int arow[kQM];
   __shared__ int orow[kQM];  // down: pair_out row of each tile row
+  __shared__ int rsc[kQM];   // scale exponent of each tile row (gate/up: token; down: h row)
   const int w = xcd_item();
   const int total = *a.n_tiles * n_ntiles;
   if (w >= total) return;
@@ -464,22 +618,26 @@ __global__ __launch_bounds__(256, NJ == 1 ? 3 : 2) void qgemm_kernel(GemmArgs a,
   const int tid = threadIdx.x;
   // A source rows: gate/up gathers token rows of x16; down reads h rows at
   // the bucket positions.  Rows past the bucket read row 0 of the tile.
+  int sc = 0;
   if (tid < kQM) {
     const int r = tid < rm.rows ? tid : 0;
     const int p = rm.shared ? rm.pos0 + r : a.bucket_pair[rm.pos0 + r];
     arow[tid] = GU ? (rm.shared ? p : p / a.k) : rm.pos0 + r;
     orow[tid] = p;
+    sc = GU ? int(a.xe[rm.shared ? p : p / a.k])
+            : int(a.hr[rm.shared ? a.P + rm.pos0 + r : rm.pos0 + r]);
+    rsc[tid] = sc;
   }
-  __syncthreads();
+  const bool scaled = __syncthreads_or(sc != 0) != 0;
   const int mt = (rm.rows + 31) >> 5;   // wave-uniform
   if (mt >= 4)
-    qgemm_tile<FMT, GU, 4, NJ>(a, rm, nt, As, Sd, arow, orow);
+    qgemm_tile<FMT, GU, 4, NJ>(a, rm, nt, As, Sd, arow, orow, rsc, scaled);
   else if (mt == 3)
-    qgemm_tile<FMT, GU, 3, NJ>(a, rm, nt, As, Sd, arow, orow);
+    qgemm_tile<FMT, GU, 3, NJ>(a, rm, nt, As, Sd, arow, orow, rsc, scaled);
   else if (mt == 2)
-    qgemm_tile<FMT, GU, 2, NJ>(a, rm, nt, As, Sd, arow, orow);
+    qgemm_tile<FMT, GU, 2, NJ>(a, rm, nt, As, Sd, arow, orow, rsc, scaled);
   else
-    qgemm_tile<FMT, GU, 1, NJ>(a, rm, nt, As, Sd, arow, orow);
+    qgemm_tile<FMT, GU, 1, NJ>(a, rm, nt, As, Sd, arow, orow, rsc, scaled);
 }
 
 // MFMA on one K step from LDS (bf16 router): wave tile = (MT x 32 rows) x
@@ -569,16 +727,18 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
 }
 
 template <int FMT>
-hipError_t launch_gemm_fmt(const GemmArgs& ga, const uint16_t* x, int max_tiles, hipStream_t st) {
-  const int64_t n_blocks = int64_t(ga.T) * ga.H / 32;
-  hipLaunchKernelGGL(x16_kernel<FMT>, dim3(unsigned((n_blocks + 255) / 256)), dim3(256), 0, st, x,
-                     n_blocks, const_cast<uint16_t*>(ga.x16));
+hipError_t launch_gemm_fmt(const GemmArgs& ga, const uint16_t* x, int max_tiles, int has_sh,
+                           hipStream_t st) {
+  hipLaunchKernelGGL(x16_kernel<FMT>, dim3(unsigned((ga.T + 3) / 4)), dim3(256), 0, st, x, ga.T,
+                     ga.H, const_cast<uint16_t*>(ga.x16), ga.xe);
   // down tiles of 256 columns (2 MFMA column tiles per wave); 128-column
   // tiles (1 per wave, 160 registers, three workgroups per CU) measured slower
   constexpr int kNJD = 2;
   const int nt_gu = ga.I / 128, nt_d = ga.H / (128 * kNJD);
   hipLaunchKernelGGL((qgemm_kernel<FMT, true, 2>), dim3(round_xcd(max_tiles * nt_gu)), dim3(256), 0, st,
                      ga, nt_gu);
+  const int64_t rows = int64_t(ga.P) + ga.T;
+  hipLaunchKernelGGL(h_range_kernel, dim3(unsigned((rows + 255) / 256)), dim3(256), 0, st, ga, has_sh);
   hipLaunchKernelGGL((qgemm_kernel<FMT, false, kNJD>), dim3(round_xcd(max_tiles * nt_d)), dim3(256), 0,
                      st, ga, nt_d);
   return hipGetLastError();
@@ -589,15 +749,40 @@ int gemm_max_tiles(int T, int k, int S) {
   return int(P / kQM + (P < S ? P : S) + T / kQM + 2);
 }
 
+// Workspace: tile list, fp16 h (bucket positions, then the shared expert's
+// rows), fp16 tokens, then the scale exponents: tokens, h row slabs, h rows.
+struct GemmWs {
+  size_t tiles, h, x16, xe, he, hr, total;
+};
+GemmWs gemm_ws(int T, int k, int H, int I, int S) {
+  auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  const int64_t P = int64_t(T) * k;
+  GemmWs w;
+  size_t o = 0;
+  w.tiles = o;
+  o += up(size_t(gemm_max_tiles(T, k, S)) * 8 + 8);
+  w.h = o;
+  o += up(size_t(P + T) * I * 2);
+  w.x16 = o;
+  o += up(size_t(T) * H * 2);
+  w.xe = o;
+  o += up(size_t(T));
+  w.he = o;
+  o += up(size_t(P + T) * (I / 128));
+  w.hr = o;
+  o += up(size_t(P + T));
+  w.total = o;
+  return w;
+}
 }  // namespace
 
-// Workspace: tile list, fp16 h (bucket positions, then the shared expert's
-// rows), fp16 tokens.
-size_t ffn_gemm_ws(int T, int k, int H, int I, int S) {
+size_t ffn_gemm_ws(int T, int k, int H, int I, int S) { return gemm_ws(T, k, H, I, S).total; }
+
+// The tile offsets are 32-bit: token rows T * H and h rows (T * k + T) * I
+// stay below 2^31 elements.
+bool ffn_gemm_fits(int T, int k, int H, int I) {
   const int64_t P = int64_t(T) * k;
-  const size_t tiles = (size_t(gemm_max_tiles(T, k, S)) * 8 + 8 + 255) / 256 * 256;
-  const size_t h = (size_t(P + T) * I * 2 + 255) / 256 * 256;
-  return tiles + h + size_t(T) * H * 2;
+  return int64_t(T) * H < (int64_t(1) << 31) && (P + T) * I < (int64_t(1) << 31);
 }
 
 // K of both GEMMs a multiple of 256 (whole groups of 8 scale blocks); the
@@ -611,13 +796,17 @@ hipError_t launch_ffn_gemm(const FfnArgs& f, int S, const int32_t* bucket_off, v
   (void)bucket_off;
   const int64_t P = int64_t(f.T) * f.k;
   const int max_tiles = gemm_max_tiles(f.T, f.k, S);
+  const GemmWs w = gemm_ws(f.T, f.k, f.H, f.I, S);
   uint8_t* base = static_cast<uint8_t*>(ws);
-  int* n_tiles = reinterpret_cast<int*>(base);
-  int2* tiles = reinterpret_cast<int2*>(base + 8);
-  const size_t off = (size_t(max_tiles) * 8 + 8 + 255) / 256 * 256;
-  uint16_t* h = reinterpret_cast<uint16_t*>(base + off);
-  uint16_t* x16 = reinterpret_cast<uint16_t*>(base + off + (size_t(P + f.T) * f.I * 2 + 255) / 256 * 256);
+  int* n_tiles = reinterpret_cast<int*>(base + w.tiles);
+  int2* tiles = reinterpret_cast<int2*>(base + w.tiles + 8);
+  uint16_t* h = reinterpret_cast<uint16_t*>(base + w.h);
+  uint16_t* x16 = reinterpret_cast<uint16_t*>(base + w.x16);
   GemmArgs ga;
+  ga.xe = reinterpret_cast<int8_t*>(base + w.xe);
+  ga.he = reinterpret_cast<int8_t*>(base + w.he);
+  ga.hr = reinterpret_cast<int8_t*>(base + w.hr);
+  ga.P = int(P);
   ga.x16 = x16;
   ga.T = f.T;
   ga.k = f.k;
@@ -637,8 +826,8 @@ hipError_t launch_ffn_gemm(const FfnArgs& f, int S, const int32_t* bucket_off, v
   hipLaunchKernelGGL(gemm_schedule_kernel, dim3(1), dim3(1024), 0, st, f.act, f.T, has_sh, tiles,
                      n_tiles);
   switch (f.fmt) {
-    case MOE_W_Q4B32: return launch_gemm_fmt<MOE_W_Q4B32>(ga, f.x, max_tiles, st);
-    case MOE_W_Q2B32: return launch_gemm_fmt<MOE_W_Q2B32>(ga, f.x, max_tiles, st);
+    case MOE_W_Q4B32: return launch_gemm_fmt<MOE_W_Q4B32>(ga, f.x, max_tiles, has_sh, st);
+    case MOE_W_Q2B32: return launch_gemm_fmt<MOE_W_Q2B32>(ga, f.x, max_tiles, has_sh, st);
     default: return hipErrorInvalidValue;
   }
 }

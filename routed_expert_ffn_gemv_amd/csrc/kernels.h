@@ -85,6 +85,7 @@ hipError_t launch_ffn_gemv(const FfnArgs& a, hipStream_t st);
 // expert FFN (prefill grouped GEMM, fp16 MFMA)
 size_t ffn_gemm_ws(int T, int k, int H, int I, int S);
 bool ffn_gemm_ok(int fmt, int H, int I);
+bool ffn_gemm_fits(int T, int k, int H, int I);
 hipError_t launch_ffn_gemm(const FfnArgs& a, int S, const int32_t* bucket_off, void* ws,
                            hipStream_t st);
 

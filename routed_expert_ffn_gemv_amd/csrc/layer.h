@@ -12,7 +12,10 @@ namespace moe {
 // call number}: a workgroup publishes a value together with the number of
 // the call that made it in one store, and a reader knows the value is
 // current when the number matches -- no separate flag, no reset.
-//   [0, 256)           call counter (uint32)
+//   [0, 256)           header: call counter (uint32, byte 0), error word
+//                      (uint32, byte 4: nonzero once a call gave up a
+//                      bounded wait), a word nothing writes (byte 128: the
+//                      test hook's wait)
 //   arrive [1024]      one tagged word per workgroup
 //   logits [16][E]     tagged router logits
 //   h      [hrows][I]  tagged SwiGLU activations: pairs first, then the
@@ -57,7 +60,31 @@ struct LayerArgs {
   int32_t* miss_off;
   uint32_t* usage;         // [E] choice counts (may be null)
   uint8_t* region;         // hand-off region (layout above)
+  uint64_t wait_ticks;     // budget of every wait, in ticks of the 100 MHz real-time counter
+  int debug_hold;          // test hook: workgroup 0 first waits on a word nothing writes
+  uint64_t* trace;         // phase stamps [grid][kTraceSlots] (null: off)
 };
+
+// Phase stamps of the fused launch (real-time counter ticks, 100 MHz), one
+// row per workgroup, written by its thread 0 when LayerArgs.trace is set.
+enum TraceSlot {
+  kTrStart = 0,        // workgroup start
+  kTrXcd = 1,          // the XCD it runs on (hardware register, not a time)
+  kTrStaged = 2,       // tokens staged (first barrier)
+  kTrTasksA = 3,       // wave 0's router / shared-expert tasks done
+  kTrLogits = 4,       // every logit seen
+  kTrRouted = 5,       // routing and resolution done
+  kTrGateUp0 = 6,      // wave 0's gate/up tasks done
+  kTrGateUpAll = 7,    // the workgroup's last wave's gate/up tasks done
+  kTrStagedH = 8,      // the first down unit's h staged
+  kTrDown = 9,         // the workgroup's down units done
+  kTrEnd = 10,         // end (workgroup 0: after the arrival check)
+  kTraceSlots = 16
+};
+
+// Byte offsets in the region header.
+constexpr int kRegionErr = 4;
+constexpr int kRegionHold = 128;
 
 bool layer_fused_ok(int fmt, int T, int k, int E, int H, int I);
 size_t layer_fused_lds(int fmt, int T, int E, int H, int I);

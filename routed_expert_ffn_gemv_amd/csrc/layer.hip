@@ -19,7 +19,8 @@
 // workgroups costs one round trip:
 //  A  each wave issues the loads of its first task (router rows, or
 //     shared-expert gate/up rows: neither depends on the routing) before the
-//     tokens are staged in LDS; router waves zero their share of y first.
+//     tokens are staged in LDS; router waves zero their share of y before
+//     they publish their logits.
 //     Logits and shared h are published as tagged words (below);
 //  B  every workgroup polls all logits (and one arrival word per
 //     workgroup) until they carry this call's number, then takes the
@@ -40,6 +41,12 @@
 // which bypasses the per-XCD L2 caches.  The grid never exceeds the
 // workgroups the device holds at once, so every producer a poll waits for
 // is running, and no producer waits on anything.
+// Every wait is bounded: a workgroup that has polled for longer than the
+// budget since its start (another kernel holding some CUs would keep
+// producers from running) marks the call failed in the region header and
+// goes on without the data; the call's outputs are then unspecified (every
+// access still stays in bounds), and later calls on the workspace return at
+// once until the caller zeroes it again (moe_layer_check reports it).
 #include "gemv_core.h"
 #include "kernels.h"
 #include "layer.h"
@@ -112,6 +119,9 @@ __device__ __forceinline__ void wait_mem() { __builtin_amdgcn_s_waitcnt(0); }
 // Parts of the hand-off region.
 __device__ __forceinline__ uint32_t* region_calls(const LayerArgs& a) {
   return reinterpret_cast<uint32_t*>(a.region);
+}
+__device__ __forceinline__ uint32_t* region_err(const LayerArgs& a) {
+  return reinterpret_cast<uint32_t*>(a.region + kRegionErr);
 }
 __device__ __forceinline__ uint64_t* region_arrive(const LayerArgs& a) {
   return reinterpret_cast<uint64_t*>(a.region + 256);
@@ -273,7 +283,29 @@ struct Lds {
   int dstart[2];            // this workgroup's down unit range
   int n_act;
   uint32_t calls;
+  int failed;               // 1: this workgroup gave up a wait; 2: the workspace was poisoned
+  unsigned long long t_gu;  // trace: latest gate/up end over the waves
 };
+
+// Phase stamp (thread 0 of the workgroup; nothing when tracing is off).
+__device__ __forceinline__ void stamp(uint64_t* trace, int slot, uint64_t v) {
+  if (trace && threadIdx.x == 0) trace[blockIdx.x * kTraceSlots + slot] = v;
+}
+__device__ __forceinline__ void stamp_now(uint64_t* trace, int slot) {
+  if (trace) stamp(trace, slot, __builtin_amdgcn_s_memrealtime());
+}
+
+// Bounded waits.  Returns true while a poll may go on.  Once the launch has
+// run for the budget (t0: the thread's start time), or another thread of
+// the workgroup has given up, it returns false; the first to give up marks
+// the workgroup and the call (error word) failed.
+__device__ __forceinline__ bool keep_waiting(const LayerArgs& a, Lds& L, uint64_t t0) {
+  if (*reinterpret_cast<volatile int*>(&L.failed)) return false;
+  if (__builtin_amdgcn_s_memrealtime() - t0 < a.wait_ticks) return true;
+  *reinterpret_cast<volatile int*>(&L.failed) = 1;
+  st_dev(region_err(a), L.calls + 1u);
+  return false;
+}
 
 // --------------------------------------------------------------- staging
 // Tokens into the expert format's LDS layout, with 32-byte loads per
@@ -365,7 +397,7 @@ __device__ __forceinline__ void token_block_sums(int T, int H, float* xsum, cons
 template <int FMT>
 __device__ __forceinline__ void stage_h(const uint64_t* const* srcs, int n, int K, uint32_t* xd,
                                         float* sd, float* psum, float* bsc, int vs,
-                                        uint32_t epoch) {
+                                        uint32_t epoch, const LayerArgs& a, Lds& L, uint64_t t0) {
   const int per_vec = K / 16;
   const int n_items = n * per_vec;
   constexpr int kIt = 2;   // items per thread and batch
@@ -381,13 +413,15 @@ __device__ __forceinline__ void stage_h(const uint64_t* const* srcs, int n, int 
         for (int c = 0; c < 16; ++c) wv[r][c] = ld_dev(src[r] + c);
       }
     }
-    for (;;) {
+    auto all_here = [&]() {
       bool ok = true;
 #pragma unroll
       for (int r = 0; r < kIt; ++r)
 #pragma unroll
         for (int c = 0; c < 16; ++c) ok = ok && (!src[r] || tag_ok(wv[r][c], epoch));
-      if (ok) break;
+      return ok;
+    };
+    while (!all_here() && keep_waiting(a, L, t0)) {
       __builtin_amdgcn_s_sleep(1);
 #pragma unroll
       for (int r = 0; r < kIt; ++r)
@@ -845,15 +879,23 @@ struct RouterRegs {
   float bias;
 };
 
-// Router task = (row group rg of 64 / lpr rows, token group).  Issues the
-// task's loads: zeroes its share of y (every router task has one; they
-// cover y), then loads this lane's router chunk and bias.
-template <int FMT>
-__device__ __forceinline__ void router_load(RouterRegs<FMT>& R, const LayerArgs& a, int task,
-                                            int rg, int n_router, int lane) {
+// Every router task zeroes its share of y (they cover y) before it
+// publishes its logits: a workgroup adds into y only after it has seen
+// every logit.
+__device__ __forceinline__ void zero_y_share(const LayerArgs& a, int task, int n_router,
+                                             int lane) {
   const int TH = a.T * a.H, per = (TH + n_router - 1) / n_router;
   const int y0 = task * per, y1 = min(y0 + per, TH);
   for (int i = y0 + lane; i < y1; i += 64) st_dev(a.y + i, 0.f);
+}
+
+// Router task = (row group rg of 64 / lpr rows, token group).  Issues the
+// task's loads: this lane's router chunk and bias.
+template <int FMT>
+__device__ __forceinline__ void router_load(RouterRegs<FMT>& R, const LayerArgs& a, int task,
+                                            int rg, int n_router, int lane) {
+  (void)task;
+  (void)n_router;
   const int lpr = router_lpr<FMT>(a.H);
   const int e = rg * (64 / lpr) + lane / lpr;
   if constexpr (FMT != MOE_W_F32) {
@@ -1174,7 +1216,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 // per-wave selection instead.  lg receives the logits.  Only wave 0 of a
 // writer workgroup stores the outputs.
 __device__ __forceinline__ void route_token(const LayerArgs& a, float* lg, int E, int k, Lds& L,
-                                            uint32_t epoch, bool writer) {
+                                            uint32_t epoch, bool writer, uint64_t t0) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int kR = kEMax / kThreads;
   uint64_t w[kR];
@@ -1185,13 +1227,14 @@ __device__ __forceinline__ void route_token(const LayerArgs& a, float* lg, int E
     bool ok = true;
 #pragma unroll
     for (int r = 0; r < kR; ++r) ok = ok && (tid + r * kThreads >= E || tag_ok(w[r], epoch));
-    if (ok) break;
+    if (ok || !keep_waiting(a, L, t0)) break;
     __builtin_amdgcn_s_sleep(1);
 #pragma unroll
     for (int r = 0; r < kR; ++r)
       if (tid + r * kThreads < E && !tag_ok(w[r], epoch))
         w[r] = ld_dev(region_lg(a) + tid + r * kThreads);
   }
+  stamp_now(a.trace, kTrLogits);
   uint64_t key[kR];   // 0: no expert
   uint32_t m = 0u;    // largest logit bits of the thread
 #pragma unroll
@@ -1395,8 +1438,15 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   float* psum = xsum + T * (K / 32);
   float* lg = psum + T * (K / 16);
 
-  // ---- A: loads first (call counter, slot table, first task's rows)
-  const uint32_t calls = tid == 0 ? ld_dev(region_calls(ka)) : 0u;
+  // ---- A: loads first (call counter and error word, slot table, first task's rows)
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();   // start of this workgroup's waits
+  if (ka.trace) {
+    uint32_t xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    stamp(ka.trace, kTrStart, t0);
+    stamp(ka.trace, kTrXcd, xcc & 0xFu);
+  }
+  const uint64_t hdr = tid == 0 ? ld_dev(reinterpret_cast<const uint64_t*>(ka.region)) : 0ull;
   int so[kEMax / kThreads];
 #pragma unroll
   for (int r = 0; r < kEMax / kThreads; ++r) {
@@ -1424,20 +1474,32 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     gateup_load<FMT>(rg, ru, ka, ka.sg, ka.su, 0,
                      ((task0 - n_router) % n_srb) * kRowsGU + lane / kLprGU, lane_gu);
   stage_tokens<FMT>(ka.x, T, K, xs, psum, vstride);
-  if (tid == 0) L.calls = calls;
+  if (tid == 0) {
+    L.calls = uint32_t(hdr);
+    L.failed = uint32_t(hdr >> 32) != 0u ? 2 : 0;   // a failed call left the workspace poisoned
+  }
   for (int e = tid; e < kEMax; e += kThreads) L.emask[e] = 0u;
   if (tid < kTMax) L.ncand[tid] = 0;
 #pragma unroll
   for (int r = 0; r < kEMax / kThreads; ++r)
     if (tid + r * kThreads < E) L.slot_of[tid + r * kThreads] = so[r];
   __syncthreads();
+  if (L.failed == 2) return;   // every thread: nothing is written
   const LayerArgs& a = sa;
+  stamp_now(a.trace, kTrStaged);
+  if (tid == 0) L.t_gu = 0ull;
   token_block_sums(T, K, xsum, psum);
   __syncthreads();
   const uint32_t epoch = L.calls + 1u;   // this call's number
+  if (a.debug_hold && b == 0 && tid == 0) {
+    // test hook: wait for a word nothing writes until the budget is spent
+    const uint32_t* hold = reinterpret_cast<const uint32_t*>(a.region + kRegionHold);
+    while (ld_dev(hold) != epoch && keep_waiting(a, L, t0)) __builtin_amdgcn_s_sleep(1);
+  }
   for (int task = task0; task < n_a; task += kWaves * G) {
     if (task < n_router) {
       if (task != task0) router_load<FMT>(rr, a, task, task % n_rg, n_router, lane);
+      zero_y_share(a, task, n_router, lane);   // after the workspace check, before the logits
       router_compute<FMT, kTG>(rr, a, task % n_rg, (task / n_rg) * kTG, xs, vstride, lane, epoch);
     } else {
       const int s = task - n_router, t0 = (s / n_srb) * kTG;
@@ -1448,13 +1510,14 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     }
   }
 
+  stamp_now(a.trace, kTrTasksA);
   // this workgroup has read the counter (workgroup 0 checks before it
   // advances the counter)
   if (tid == 0) st_dev(region_arrive(a) + b, tag_word(0.f, epoch));
 
   // ---- B: every logit of this call, then routing
   if constexpr (TB == 1) {
-    route_token(a, lg, E, k, L, epoch, b == 0);
+    route_token(a, lg, E, k, L, epoch, b == 0, t0);
   } else {
     const int n_lg = T * E;
     constexpr int kR = TB * kEMax / kThreads > 16 ? 16 : TB * kEMax / kThreads;
@@ -1472,7 +1535,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
           const int i = base + r * kThreads + tid;
           ok = ok && (i >= n_lg || tag_ok(w[r], epoch));
         }
-        if (ok) break;
+        if (ok || !keep_waiting(a, L, t0)) break;
         __builtin_amdgcn_s_sleep(1);
 #pragma unroll
         for (int r = 0; r < kR; ++r) {
@@ -1486,6 +1549,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
         if (i < n_lg) lg[i] = tag_val(w[r]);
       }
     }
+  stamp_now(a.trace, kTrLogits);
   __syncthreads();
   const bool thresh = k <= kTopkListMax;
   if (thresh) topk_threshold<TB>(lg, T, E, k, L);
@@ -1522,6 +1586,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   resolve_multi(a, L, P, b == 0);   // T >= 2 here
   __syncthreads();
   }
+  stamp_now(a.trace, kTrRouted);
   const int n_act = L.n_act;
   if (b == 0 && a.usage && tid < P)
     __hip_atomic_fetch_add(gmem_w(a.usage + L.idx[tid]), 1u, __ATOMIC_RELAXED,
@@ -1689,6 +1754,11 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     }
   }
 
+  if (a.trace) {   // this wave's gate/up end
+    const uint64_t t = __builtin_amdgcn_s_memrealtime();
+    if (lane == 0) atomicMax(&L.t_gu, static_cast<unsigned long long>(t));
+    if (wave == 0) stamp(a.trace, kTrGateUp0, t);
+  }
   // ---- D: down units (expert or shared, block of rows), y += gate * D h
   {
     uint32_t* xd = smem;                                    // reuses the token area
@@ -1717,8 +1787,12 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
           srcs[tid] = shared ? region_h_sh(a) + int64_t(tid) * Kd
                              : region_h(a) + int64_t(L.bpair[st + tid]) * Kd;
         __syncthreads();
-        stage_h<FMT>(srcs, n, Kd, xd, sd, pd, bsc, vs_d, epoch);
+        stage_h<FMT>(srcs, n, Kd, xd, sd, pd, bsc, vs_d, epoch, a, L, t0);
         __syncthreads();
+        if (staged < 0 && a.trace) {
+          stamp(a.trace, kTrStagedH, __builtin_amdgcn_s_memrealtime());
+          stamp(a.trace, kTrGateUpAll, L.t_gu);
+        }
         staged = u;
       }
       for (int v0 = 0; v0 < n; v0 += kNG) {
@@ -1748,16 +1822,19 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
       rd = nd;
     }
   }
-  // Workgroup 0 advances the call counter once every workgroup has read it.
+  stamp_now(a.trace, kTrDown);
+  // Workgroup 0 advances the call counter once every workgroup has read it
+  // (a failed call leaves it: the workspace is poisoned anyway).
   if (b == 0) {
     if (tid < G)
-      while (!tag_ok(arr, epoch)) {
+      while (!tag_ok(arr, epoch) && keep_waiting(a, L, t0)) {
         __builtin_amdgcn_s_sleep(1);
         arr = ld_dev(region_arrive(a) + tid);
       }
     __syncthreads();
-    if (tid == 0) st_dev(region_calls(a), epoch);
+    if (tid == 0 && !L.failed) st_dev(region_calls(a), epoch);
   }
+  stamp_now(a.trace, kTrEnd);
   asm volatile("" ::"v"(pf));   // the prefetch's value counts as used
 }
 

@@ -2,6 +2,7 @@
 the synthetic generator, call the library through its C ABI, compare with
 the oracle."""
 
+import os
 import sys
 
 import numpy as np
@@ -10,6 +11,8 @@ import oracle
 import synth
 
 TOL = 2e-3   # max relative error of floating outputs (normwise per token row)
+# threads for the oracle's per-expert calls (each call single-threaded)
+ORACLE_THREADS = min(16, os.cpu_count() or 1)
 
 
 def say(msg):

@@ -9,8 +9,8 @@ import pytest
 
 import oracle
 import synth
-from helpers import (TOL, DeviceLayer, check_routing, host, rowwise_rel_err, say,
-                     small_cfg)
+from helpers import (ORACLE_THREADS, TOL, DeviceLayer, check_routing, host,
+                     rowwise_rel_err, say, small_cfg)
 
 pytestmark = pytest.mark.gpu
 
@@ -236,6 +236,50 @@ def test_c2_decode_layer():
         assert err <= TOL
 
 
+WAIT_CASES = {"c2_T1": synth.CONFIGS["c2"],
+              "q2_T9": small_cfg(E=96, k=6, H=1024, I=256, T=9, bias="zipf", seed=83)}
+
+
+@pytest.mark.parametrize("name", list(WAIT_CASES))
+def test_fused_wait_gives_up_and_poisons_workspace(name):
+    """The fused launch's waits are bounded.  With the test hold set,
+    workgroup 0 first waits on a word nothing writes: the launch gives up
+    after its budget (1 ms here) instead of hanging, every workgroup exits,
+    and moe_layer_check reports MOE_ERR_DEVICE.  Later calls on the
+    poisoned workspace write nothing; once the workspace is zeroed again,
+    calls match the oracle."""
+    import torch
+    import routed_expert_ffn_gemv_amd as moe
+    cfg = WAIT_CASES[name]
+    say(f"[gpu] bounded waits ({name}): forced give-up, poisoned workspace, recovery")
+    x, _ = oracle.margin_x(cfg, 0)
+    L = DeviceLayer(cfg, 0, x=x)
+    ref = L.oracle()
+    ws = moe.workspace(L.desc, cfg.T)
+    o = L.run_layer(ws)
+    moe.moe_layer_check(ws)
+    check_routing(o, ref, cfg.k)
+    try:
+        moe.moe_set_wait_budget(1_000_000, hold=True)
+        L.run_layer(ws)
+        torch.cuda.synchronize()
+    finally:
+        moe.moe_set_wait_budget(0, hold=False)
+    with pytest.raises(moe.MoEError) as err:
+        moe.moe_layer_check(ws)
+    assert err.value.status == moe.MOE_ERR_DEVICE
+    o = L.run_layer(ws)
+    torch.cuda.synchronize()
+    assert torch.isnan(o["y"]).all() and bool((o["idx"] == -7).all())
+    with pytest.raises(moe.MoEError):
+        moe.moe_layer_check(ws)
+    ws.zero_()
+    o = L.run_layer(ws)
+    moe.moe_layer_check(ws)
+    check_routing(o, ref, cfg.k)
+    assert rowwise_rel_err(host(o["y"]), ref["y"]) <= TOL
+
+
 def test_repeated_calls_share_one_workspace():
     """Back-to-back fused calls on one workspace (counters and flag are
     reused across calls), alternating layers and token counts."""
@@ -255,44 +299,100 @@ def test_repeated_calls_share_one_workspace():
             assert rowwise_rel_err(host(o["y"]), refs[l]["y"]) <= TOL
 
 
-def test_c3_verify_stack_sampled_layers():
-    """4-token verify batch through full-size layers of the 48-layer stack
-    (Zipf-biased routing, all experts resident); moe_layer as bench.py
-    times it."""
+def _float_layers(cfg, must, n=8, seed=7):
+    """n layers for the float checks: the ones named in `must` plus seeded
+    picks from the rest."""
+    rest = [l for l in range(cfg.layers) if l not in must]
+    pick = np.random.default_rng(seed).choice(rest, n - len(must), replace=False)
+    return sorted(set(must) | set(int(v) for v in pick))
+
+
+def test_c3_verify_stack_all_layers():
+    """4-token verify batch through all 48 full-size layers of the stack
+    (Zipf-biased routing, all experts resident), moe_layer as bench.py times
+    it: every layer's indices, slots and miss lists bit-exact and gates within
+    tolerance; y of 8 layers (the first and the last among them) within
+    tolerance."""
     cfg = synth.CONFIGS["c3"]
-    for layer in (0, 23, 47):
-        say(f"[gpu] c3 layer {layer}: E=512 k=10 T=4 q2 zipf")
+    floats = _float_layers(cfg, [0, cfg.layers - 1])
+    say(f"[gpu] c3 stack: routing of all {cfg.layers} layers, floats on layers {floats}")
+    for layer in range(cfg.layers):
         x, _ = oracle.margin_x(cfg, layer)
         L = DeviceLayer(cfg, layer, x=x)
         o = L.run_layer()
-        ref = L.oracle()
-        check_routing(o, ref, cfg.k)
-        err = rowwise_rel_err(host(o["y"]), ref["y"])
-        say(f"  rel err {err:.2e}, distinct experts {len(np.unique(ref['idx']))}")
-        assert err <= TOL
+        r = oracle.route_from_synth(cfg, layer, x)
+        check_routing(o, r, cfg.k)
+        msg = f"  c3 layer {layer}: routing exact, distinct experts {len(np.unique(r['idx']))}"
+        if layer in floats:
+            ref = oracle.layer_from_synth(cfg, layer, x, route=r, threads=ORACLE_THREADS)
+            err = rowwise_rel_err(host(o["y"]), ref["y"])
+            msg += f", rel err {err:.2e}"
+            assert err <= TOL, msg
+        say(msg)
+        del L, o
 
 
-def test_c4_slot_tiering_sampled_layers():
-    """16 tokens per layer against the 4,176-expert global slot table:
-    bit-exact miss lists, hits-only y, and the completion invariant."""
+def test_c4_slot_tiering_all_layers():
+    """16 tokens per layer against the 4,176-expert global slot table, all 48
+    layers: every layer's indices, slots and miss lists (expert, token,
+    offsets) bit-exact; on 8 layers -- among them the smallest (57) and the
+    largest (109) resident sets -- y (hits only) within tolerance and the
+    completion invariant y + sum of the listed misses' gate * FFN = the
+    all-resident layer."""
     from synth import device as sdev
     cfg = synth.CONFIGS["c4"]
     slot_of, sl, se, S = synth.slot_layout(cfg)
-    say(f"[gpu] c4: filling the global pool of {S} slots")
+    n_l = (slot_of >= 0).sum(axis=1)
+    lo, hi = int(np.argmin(n_l)), int(np.argmax(n_l))
+    assert n_l[lo] == 57 and n_l[hi] == 109
+    floats = _float_layers(cfg, [lo, hi, 0, cfg.layers - 1])
+    say(f"[gpu] c4: filling the global pool of {S} slots; floats on layers {floats}")
     pool = sdev.expert_pool(cfg, sl, se)
-    for layer in (0, 31):
-        say(f"[gpu] c4 layer {layer}: T=16, resident {int((slot_of[layer] >= 0).sum())}")
+    for layer in range(cfg.layers):
         x, _ = oracle.margin_x(cfg, layer)
         L = DeviceLayer(cfg, layer, x=x, pool=pool, slot_of=slot_of[layer], num_slots=S)
         o = L.run_layer()
-        ref = L.oracle(with_misses=(layer == 0))
-        check_routing(o, ref, cfg.k)
-        err = rowwise_rel_err(host(o["y"]), ref["y"])
-        hit = (ref["slot_idx"] >= 0).mean()
-        say(f"  rel err {err:.2e}, hit rate {hit:.2f}, misses {len(ref['miss_expert'])}")
-        assert err <= TOL
-        if layer == 0:
+        r = oracle.route_from_synth(cfg, layer, x, slot_of=slot_of[layer], num_slots=S)
+        check_routing(o, r, cfg.k)
+        hit = (r["slot_idx"] >= 0).mean()
+        msg = (f"  c4 layer {layer}: resident {int(n_l[layer])}, routing and miss list exact, "
+               f"hit rate {hit:.2f}, misses {len(r['miss_expert'])}")
+        if layer in floats:
+            ref = oracle.layer_from_synth(cfg, layer, x, slot_of=slot_of[layer], num_slots=S,
+                                          with_misses=True, route=r, threads=ORACLE_THREADS)
             y = host(o["y"]).astype(np.float64)
+            err = rowwise_rel_err(y, ref["y"])
             for e, t, g in zip(ref["miss_expert"], ref["miss_token"], ref["miss_gate"]):
                 y[t] += g * ref["pair_out"][t * cfg.k + list(ref["idx"][t]).index(e)]
-            assert rowwise_rel_err(y, ref["y_full"]) <= TOL
+            err_full = rowwise_rel_err(y, ref["y_full"])
+            msg += f", rel err {err:.2e}, completed {err_full:.2e}"
+            assert err <= TOL and err_full <= TOL, msg
+        say(msg)
+        del L, o
+
+
+@pytest.mark.parametrize("name", ["c2", "c3"])
+def test_separate_calls_full_size(name):
+    """The four separate calls (moe_route, moe_resolve_slots, moe_expert_ffn,
+    moe_combine) at the decode (T = 1) and verify (T = 4) shapes, H = 2048,
+    I = 768: the router GEMV, the one-block resolution and the dequant-fused
+    gate/up and down GEMVs at full width.  Indices, slots, miss lists and
+    buckets bit-exact; pair outputs, shared-expert outputs and y within
+    tolerance."""
+    cfg = synth.CONFIGS[name]
+    layer = 3
+    say(f"[gpu] separate calls at full size: {cfg.name} layer {layer}")
+    x, _ = oracle.margin_x(cfg, layer)
+    L = DeviceLayer(cfg, layer, x=x)
+    o = L.run_steps()
+    ref = oracle.layer_from_synth(cfg, layer, x, threads=ORACLE_THREADS)
+    check_routing(o, ref, cfg.k)
+    np.testing.assert_array_equal(host(o["bucket_off"]), ref["bucket_off"])
+    np.testing.assert_array_equal(host(o["bucket_pair"])[: len(ref["bucket_pair"])],
+                                  ref["bucket_pair"])
+    hit = ref["slot_idx"].ravel() >= 0
+    e_pair = rowwise_rel_err(host(o["pair_out"])[hit], ref["pair_out"][hit])
+    e_sh = rowwise_rel_err(host(o["shared_out"]), ref["shared_out"])
+    e_y = rowwise_rel_err(host(o["y"]), ref["y"])
+    say(f"  rel err: pairs {e_pair:.2e}, shared {e_sh:.2e}, y {e_y:.2e}")
+    assert max(e_pair, e_sh, e_y) <= TOL

@@ -6,7 +6,8 @@ import pytest
 
 import oracle
 import synth
-from helpers import TOL, DeviceLayer, check_routing, host, rowwise_rel_err, say, small_cfg
+from helpers import (ORACLE_THREADS, TOL, DeviceLayer, check_routing, host, rowwise_rel_err,
+                     say, small_cfg)
 
 pytestmark = pytest.mark.gpu
 
@@ -89,7 +90,8 @@ def test_prefill_mid_partial_slots(name):
 def test_c5_prefill_full_size():
     """32,768 tokens through one layer, 4-bit experts, Zipf routing, in the
     calls bench.py times: every token's routing and every bucket bit-exact,
-    floats on a sample that includes the largest and the smallest bucket."""
+    y on 1,024 sampled tokens that include the first and last tokens of the
+    largest bucket and the first of the smallest non-empty one."""
     cfg = synth.CONFIGS["c5"]
     say("[gpu] c5: drawing 32768 tokens with a routing margin (threaded oracle router)")
     x, att = oracle.margin_x(cfg, 0, threads=16)
@@ -110,11 +112,61 @@ def test_c5_prefill_full_size():
             r["bucket_pair"][r["bucket_off"][big + 1] - 1] // cfg.k,
             r["bucket_pair"][r["bucket_off"][small]] // cfg.k]
     rng = np.random.default_rng(5)
-    tokens = np.unique(np.concatenate([pick, rng.choice(cfg.T, 29, replace=False)]))
-    ref = oracle.layer_from_synth(cfg, 0, x, tokens=tokens, route=r)
+    others = np.setdiff1d(np.arange(cfg.T), pick)
+    tokens = np.unique(np.concatenate([pick, rng.choice(others, 1024 - len(set(pick)),
+                                                        replace=False)]))
+    assert len(tokens) == 1024
+    ref = oracle.layer_from_synth(cfg, 0, x, tokens=tokens, route=r, threads=ORACLE_THREADS)
     err = rowwise_rel_err(host(o["y"])[tokens], ref["y"][tokens])
     say(f"  sampled {len(tokens)} tokens: rel err {err:.2e}")
     assert err <= TOL
+
+
+RANGE = {
+    "q4": small_cfg(E=32, k=4, H=512, I=512, T=1100, wfmt="q4", bias="zipf", seed=51),
+    "q2": small_cfg(E=24, k=3, H=256, I=768, T=900, wfmt="q2", bias="zipf", seed=52),
+}
+
+
+@pytest.mark.parametrize("name", list(RANGE))
+def test_prefill_gemm_activation_range(name):
+    """The grouped-GEMM path with token rows scaled by 2^-24 .. 2^16 (exact
+    in bf16): tokens beyond the fp16 range (|x| > 65504), h beyond it (up to
+    ~10^14), and rows so small that fp16 would flush them.  Each token row
+    and h row slab outside the fp16 working range is carried with a power-
+    of-two scale, so y stays within tolerance on every row.  Routing comes
+    from the bias alone (zero router weights), so the scaled tokens do not
+    reach the logits."""
+    import torch
+    cfg = RANGE[name]
+    assert _uses_gemm(cfg)
+    say(f"[gpu] prefill GEMM activation range ({name}): T={cfg.T} H={cfg.H} I={cfg.I}")
+    x = synth.gen_x(cfg, 0, cfg.T)
+    f = (x.astype(np.uint32) << 16).view(np.float32)
+    scale = np.float32(2.0) ** np.array([-24, -10, 0, 8, 16], np.float32)[np.arange(cfg.T) % 5]
+    x = ((f * scale[:, None]).view(np.uint32) >> 16).astype(np.uint16)   # exact: powers of two
+    L = DeviceLayer(cfg, 0, x=x)
+    bias = (np.random.default_rng(6).permutation(cfg.E) * 0.01).astype(np.float32)
+    L.inp["router_w"].zero_()
+    L.inp["bias"].copy_(torch.from_numpy(bias))
+    o = L.run_steps()
+    logits = oracle.router(x, np.zeros((cfg.E, cfg.H), np.uint16), cfg.router_fmt, bias)
+    idx, gate = oracle.topk(logits, cfg.k)
+    slot_idx, me, mt, mg, moff = oracle.resolve(idx, gate, cfg.E)
+    route = {"logits": logits, "idx": idx, "gate": gate, "slot_idx": slot_idx,
+             "miss_expert": me, "miss_token": mt, "miss_gate": mg, "miss_off": moff}
+    ref = oracle.layer_from_synth(cfg, 0, x, route=route, threads=ORACLE_THREADS)
+    check_routing(o, ref, cfg.k)
+    y = host(o["y"])
+    assert np.isfinite(y).all()
+    ay = np.abs(ref["y"]).max(axis=1)
+    say(f"  |y| row maxima {ay.min():.2e} .. {ay.max():.2e}")
+    assert ay.max() > 1e10 and ay.min() < 1e-12
+    for sc in np.unique(scale):
+        rows = scale == sc
+        err = rowwise_rel_err(y[rows], ref["y"][rows])
+        say(f"  rows scaled by 2^{int(np.log2(sc))}: rel err {err:.2e}")
+        assert err <= TOL
 
 
 CHUNKED = {
