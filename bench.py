@@ -9,10 +9,17 @@ keep the weights out of the 256 MB Infinity Cache, steps cycle through
 stack: 43.5 GB of expert weights) and through distinct tokens, so every
 step streams its experts from HBM as a real decode step does.
 
-Prints one JSON line (see the keys below).  --config c3/c4/c5 measures the
-other workloads (c3: 48-layer 4-token verify stack, step = 48 layers; c4:
-the 16-token slot-table stack; c5: prefill of 32,768 tokens through one
-layer).
+Prints one JSON line (see the keys below).  By default the line is the
+decode layer's, and it carries two more legs under "legs": the 48-layer
+4-token verify stack (c3, step = 48 moe_layer calls) and the prefill of
+32,768 tokens through one layer (c5), each with its own roofline and CPU
+baseline.  --config c2/c3/c4/c4a/c5 measures one workload alone (c4: the
+16-token slot-table stack; c4a: the same with the adaptive slot table).
+
+No timed step repeats a (layer, tokens) pair of the warm-up: steps draw
+their tokens from a step counter that runs on from the warm-up.  The
+distinct experts of every timed call (for the algorithmic bytes) come from
+the slot tables those calls write, one buffer per call.
 """
 
 import argparse
@@ -33,6 +40,36 @@ MFMA_F16_PEAK_TFLOPS = 2500.0
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+class pinned_core:
+    """Runs the block with this process pinned to one host core (the last
+    one it may use), then restores the affinity.  Reports the host."""
+
+    def __enter__(self):
+        self.before = os.sched_getaffinity(0)
+        self.core = max(self.before)
+        os.sched_setaffinity(0, {self.core})
+        return self
+
+    def __exit__(self, *exc):
+        os.sched_setaffinity(0, self.before)
+
+    def info(self):
+        return {"cores": 1, "pinned_core": self.core, "cpu_model": cpu_model(),
+                "host_cpus": os.cpu_count(), "cpus_allowed": len(self.before)}
 
 
 # HBM bytes per launch of the roofline kernel(s), from two rocprofv3 --pmc
@@ -95,52 +132,67 @@ def algorithmic_bytes_decode(cfg, n_experts_read, T):
     return router + bias + experts + io
 
 
-def cpu_baseline_decode(cfg, n_tokens, layers):
-    """The oracle (single-threaded fp64) on a bounded sample: n_tokens
-    decode steps, each on its own layer copy; input generation untimed."""
+def cpu_baseline_decode(cfg, n_calls, layers):
+    """The oracle (single-threaded fp64, pinned to one core) on a bounded
+    sample: n_calls layer calls of cfg's T tokens, each on its own layer;
+    input generation untimed.  Returns (seconds per layer call, elapsed, host
+    info)."""
     import oracle
     import synth
     elapsed = 0.0
-    for i in range(n_tokens):
-        layer = i % layers
-        x = synth.gen_x_rows(cfg, layer, [1000 + i])
-        W = synth.gen_router(cfg, layer)
-        bias = synth.gen_bias(cfg, layer)
-        t0 = time.perf_counter()
-        logits = oracle.router(x, W, cfg.router_fmt, bias)
-        idx, gate = oracle.topk(logits, cfg.k)
-        slot_idx, *_ = oracle.resolve(idx, gate, cfg.E, None)
-        elapsed += time.perf_counter() - t0
-        experts = {int(e): synth.gen_expert(cfg, layer, int(e)) for e in idx[0]}
-        shared = synth.gen_expert(cfg, layer, synth.SHARED_ID) if cfg.shared else None
-        t0 = time.perf_counter()
-        pair_out = np.stack([oracle.ffn(cfg.wfmt, cfg.H, cfg.I, experts[int(e)], x)[0]
-                             for e in idx[0]])
-        sh = oracle.ffn(cfg.wfmt, cfg.H, cfg.I, shared, x) if shared else None
-        oracle.combine(slot_idx, gate, pair_out, sh)
-        elapsed += time.perf_counter() - t0
-    return n_tokens / elapsed, elapsed
+    with pinned_core() as pc:
+        for i in range(n_calls):
+            layer = i % layers
+            x = synth.gen_x_rows(cfg, layer, 1000 + np.arange(cfg.T) + i * cfg.T)
+            W = synth.gen_router(cfg, layer)
+            bias = synth.gen_bias(cfg, layer)
+            t0 = time.perf_counter()
+            logits = oracle.router(x, W, cfg.router_fmt, bias)
+            idx, gate = oracle.topk(logits, cfg.k)
+            slot_idx, *_ = oracle.resolve(idx, gate, cfg.E, None)
+            elapsed += time.perf_counter() - t0
+            experts = {int(e): synth.gen_expert(cfg, layer, int(e)) for e in np.unique(idx)}
+            shared = synth.gen_expert(cfg, layer, synth.SHARED_ID) if cfg.shared else None
+            t0 = time.perf_counter()
+            pair_out = np.zeros((cfg.T * cfg.k, cfg.H))
+            for e in sorted(experts):
+                ps = np.nonzero(idx.ravel() == e)[0]
+                pair_out[ps] = oracle.ffn(cfg.wfmt, cfg.H, cfg.I, experts[e], x[ps // cfg.k])
+            sh = oracle.ffn(cfg.wfmt, cfg.H, cfg.I, shared, x) if shared else None
+            oracle.combine(slot_idx, gate, pair_out, sh)
+            elapsed += time.perf_counter() - t0
+        info = pc.info()
+    return elapsed / n_calls, elapsed, info
 
 
-def bench_decode(args, cfg_name):
+def bench_decode(args, cfg_name, steps=None, warmup=None, cpu_calls=None):
+    """One decode workload: c2 (a step = one moe_layer call, cycling through
+    --layers layer copies) or a 48-layer stack c3 / c4 (a step = 48 calls)."""
     import torch
     import routed_expert_ffn_gemv_amd as moe
     import synth
     from synth import device as sdev
 
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
     cfg = synth.CONFIGS[cfg_name]
     T = cfg.T
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     L = args.layers if cfg.layers == 1 else cfg.layers
-    log(f"[bench] {cfg.name}: building {L} layer copies on the device")
+    n_steps = warmup + steps + args.phase_trace
+    # token groups: c2 uses group s // L on layer s % L; a stack uses group
+    # s mod 64 (every layer) -- so no (layer, tokens) pair occurs twice within
+    # 64 steps of a stack (a stack step streams ~3 GB, far beyond the 256 MB
+    # Infinity Cache, so later repeats find nothing cached either)
+    ngroups = n_steps // L + 1 if cfg.layers == 1 else min(n_steps, 64)
+    log(f"[bench] {cfg.name}: building {L} layers on the device ({ngroups} token groups)")
     t0 = time.time()
     slot_of, sl, se, S = synth.slot_layout(cfg) if cfg.slots == "tiered" else (None, None, None, cfg.E)
     global_pool = sdev.expert_pool(cfg, sl, se, dev) if cfg.slots == "tiered" else None
     layers = []
-    ntok = max(8, (args.steps + args.warmup) // L + 1) if cfg.layers == 1 else 1
     for l in range(L):
-        inp = sdev.layer_inputs(cfg, l, dev, x=synth.gen_x(cfg, l, T * ntok))
+        inp = sdev.layer_inputs(cfg, l, dev, x=synth.gen_x(cfg, l, T * ngroups))
         pool = global_pool if global_pool is not None else sdev.expert_pool(
             cfg, [l] * cfg.E, list(range(cfg.E)), dev)
         so = (torch.as_tensor(slot_of[l], device=dev) if slot_of is not None else None)
@@ -155,52 +207,42 @@ def bench_decode(args, cfg_name):
     y = torch.empty((T, H), dtype=torch.float32, device=dev)
     idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     gate = torch.empty((T, k), dtype=torch.float32, device=dev)
-    slot_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    calls_per_step = 1 if cfg.layers == 1 else L
+    # one slot table per timed call: the distinct experts those calls read
+    slot_rec = torch.empty((max(steps, 1), calls_per_step, T, k), dtype=torch.int32, device=dev)
+    slot_tmp = torch.empty((T, k), dtype=torch.int32, device=dev)
     miss = torch.empty((T * k * 3,), dtype=torch.int32, device=dev)
     miss_off = torch.empty((T + 1,), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
-    nx = layers[0][1]["x"].shape[0] // T
 
-    def step(s):
-        """One step: one layer (c2) or the whole 48-layer stack (c3/c4)."""
+    def step(s, rec):
+        """Step s: one layer (c2) or the whole stack (c3/c4); rec: the step's
+        slot-table buffer [calls][T][k] or None."""
         if cfg.layers == 1:
             desc, inp, _, _ = layers[s % L]
-            x = inp["x"][((s // L) % nx) * T:((s // L) % nx + 1) * T]
-            moe.moe_layer(desc, x, T, y, idx, gate, slot_idx, miss, miss_off, ws, stream)
+            g = s // L
+            moe.moe_layer(desc, inp["x"][g * T:(g + 1) * T], T, y, idx, gate,
+                          rec[0] if rec is not None else slot_tmp, miss, miss_off, ws, stream)
         else:
-            for desc, inp, _, _ in layers:
-                moe.moe_layer(desc, inp["x"], T, y, idx, gate, slot_idx, miss, miss_off, ws,
-                              stream)
+            g = s % ngroups
+            for l, (desc, inp, _, _) in enumerate(layers):
+                moe.moe_layer(desc, inp["x"][g * T:(g + 1) * T], T, y, idx, gate,
+                              rec[l] if rec is not None else slot_tmp, miss, miss_off, ws, stream)
 
-    # distinct experts read per layer call (for the algorithmic bytes): the
-    # stacks run one step with a slot buffer per layer
-    uniq = []
-    for s in range(min(64, args.steps)):
-        if cfg.layers == 1:
-            step(s)
-            torch.cuda.synchronize()
-            sl_h = slot_idx.cpu().numpy()
-            uniq.append(len(np.unique(sl_h[sl_h >= 0])))
-            continue
-        per = torch.empty((L, T, k), dtype=torch.int32, device=dev)
-        for l, (desc, inp, _, _) in enumerate(layers):
-            moe.moe_layer(desc, inp["x"], T, y, idx, gate, per[l], miss, miss_off, ws, stream)
-        torch.cuda.synchronize()
-        for sl_h in per.cpu().numpy():
-            uniq.append(len(np.unique(sl_h[sl_h >= 0])))
-        break   # the stack's inputs are the same every step
-    for s in range(args.warmup):
-        step(s)
+    for s in range(warmup):
+        step(s, None)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for s in range(args.steps):
-        step(s)
+    for i in range(steps):
+        step(warmup + i, slot_rec[i])
     e1.record(stream)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    calls_per_step = 1 if cfg.layers == 1 else L
+    moe.moe_layer_check(ws)
+    ms = e0.elapsed_time(e1) / steps
     ms_call = ms / calls_per_step
+    rec = slot_rec.cpu().numpy().reshape(steps * calls_per_step, T * k)
+    uniq = [len(np.unique(r[r >= 0])) for r in rec]
     u = float(np.mean(uniq))
     bytes_call = algorithmic_bytes_decode(cfg, u, T)
     gbs = bytes_call / (ms_call * 1e-3) / 1e9
@@ -210,8 +252,8 @@ def bench_decode(args, cfg_name):
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -231,15 +273,76 @@ def bench_decode(args, cfg_name):
     }
     if args.host_tier and cfg.slots == "tiered":
         out["host_tier"] = host_tier_leg(cfg, layers, ws, ms)
+    if args.phase_trace:
+        out["phase_trace"] = phase_trace(args.phase_trace, lambda s: step(s, None),
+                                         warmup + steps, n_steps)
+    del layers, global_pool
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        n = args.cpu_tokens
-        log(f"[bench] cpu baseline: oracle on {n} tokens")
-        tps, el = cpu_baseline_decode(cfg, n, L)
-        out["cpu_baseline"] = {"value": round(tps, 3), "unit": "tokens/s", "cores": 1,
-                               "kind": "oracle",
-                               "sample": f"{n} single-token decode layers of {cfg.name} "
-                                         f"(router..combine, fp64, one thread, {el:.1f}s)"}
+        n = cpu_calls if cpu_calls is not None else (args.cpu_tokens if cfg.layers == 1 else 3)
+        log(f"[bench] cpu baseline: oracle on {n} layer calls of {T} tokens")
+        sec, el, info = cpu_baseline_decode(cfg, n, L)
+        step_s = sec * calls_per_step
+        out["cpu_baseline"] = dict({"value": round(T / step_s, 4), "unit": "tokens/s",
+                                    "kind": "oracle",
+                                    "sample": f"{n} layer calls of {T} token(s) of {cfg.name} "
+                                              f"(router..combine, fp64, one pinned thread, "
+                                              f"{el:.1f}s), scaled to a step of "
+                                              f"{calls_per_step} call(s)"}, **info)
     return out
+
+
+PHASES = [(0, "start"), (2, "tokens staged"), (3, "router/shared tasks (wave 0)"),
+          (4, "every logit seen (wave 0)"), (11, "every logit seen (all waves)"),
+          (5, "routing done"), (6, "gate/up done (wave 0)"), (7, "gate/up done (last wave)"),
+          (12, "down phase entered"), (13, "first unit's h present"), (8, "first h staged"),
+          (9, "down done"), (10, "end")]
+
+
+def phase_trace(n_calls, run_step, first_step, n_distinct):
+    """Phase stamps of n_calls further fused launches (steps after the timed
+    ones, so cold), one call per step: per phase, the median and the maximum
+    over workgroups of the time since the first workgroup started, then the
+    median over calls; and each XCD's median start offset (us)."""
+    import torch
+    import routed_expert_ffn_gemv_amd as moe
+    tr = torch.zeros((1024, 16), dtype=torch.int64, device="cuda")
+    per_phase = {name: [] for _, name in PHASES}
+    xcd_start = {}
+    moe.moe_set_trace(tr)
+    try:
+        for i in range(n_calls):
+            s = first_step + i
+            if s >= n_distinct:
+                break
+            tr.zero_()
+            run_step(s)
+            torch.cuda.synchronize()
+            t = tr.cpu().numpy()
+            t = t[t[:, 0] > 0]
+            t0 = t[:, 0].min()
+            for slot, name in PHASES:
+                v = t[:, slot]
+                v = v[v > 0]
+                if len(v):
+                    per_phase[name].append((np.median(v - t0) / 100.0, (v.max() - t0) / 100.0))
+            for x in np.unique(t[:, 1]):
+                xcd_start.setdefault(int(x), []).append(np.median(t[t[:, 1] == x, 0] - t0) / 100.0)
+    finally:
+        moe.moe_set_trace(None)
+    res = {"calls": len(per_phase["start"]), "unit": "us since the first workgroup started",
+           "phases": {name: {"median_over_wgs": round(float(np.median([a for a, _ in v])), 2),
+                             "max_over_wgs": round(float(np.median([b for _, b in v])), 2)}
+                      for name, v in per_phase.items() if v},
+           "xcd_start_median": {str(x): round(float(np.median(v)), 2)
+                                for x, v in sorted(xcd_start.items())}}
+    log("[bench] phase trace (us since the first workgroup started; medians over calls)")
+    log("| phase | median over workgroups | last workgroup |")
+    log("|---|---:|---:|")
+    for name, v in res["phases"].items():
+        log(f"| {name} | {v['median_over_wgs']:.2f} | {v['max_over_wgs']:.2f} |")
+    log("XCD start offsets: " + ", ".join(f"{x}: {v:.2f}" for x, v in res["xcd_start_median"].items()))
+    return res
 
 
 def host_tier_leg(cfg, layers, ws, gpu_ms):
@@ -441,33 +544,39 @@ def gemm_flops(cfg, n_hit, T):
 
 
 def cpu_baseline_prefill(cfg, n_route, n_ffn):
-    """Oracle on a bounded sample of the prefill layer: routing of n_route
-    tokens and the FFN + combine of n_ffn of them; tokens/s extrapolated
-    from the per-token times (input generation untimed)."""
+    """Oracle (one pinned thread) on a bounded sample of the prefill layer:
+    routing of n_route tokens and the FFN + combine of n_ffn of them;
+    tokens/s extrapolated from the per-token times (input generation
+    untimed).  Returns (tokens/s, elapsed, host info)."""
     import oracle
     import synth
     x = synth.gen_x_rows(cfg, 0, np.arange(n_route))
     W = synth.gen_router(cfg, 0)
     bias = synth.gen_bias(cfg, 0)
-    t0 = time.perf_counter()
-    logits = oracle.router(x, W, cfg.router_fmt, bias)
-    idx, gate = oracle.topk(logits, cfg.k)
-    slot_idx, *_ = oracle.resolve(idx, gate, cfg.E, None)
-    oracle.bucket(slot_idx, cfg.E)
-    t_route = (time.perf_counter() - t0) / n_route
-    experts = {int(e): synth.gen_expert(cfg, 0, int(e)) for e in np.unique(idx[:n_ffn])}
-    shared = synth.gen_expert(cfg, 0, synth.SHARED_ID) if cfg.shared else None
-    t0 = time.perf_counter()
-    for t in range(n_ffn):
-        po = np.stack([oracle.ffn(cfg.wfmt, cfg.H, cfg.I, experts[int(e)], x[t:t + 1])[0]
-                       for e in idx[t]])
-        sh = oracle.ffn(cfg.wfmt, cfg.H, cfg.I, shared, x[t:t + 1]) if shared else None
-        oracle.combine(slot_idx[t:t + 1], gate[t:t + 1], po, sh)
-    t_ffn = (time.perf_counter() - t0) / n_ffn
-    return 1.0 / (t_route + t_ffn), t_route * n_route + t_ffn * n_ffn
+    with pinned_core() as pc:
+        t0 = time.perf_counter()
+        logits = oracle.router(x, W, cfg.router_fmt, bias)
+        idx, gate = oracle.topk(logits, cfg.k)
+        slot_idx, *_ = oracle.resolve(idx, gate, cfg.E, None)
+        oracle.bucket(slot_idx, cfg.E)
+        t_route = (time.perf_counter() - t0) / n_route
+        experts = {int(e): synth.gen_expert(cfg, 0, int(e)) for e in np.unique(idx[:n_ffn])}
+        shared = synth.gen_expert(cfg, 0, synth.SHARED_ID) if cfg.shared else None
+        t0 = time.perf_counter()
+        for t in range(n_ffn):
+            po = np.stack([oracle.ffn(cfg.wfmt, cfg.H, cfg.I, experts[int(e)], x[t:t + 1])[0]
+                           for e in idx[t]])
+            sh = oracle.ffn(cfg.wfmt, cfg.H, cfg.I, shared, x[t:t + 1]) if shared else None
+            oracle.combine(slot_idx[t:t + 1], gate[t:t + 1], po, sh)
+        t_ffn = (time.perf_counter() - t0) / n_ffn
+        info = pc.info()
+    return 1.0 / (t_route + t_ffn), t_route * n_route + t_ffn * n_ffn, info
 
 
-def bench_prefill(args, cfg_name):
+def bench_prefill(args, cfg_name, steps=None, warmup=None):
+    """Prefill: one step = moe_route + moe_resolve_slots + moe_expert_ffn +
+    moe_combine over the whole prompt (the same synthetic prompt every step:
+    a step streams ~4.5 GB, so nothing of one step is cached for the next)."""
     import torch
     import routed_expert_ffn_gemv_amd as moe
     import synth
@@ -499,6 +608,8 @@ def bench_prefill(args, cfg_name):
     stream = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
     x = inp["x"]
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
 
     def step(times=None):
         if times is not None:
@@ -518,16 +629,16 @@ def bench_prefill(args, cfg_name):
             torch.cuda.synchronize()
             times.append([ev[i].elapsed_time(ev[i + 1]) for i in range(4)])
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     e1.record(stream)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = e0.elapsed_time(e1) / steps
     parts = []
     for _ in range(3):
         step(parts)
@@ -540,7 +651,7 @@ def bench_prefill(args, cfg_name):
         "metric": METRIC,
         "value": round(T / (ms * 1e-3), 1),
         "unit": "tokens/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "q4 weights dequantised to fp16 tiles, fp16 MFMA, fp32 accumulation",
@@ -581,14 +692,15 @@ def bench_prefill(args, cfg_name):
                 del wsp
                 torch.cuda.empty_cache()
         log(f"[bench] prefill layer: {out['prefill_layer']}")
+    del pair_out, shared_out, ws, pool
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline: oracle on a sample")
-        tps, el = cpu_baseline_prefill(cfg, 512, 4)
-        out["cpu_baseline"] = {"value": round(tps, 3), "unit": "tokens/s", "cores": 1,
-                               "kind": "oracle",
-                               "sample": f"routing of 512 tokens + FFN/combine of 4 tokens of "
-                                         f"{cfg.name}, extrapolated per token (fp64, one thread, "
-                                         f"{el:.1f}s)"}
+        tps, el, info = cpu_baseline_prefill(cfg, 512, 4)
+        out["cpu_baseline"] = dict({"value": round(tps, 3), "unit": "tokens/s", "kind": "oracle",
+                                    "sample": f"routing of 512 tokens + FFN/combine of 4 tokens "
+                                              f"of {cfg.name}, extrapolated per token (fp64, one "
+                                              f"pinned thread, {el:.1f}s)"}, **info)
     return out
 
 
@@ -610,7 +722,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c4a", "c5"])
+    ap.add_argument("--config", default=None, choices=["c2", "c3", "c4", "c4a", "c5"],
+                    help="one workload alone (default: c2 with the c3 and c5 legs)")
+    ap.add_argument("--legs", default="c3,c5",
+                    help="legs added to the default c2 line (comma-separated; '' for none)")
     ap.add_argument("--layers", type=int, default=48)
     ap.add_argument("--cpu-tokens", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -619,6 +734,9 @@ def main():
                          "without a second stream")
     ap.add_argument("--host-tier", action="store_true",
                     help="c4: also time the host tier on one step's misses")
+    ap.add_argument("--phase-trace", type=int, default=0, metavar="N",
+                    help="decode workloads: after the timed steps, N more cold calls with the "
+                         "fused launch's phase stamps on (medians reported)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="first run a plain device-to-device copy of MIB MiB (3 times): the "
                          "known-size kernel that scales the HBM byte counters of a profile")
@@ -632,8 +750,16 @@ def main():
         out = bench_prefill(args, "c5")
     elif args.config == "c4a":
         out = bench_adaptive(args)
-    else:
+    elif args.config is not None:
         out = bench_decode(args, args.config)
+    else:
+        out = bench_decode(args, "c2")
+        legs = [l for l in args.legs.split(",") if l]
+        if legs:
+            out["legs"] = []
+        for leg in legs:
+            log(f"[bench] leg {leg}")
+            out["legs"].append(bench_prefill(args, leg) if leg == "c5" else bench_decode(args, leg))
     print(json.dumps(out), flush=True)
 
 

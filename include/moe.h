@@ -210,9 +210,11 @@ void moe_set_wait_budget(uint64_t ns, int32_t hold);
  * device buffer of 16 uint64 words per workgroup of the launch (one per
  * compute unit; 1024 rows always suffice), or NULL to stop.  Row b holds
  * workgroup b's real-time counter stamps (100 MHz) at: 0 start, 2 tokens
- * staged, 3 router/shared tasks of wave 0 done, 4 every logit seen,
- * 5 routing done, 6 wave 0's gate/up done, 7 the last wave's gate/up done,
- * 8 first h staged, 9 down done, 10 end; word 1 is the XCD it ran on.
+ * staged, 3 router/shared tasks of wave 0 done, 4 every logit seen by wave 0,
+ * 11 by every wave, 5 routing done, 6 wave 0's gate/up done, 7 the last
+ * wave's gate/up done, 12 down phase entered, 13 the first down unit's h
+ * present, 8 first h staged, 9 down done, 10 end; word 1 is the XCD it ran
+ * on.
  * Every launch overwrites the rows it writes.  Process-wide, read when a
  * call is issued. */
 void moe_set_trace(uint64_t* trace);

@@ -79,6 +79,9 @@ enum TraceSlot {
   kTrStagedH = 8,      // the first down unit's h staged
   kTrDown = 9,         // the workgroup's down units done
   kTrEnd = 10,         // end (workgroup 0: after the arrival check)
+  kTrLogitsAll = 11,   // every wave has seen every logit (the barrier after the polls)
+  kTrDStart = 12,      // down phase entered (the workgroup's gate/up tasks issued and done)
+  kTrHPolled = 13,     // the first down unit's h all present (thread 0's poll)
   kTraceSlots = 16
 };
 

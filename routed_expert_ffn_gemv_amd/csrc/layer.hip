@@ -312,9 +312,11 @@ __device__ __forceinline__ bool keep_waiting(const LayerArgs& a, Lds& L, uint64_
 // thread (16 columns of one token) issued before any is used.  psum holds
 // each 16-column group's sum; block sums add two groups in a fixed order.
 // The caller synchronises before reading xs or psum.
-template <int FMT>
+// mid() runs once, after the first batch's loads are issued and before they
+// are used.
+template <int FMT, typename Mid>
 __device__ __forceinline__ void stage_tokens(const uint16_t* __restrict__ x, int T, int H, uint32_t* xs,
-                                             float* psum, int vstride) {
+                                             float* psum, int vstride, Mid mid) {
   const int per_tok = H / 16;
   const int n_items = T * per_tok;
   constexpr int kR = 4;
@@ -329,6 +331,7 @@ __device__ __forceinline__ void stage_tokens(const uint16_t* __restrict__ x, int
         w[r][1] = src[1];
       }
     }
+    if (base == 0) mid();
 #pragma unroll
     for (int r = 0; r < kR; ++r) {
       const int it = base + r * kThreads + threadIdx.x;
@@ -397,7 +400,8 @@ __device__ __forceinline__ void token_block_sums(int T, int H, float* xsum, cons
 template <int FMT>
 __device__ __forceinline__ void stage_h(const uint64_t* const* srcs, int n, int K, uint32_t* xd,
                                         float* sd, float* psum, float* bsc, int vs,
-                                        uint32_t epoch, const LayerArgs& a, Lds& L, uint64_t t0) {
+                                        uint32_t epoch, const LayerArgs& a, Lds& L, uint64_t t0,
+                                        bool trace_h) {
   const int per_vec = K / 16;
   const int n_items = n * per_vec;
   constexpr int kIt = 2;   // items per thread and batch
@@ -429,6 +433,7 @@ __device__ __forceinline__ void stage_h(const uint64_t* const* srcs, int n, int 
         for (int c = 0; c < 16; ++c)
           if (src[r] && !tag_ok(wv[r][c], epoch)) wv[r][c] = ld_dev(src[r] + c);
     }
+    if (base == 0 && trace_h) stamp_now(a.trace, kTrHPolled);
 #pragma unroll
     for (int r = 0; r < kIt; ++r) {
       const int it = base + r * kThreads + threadIdx.x;
@@ -1256,6 +1261,7 @@ __device__ __forceinline__ void route_token(const LayerArgs& a, float* lg, int E
   if ((tid & 15) == 0) L.tmp[tid >> 4] = m;
   if (tid < 64) L.rkey[tid] = 0ull;   // the candidate list's empty slots
   __syncthreads();
+  stamp_now(a.trace, kTrLogitsAll);
   const bool thresh = k <= kTopkListMax;
   if (thresh) {
     const uint32_t my = L.tmp[lane & 31];
@@ -1446,7 +1452,8 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     stamp(ka.trace, kTrStart, t0);
     stamp(ka.trace, kTrXcd, xcc & 0xFu);
   }
-  const uint64_t hdr = tid == 0 ? ld_dev(reinterpret_cast<const uint64_t*>(ka.region)) : 0ull;
+  // every wave reads the header (its router task zeroes y only on a sound workspace)
+  const uint64_t hdr = lane == 0 ? ld_dev(reinterpret_cast<const uint64_t*>(ka.region)) : 0ull;
   int so[kEMax / kThreads];
 #pragma unroll
   for (int r = 0; r < kEMax / kThreads; ++r) {
@@ -1473,7 +1480,13 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   else if (task0 < n_a)
     gateup_load<FMT>(rg, ru, ka, ka.sg, ka.su, 0,
                      ((task0 - n_router) % n_srb) * kRowsGU + lane / kLprGU, lane_gu);
-  stage_tokens<FMT>(ka.x, T, K, xs, psum, vstride);
+  // The first router task zeroes its share of y while the tokens load: the
+  // stores land before the task publishes its logits, and the wait for the
+  // header lets the row and token loads stay in flight.
+  stage_tokens<FMT>(ka.x, T, K, xs, psum, vstride, [&]() {
+    if (task0 < n_router && __builtin_amdgcn_readfirstlane(uint32_t(hdr >> 32)) == 0u)
+      zero_y_share(ka, task0, n_router, lane);
+  });
   if (tid == 0) {
     L.calls = uint32_t(hdr);
     L.failed = uint32_t(hdr >> 32) != 0u ? 2 : 0;   // a failed call left the workspace poisoned
@@ -1498,8 +1511,10 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   }
   for (int task = task0; task < n_a; task += kWaves * G) {
     if (task < n_router) {
-      if (task != task0) router_load<FMT>(rr, a, task, task % n_rg, n_router, lane);
-      zero_y_share(a, task, n_router, lane);   // after the workspace check, before the logits
+      if (task != task0) {
+        router_load<FMT>(rr, a, task, task % n_rg, n_router, lane);
+        zero_y_share(a, task, n_router, lane);   // after the workspace check, before the logits
+      }
       router_compute<FMT, kTG>(rr, a, task % n_rg, (task / n_rg) * kTG, xs, vstride, lane, epoch);
     } else {
       const int s = task - n_router, t0 = (s / n_srb) * kTG;
@@ -1551,6 +1566,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     }
   stamp_now(a.trace, kTrLogits);
   __syncthreads();
+  stamp_now(a.trace, kTrLogitsAll);
   const bool thresh = k <= kTopkListMax;
   if (thresh) topk_threshold<TB>(lg, T, E, k, L);
   // tokens the threshold selection did not take: one wave each
@@ -1760,6 +1776,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     if (wave == 0) stamp(a.trace, kTrGateUp0, t);
   }
   // ---- D: down units (expert or shared, block of rows), y += gate * D h
+  stamp_now(a.trace, kTrDStart);
   {
     uint32_t* xd = smem;                                    // reuses the token area
     float* sd = reinterpret_cast<float*>(xd + kTMax * vs_d);
@@ -1787,7 +1804,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
           srcs[tid] = shared ? region_h_sh(a) + int64_t(tid) * Kd
                              : region_h(a) + int64_t(L.bpair[st + tid]) * Kd;
         __syncthreads();
-        stage_h<FMT>(srcs, n, Kd, xd, sd, pd, bsc, vs_d, epoch, a, L, t0);
+        stage_h<FMT>(srcs, n, Kd, xd, sd, pd, bsc, vs_d, epoch, a, L, t0, staged < 0);
         __syncthreads();
         if (staged < 0 && a.trace) {
           stamp(a.trace, kTrStagedH, __builtin_amdgcn_s_memrealtime());
