@@ -186,6 +186,30 @@ moe_status moe_layer(const moe_layer_desc* desc, const uint16_t* x, int32_t T, f
                      int32_t* topk_idx, float* topk_gate, int32_t* slot_idx, moe_miss* miss,
                      int32_t* miss_off, void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of the static hand-off region moe_layer_noalloc uses on each GPU. */
+#define MOE_LAYER_SCRATCH_BYTES (16u << 20)
+
+/* moe_layer for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid allocation): no
+ * workspace argument.  The fused launch hands over through a static device
+ * array of the library, MOE_LAYER_SCRATCH_BYTES on each GPU it runs on,
+ * held until the process ends and cleared (by a kernel on `stream`) before
+ * the first call on that GPU.  Every call on one GPU shares that GPU's
+ * array, which carries the calls' sequence state from one call to the next:
+ * calls that overlap on one GPU (several streams or host threads at once)
+ * race and must not be made.  Only shapes that take the fused launch are
+ * accepted (T * k <= 256, a BF16 router for Q2/Q4 experts, limits as for
+ * moe_layer) and only while the hand-off region they need fits the array
+ * (E <= 1024, k <= 32, I <= 4096 always do); others return
+ * MOE_ERR_UNSUPPORTED and launch nothing.  Arguments, outputs and errors
+ * as moe_layer; slot_idx may be NULL.  moe_layer_check(NULL, 0, stream)
+ * reports whether a call on this GPU gave up a bounded wait, and clears the
+ * array again if one did.  The call allocates nothing (no hipMalloc, no
+ * allocating library routine). */
+moe_status moe_layer_noalloc(const moe_layer_desc* desc, const uint16_t* x, int32_t T, float* y,
+                             int32_t* topk_idx, float* topk_gate, int32_t* slot_idx,
+                             moe_miss* miss, int32_t* miss_off, void* stream);
+
 /* Whether the fused moe_layer calls made on workspace ws completed: MOE_OK,
  * or MOE_ERR_DEVICE when one of them gave up a bounded wait (for example
  * because another kernel kept some of its workgroups from running for
@@ -193,8 +217,11 @@ moe_status moe_layer(const moe_layer_desc* desc, const uint16_t* x, int32_t T, f
  * accesses memory out of bounds), and every later moe_layer call on the
  * same workspace returns at once without writing anything, until the caller
  * zeroes the workspace again.  This call waits for the work queued on
- * `stream` and reads 8 bytes of ws: a host synchronisation, meant for
- * checks outside the hot path.  ws NULL or ws_bytes < 256: MOE_ERR_INVALID. */
+ * `stream` and reads 4 bytes of ws: a host synchronisation, meant for
+ * checks outside the hot path.  ws NULL checks the static region of
+ * moe_layer_noalloc on the current GPU instead (and, when a call on it
+ * gave up, clears it so that later calls work again).  ws not NULL and
+ * ws_bytes < 256: MOE_ERR_INVALID. */
 moe_status moe_layer_check(const void* ws, size_t ws_bytes, void* stream);
 
 /* Budget of every wait of the fused moe_layer launch, in nanoseconds of the

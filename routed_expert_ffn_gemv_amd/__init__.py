@@ -27,7 +27,7 @@ EXPORTS = ("moe_status_string", "moe_version", "moe_workspace_size", "moe_route"
            "moe_slot_refresh_workspace_size", "moe_slot_refresh", "moe_host_miss_ffn",
            "moe_host_isa", "moe_verify_workspace_size", "moe_verify_accept",
            "moe_prefill_workspace_size", "moe_prefill_layer", "moe_layer_check",
-           "moe_set_wait_budget", "moe_set_trace")
+           "moe_set_wait_budget", "moe_set_trace", "moe_layer_noalloc")
 MOE_REFRESH_MAX_SWAPS = 1024
 
 
@@ -91,6 +91,8 @@ def _load():
     lib.moe_combine.argtypes = [D, I32, P, P, P, P, P, P]
     lib.moe_layer.restype = I32
     lib.moe_layer.argtypes = [D, P, I32, P, P, P, P, P, P, P, SZ, P]
+    lib.moe_layer_noalloc.restype = I32
+    lib.moe_layer_noalloc.argtypes = [D, P, I32, P, P, P, P, P, P, P]
     lib.moe_layer_check.restype = I32
     lib.moe_layer_check.argtypes = [P, SZ, P]
     lib.moe_set_wait_budget.restype = None
@@ -238,9 +240,18 @@ def moe_layer(desc, x, T, y, topk_idx, topk_gate, slot_idx, miss, miss_off, ws, 
                          ws.numel() if ws is not None else 0, _stream(stream)), "moe_layer")
 
 
+def moe_layer_noalloc(desc, x, T, y, topk_idx, topk_gate, slot_idx, miss, miss_off, stream=None):
+    """moe_layer without a workspace: the hand-off region is the library's
+    static device array (fused shapes only)."""
+    _check(lib.moe_layer_noalloc(desc.ref, _ptr(x), int(T), _ptr(y), _ptr(topk_idx),
+                                 _ptr(topk_gate), _ptr(slot_idx), _ptr(miss), _ptr(miss_off),
+                                 _stream(stream)), "moe_layer_noalloc")
+
+
 def moe_layer_check(ws, stream=None):
-    """Raises MoEError(MOE_ERR_DEVICE) if a fused moe_layer call on ws gave
-    up a bounded wait (waits for the stream)."""
+    """Raises MoEError(MOE_ERR_DEVICE) if a fused moe_layer call on ws (None:
+    moe_layer_noalloc's static region of this GPU) gave up a bounded wait
+    (waits for the stream)."""
     _check(lib.moe_layer_check(_ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)),
            "moe_layer_check")
 

@@ -466,12 +466,41 @@ moe_status moe_layer(const moe_layer_desc* desc, const uint16_t* x, int32_t T, f
   return device_status(e);
 }
 
+moe_status moe_layer_noalloc(const moe_layer_desc* desc, const uint16_t* x, int32_t T, float* y,
+                             int32_t* topk_idx, float* topk_gate, int32_t* slot_idx,
+                             moe_miss* miss, int32_t* miss_off, void* stream) {
+  const moe_status s = check_desc(desc);
+  if (s != MOE_OK) return s;
+  if (T < 0) return MOE_ERR_INVALID;
+  if (T > MOE_LAYER_MAX_T) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !aligned(x, 16) || !y || !aligned(y, 16) || !topk_idx || !topk_gate || !miss ||
+      !miss_off)
+    return MOE_ERR_INVALID;
+  if (!fused_shape(desc, T) ||
+      layer_region_bytes(desc->E, desc->k, desc->I) > size_t(MOE_LAYER_SCRATCH_BYTES))
+    return MOE_ERR_UNSUPPORTED;
+  const LayerArgs L =
+      layer_args(desc, x, T, y, topk_idx, topk_gate, slot_idx, miss, miss_off, nullptr);
+  return device_status(launch_layer_noalloc(L, desc->gate.fmt, static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_layer_check(const void* ws, size_t ws_bytes, void* stream) {
-  if (!ws || !aligned(ws, kAlign) || ws_bytes < 256) return MOE_ERR_INVALID;
-  if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return MOE_ERR_DEVICE;
-  uint32_t err = 0;   // the error word of the hand-off region's header (region at offset 0)
-  if (hipMemcpy(&err, static_cast<const uint8_t*>(ws) + kRegionErr, 4, hipMemcpyDeviceToHost) !=
-      hipSuccess)
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint8_t* region = static_cast<const uint8_t*>(ws);   // the hand-off region: offset 0
+  if (!ws) {
+    uint8_t* p = nullptr;
+    if (layer_scratch_address(&p) != hipSuccess) return MOE_ERR_DEVICE;
+    if (!p) return MOE_OK;   // no moe_layer_noalloc call on this GPU yet
+    region = p;
+  } else if (!aligned(ws, kAlign) || ws_bytes < 256) {
+    return MOE_ERR_INVALID;
+  }
+  if (hipStreamSynchronize(st) != hipSuccess) return MOE_ERR_DEVICE;
+  uint32_t err = 0;   // the error word of the region's header
+  if (hipMemcpy(&err, region + kRegionErr, 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return MOE_ERR_DEVICE;
+  if (err && !ws && (layer_scratch_clear(st) != hipSuccess || hipStreamSynchronize(st) != hipSuccess))
     return MOE_ERR_DEVICE;
   return err ? MOE_ERR_DEVICE : MOE_OK;
 }

@@ -93,4 +93,12 @@ bool layer_fused_ok(int fmt, int T, int k, int E, int H, int I);
 size_t layer_fused_lds(int fmt, int T, int E, int H, int I);
 hipError_t launch_layer_fused(const LayerArgs& a, int fmt, hipStream_t st, int* grid);
 
+// The fused launch on the library's static hand-off region of the current
+// device (moe_layer_noalloc): a.region is set here.
+hipError_t launch_layer_noalloc(LayerArgs a, int fmt, hipStream_t st);
+// Device address of that region (set up on first use: *ptr = null if it
+// never was), and a clear of it on stream st.
+hipError_t layer_scratch_address(uint8_t** ptr);
+hipError_t layer_scratch_clear(hipStream_t st);
+
 }  // namespace moe

@@ -47,6 +47,8 @@
 // goes on without the data; the call's outputs are then unspecified (every
 // access still stays in bounds), and later calls on the workspace return at
 // once until the caller zeroes it again (moe_layer_check reports it).
+#include <mutex>
+
 #include "gemv_core.h"
 #include "kernels.h"
 #include "layer.h"
@@ -1927,6 +1929,81 @@ bool layer_fused_ok(int fmt, int T, int k, int E, int H, int I) {
     return false;
   // dynamic LDS beside the static routing tables (~19 KB) within 160 KB
   return layer_fused_lds(fmt, T, E, H, I) <= 140 * 1024;
+}
+
+// ---------------------------------------------------------------- no-alloc
+// Hand-off region of moe_layer_noalloc: one static array, which every GPU
+// the library runs on holds at its own address until the process ends.  In
+// host code the array's name is not a device address: the address comes
+// from hipGetSymbolAddress, taken once per device with that device current,
+// and only that address is used (kernel arguments, the clear below).
+static __device__ __align__(256) uint8_t scratch[MOE_LAYER_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch[kMaxDevices] = {};
+
+__global__ __launch_bounds__(256) void clear_words_kernel(u32x4* p, int64_t n) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += int64_t(gridDim.x) * blockDim.x)
+    p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+hipError_t clear_region(uint8_t* p, hipStream_t st) {
+  // a fill kernel rather than a memset node, so that a captured first call
+  // records a kernel
+  hipLaunchKernelGGL(clear_words_kernel, dim3(256), dim3(256), 0, st, reinterpret_cast<u32x4*>(p),
+                     int64_t(MOE_LAYER_SCRATCH_BYTES / 16));
+  return hipGetLastError();
+}
+
+// The current device's region: its address on first use (then cleared on
+// st, ahead of the call that follows on st).
+hipError_t scratch_of_device(hipStream_t st, uint8_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    e = clear_region(static_cast<uint8_t*>(p), st);
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = static_cast<uint8_t*>(p);
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_layer_noalloc(LayerArgs a, int fmt, hipStream_t st) {
+  uint8_t* region = nullptr;
+  const hipError_t e = scratch_of_device(st, &region);
+  if (e != hipSuccess) return e;
+  a.region = region;
+  return launch_layer_fused(a, fmt, st, nullptr);
+}
+
+hipError_t layer_scratch_address(uint8_t** ptr) {
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  *ptr = g_scratch[dev];
+  return hipSuccess;
+}
+
+hipError_t layer_scratch_clear(hipStream_t st) {
+  uint8_t* p = nullptr;
+  const hipError_t e = layer_scratch_address(&p);
+  if (e != hipSuccess || !p) return e;
+  return clear_region(p, st);
 }
 
 hipError_t launch_layer_fused(const LayerArgs& a, int fmt, hipStream_t st, int* grid) {
