@@ -294,9 +294,13 @@ def bench_decode(args, cfg_name, steps=None, warmup=None, cpu_calls=None):
 
 PHASES = [(0, "start"), (2, "tokens staged"), (3, "router/shared tasks (wave 0)"),
           (4, "every logit seen (wave 0)"), (11, "every logit seen (all waves)"),
+          (16, "  routing: candidates listed"), (17, "  routing: second barrier"),
+          (18, "  routing: ranks"), (19, "  routing: gates"), (20, "  routing: resolved"),
           (5, "routing done"), (6, "gate/up done (wave 0)"), (7, "gate/up done (last wave)"),
-          (12, "down phase entered"), (13, "first unit's h present"), (8, "first h staged"),
-          (9, "down done"), (10, "end")]
+          (12, "down phase entered"), (24, "  down: LDS free (barrier)"),
+          (25, "  down: h sources set (barrier)"), (13, "first unit's h present"),
+          (26, "  down: h converted (thread 0)"), (27, "  down: staging barrier"),
+          (8, "first h staged"), (9, "down done"), (10, "end")]
 
 
 def phase_trace(n_calls, run_step, first_step, n_distinct):
@@ -306,8 +310,9 @@ def phase_trace(n_calls, run_step, first_step, n_distinct):
     median over calls; and each XCD's median start offset (us)."""
     import torch
     import routed_expert_ffn_gemv_amd as moe
-    tr = torch.zeros((1024, 16), dtype=torch.int64, device="cuda")
+    tr = torch.zeros((1024, 32), dtype=torch.int64, device="cuda")
     per_phase = {name: [] for _, name in PHASES}
+    polls = {"lg": [], "h": []}
     xcd_start = {}
     moe.moe_set_trace(tr)
     try:
@@ -326,11 +331,15 @@ def phase_trace(n_calls, run_step, first_step, n_distinct):
                 v = v[v > 0]
                 if len(v):
                     per_phase[name].append((np.median(v - t0) / 100.0, (v.max() - t0) / 100.0))
+            polls["lg"] += [int(v) for v in t[:, 15] if v > 0]
+            polls["h"] += [int(v) for v in t[:, 14] if v > 0]
             for x in np.unique(t[:, 1]):
                 xcd_start.setdefault(int(x), []).append(np.median(t[t[:, 1] == x, 0] - t0) / 100.0)
     finally:
         moe.moe_set_trace(None)
     res = {"calls": len(per_phase["start"]), "unit": "us since the first workgroup started",
+           "poll_rounds_median": {"logits (thread 0)": float(np.median(polls["lg"])) if polls["lg"] else None,
+                                  "first h (thread 0)": float(np.median(polls["h"])) if polls["h"] else None},
            "phases": {name: {"median_over_wgs": round(float(np.median([a for a, _ in v])), 2),
                              "max_over_wgs": round(float(np.median([b for _, b in v])), 2)}
                       for name, v in per_phase.items() if v},
@@ -342,6 +351,7 @@ def phase_trace(n_calls, run_step, first_step, n_distinct):
     for name, v in res["phases"].items():
         log(f"| {name} | {v['median_over_wgs']:.2f} | {v['max_over_wgs']:.2f} |")
     log("XCD start offsets: " + ", ".join(f"{x}: {v:.2f}" for x, v in res["xcd_start_median"].items()))
+    log(f"poll rounds (median over workgroups and calls): {res['poll_rounds_median']}")
     return res
 
 

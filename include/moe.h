@@ -234,14 +234,17 @@ moe_status moe_layer_check(const void* ws, size_t ws_bytes, void* stream);
 void moe_set_wait_budget(uint64_t ns, int32_t hold);
 
 /* Diagnostics: phase stamps of later fused moe_layer launches.  trace is a
- * device buffer of 16 uint64 words per workgroup of the launch (one per
+ * device buffer of 32 uint64 words per workgroup of the launch (one per
  * compute unit; 1024 rows always suffice), or NULL to stop.  Row b holds
  * workgroup b's real-time counter stamps (100 MHz) at: 0 start, 2 tokens
  * staged, 3 router/shared tasks of wave 0 done, 4 every logit seen by wave 0,
  * 11 by every wave, 5 routing done, 6 wave 0's gate/up done, 7 the last
  * wave's gate/up done, 12 down phase entered, 13 the first down unit's h
  * present, 8 first h staged, 9 down done, 10 end; word 1 is the XCD it ran
- * on.
+ * on, words 14 and 15 thread 0's poll rounds for that h and (one token)
+ * for the logits; words 16-20 steps of one-token routing (candidates
+ * listed, second barrier, ranks, gates, resolution) and 24-27 steps of the
+ * first down unit's staging (two barriers, h converted, staging barrier).
  * Every launch overwrites the rows it writes.  Process-wide, read when a
  * call is issued. */
 void moe_set_trace(uint64_t* trace);

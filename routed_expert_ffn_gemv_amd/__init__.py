@@ -264,7 +264,7 @@ def moe_set_wait_budget(ns=0, hold=False):
 
 def moe_set_trace(trace):
     """Phase stamps of later fused moe_layer launches into trace (a uint64-
-    sized int64 device tensor of [1024][16] words), or None to stop."""
+    sized int64 device tensor of [1024][32] words), or None to stop."""
     lib.moe_set_trace(_ptr(trace))
 
 

@@ -82,7 +82,20 @@ enum TraceSlot {
   kTrLogitsAll = 11,   // every wave has seen every logit (the barrier after the polls)
   kTrDStart = 12,      // down phase entered (the workgroup's gate/up tasks issued and done)
   kTrHPolled = 13,     // the first down unit's h all present (thread 0's poll)
-  kTraceSlots = 16
+  kTrHPolls = 14,      // thread 0's poll rounds for that h (a count, not a time)
+  kTrLgPolls = 15,     // thread 0's poll rounds for the logits (a count)
+  // one-token routing, step by step
+  kTrRtCand = 16,      // candidates listed (before the second barrier)
+  kTrRtBar2 = 17,      // after the second barrier
+  kTrRtRank = 18,      // ranks taken, choices moved to their lanes
+  kTrRtGate = 19,      // gates made
+  kTrRtResolved = 20,  // slots and miss list resolved
+  // first down unit
+  kTrDBar1 = 24,       // after the barrier that ends the LDS use of gate/up
+  kTrDBar2 = 25,       // after the barrier that publishes the h sources
+  kTrHConv = 26,       // h converted and stored in LDS (thread 0)
+  kTrHBar = 27,        // after the staging barrier
+  kTraceSlots = 32
 };
 
 // Byte offsets in the region header.

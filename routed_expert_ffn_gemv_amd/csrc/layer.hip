@@ -427,6 +427,7 @@ __device__ __forceinline__ void stage_h(const uint64_t* const* srcs, int n, int 
         for (int c = 0; c < 16; ++c) ok = ok && (!src[r] || tag_ok(wv[r][c], epoch));
       return ok;
     };
+    int rounds = 1;
     while (!all_here() && keep_waiting(a, L, t0)) {
       __builtin_amdgcn_s_sleep(1);
 #pragma unroll
@@ -434,8 +435,12 @@ __device__ __forceinline__ void stage_h(const uint64_t* const* srcs, int n, int 
 #pragma unroll
         for (int c = 0; c < 16; ++c)
           if (src[r] && !tag_ok(wv[r][c], epoch)) wv[r][c] = ld_dev(src[r] + c);
+      ++rounds;
     }
-    if (base == 0 && trace_h) stamp_now(a.trace, kTrHPolled);
+    if (base == 0 && trace_h) {
+      stamp_now(a.trace, kTrHPolled);
+      stamp(a.trace, kTrHPolls, uint64_t(rounds));
+    }
 #pragma unroll
     for (int r = 0; r < kIt; ++r) {
       const int it = base + r * kThreads + threadIdx.x;
@@ -491,6 +496,7 @@ __device__ __forceinline__ void stage_h(const uint64_t* const* srcs, int n, int 
       }
     }
   }
+  if (trace_h) stamp_now(a.trace, kTrHConv);
   __syncthreads();
   if (FMT != MOE_W_F32) {
     const int nb = K / 32;
@@ -1230,6 +1236,7 @@ __device__ __forceinline__ void route_token(const LayerArgs& a, float* lg, int E
 #pragma unroll
   for (int r = 0; r < kR; ++r)
     if (tid + r * kThreads < E) w[r] = ld_dev(region_lg(a) + tid + r * kThreads);
+  int rounds = 1;
   for (;;) {
     bool ok = true;
 #pragma unroll
@@ -1240,8 +1247,12 @@ __device__ __forceinline__ void route_token(const LayerArgs& a, float* lg, int E
     for (int r = 0; r < kR; ++r)
       if (tid + r * kThreads < E && !tag_ok(w[r], epoch))
         w[r] = ld_dev(region_lg(a) + tid + r * kThreads);
+    ++rounds;
   }
-  stamp_now(a.trace, kTrLogits);
+  if (a.trace) {
+    stamp_now(a.trace, kTrLogits);
+    stamp(a.trace, kTrLgPolls, uint64_t(rounds));
+  }
   uint64_t key[kR];   // 0: no expert
   uint32_t m = 0u;    // largest logit bits of the thread
 #pragma unroll
@@ -1297,7 +1308,9 @@ __device__ __forceinline__ void route_token(const LayerArgs& a, float* lg, int E
       }
     }
   }
+  stamp_now(a.trace, kTrRtCand);
   __syncthreads();
+  stamp_now(a.trace, kTrRtBar2);
   // The count, this lane's candidate and the first eight candidates are
   // read together; list slots past the count hold key 0 (zeroed before the
   // first barrier), which is below every key.
@@ -1325,6 +1338,7 @@ __device__ __forceinline__ void route_token(const LayerArgs& a, float* lg, int E
     const uint32_t lo = uint32_t(__builtin_amdgcn_ds_permute(to, int(uint32_t(ck))));
     my_e = int(~lo);
     my_v = key_value(hi);
+    stamp_now(a.trace, kTrRtRank);
   } else if (E <= 512) {
     wave_topk<8>(lg, E, k, lane, &my_e, &my_v);
   } else {
@@ -1338,6 +1352,7 @@ __device__ __forceinline__ void route_token(const LayerArgs& a, float* lg, int E
   const float vmax = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_v), 0));
   const float ex = lane < k ? __expf(my_v - vmax) : 0.f;
   const float g = ex * __frcp_rn(wave_sum_f32(ex));
+  stamp_now(a.trace, kTrRtGate);
   const bool out = writer && wave == 0;
   if (lane < k) {
     L.idx[lane] = my_e;
@@ -1349,6 +1364,7 @@ __device__ __forceinline__ void route_token(const LayerArgs& a, float* lg, int E
   }
   resolve_one(a, L, my_e, g, lane, out);
   wave_lds_sync();
+  stamp_now(a.trace, kTrRtResolved);
 }
 
 // Resolution of the P = T*k pairs of T >= 2 tokens (thread p = pair p).
@@ -1802,13 +1818,16 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
       const int r = rb * kRowsD + wave * (64 / kLprD) + lane / kLprD;
       if (u != staged) {
         __syncthreads();   // gate/up tasks and the previous unit are done with the LDS
+        if (staged < 0) stamp_now(a.trace, kTrDBar1);
         if (tid < n)
           srcs[tid] = shared ? region_h_sh(a) + int64_t(tid) * Kd
                              : region_h(a) + int64_t(L.bpair[st + tid]) * Kd;
         __syncthreads();
+        if (staged < 0) stamp_now(a.trace, kTrDBar2);
         stage_h<FMT>(srcs, n, Kd, xd, sd, pd, bsc, vs_d, epoch, a, L, t0, staged < 0);
         __syncthreads();
         if (staged < 0 && a.trace) {
+          stamp(a.trace, kTrHBar, __builtin_amdgcn_s_memrealtime());
           stamp(a.trace, kTrStagedH, __builtin_amdgcn_s_memrealtime());
           stamp(a.trace, kTrGateUpAll, L.t_gu);
         }
