@@ -621,7 +621,10 @@ def bench_prefill(args, cfg_name, steps=None, warmup=None):
     steps = args.steps if steps is None else steps
     warmup = args.warmup if warmup is None else warmup
 
-    def step(times=None):
+    def step(mode, times=None):
+        """One prefill step.  pairs: moe_expert_ffn writes every pair's output
+        and moe_combine sums them; accum: y is zeroed and
+        moe_expert_ffn_accum adds the gate-weighted outputs into it."""
         if times is not None:
             ev[0].record(stream)
         moe.moe_route(desc, x, T, idx, gate, ws, stream)
@@ -630,29 +633,39 @@ def bench_prefill(args, cfg_name, steps=None, warmup=None):
         moe.moe_resolve_slots(desc, idx, gate, T, slot_idx, boff, bpair, miss, moff, ws, stream)
         if times is not None:
             ev[2].record(stream)
-        moe.moe_expert_ffn(desc, x, T, boff, bpair, pair_out, shared_out, ws, stream)
+        if mode == "pairs":
+            moe.moe_expert_ffn(desc, x, T, boff, bpair, pair_out, shared_out, ws, stream)
+        else:
+            y.zero_()
+            moe.moe_expert_ffn_accum(desc, x, T, boff, bpair, gate, y, ws, stream)
         if times is not None:
             ev[3].record(stream)
-        moe.moe_combine(desc, T, slot_idx, gate, pair_out, shared_out, y, stream)
+        if mode == "pairs":
+            moe.moe_combine(desc, T, slot_idx, gate, pair_out, shared_out, y, stream)
         if times is not None:
             ev[4].record(stream)
             torch.cuda.synchronize()
             times.append([ev[i].elapsed_time(ev[i + 1]) for i in range(4)])
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    parts = []
-    for _ in range(3):
-        step(parts)
-    parts = np.median(np.array(parts), axis=0)
+    modes = ["pairs", "accum"] if args.prefill_mode == "both" else [args.prefill_mode]
+    res = {}
+    for mode in modes:
+        for _ in range(warmup):
+            step(mode)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            step(mode)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        parts = []
+        for _ in range(3):
+            step(mode, parts)
+        res[mode] = (e0.elapsed_time(e1) / steps, np.median(np.array(parts), axis=0))
+        log(f"[bench] prefill ({mode}): {res[mode][0]:.4f} ms per step, parts {res[mode][1]}")
+    best = min(res, key=lambda m: res[m][0])
+    ms, parts = res[best]
     n_hit = int(boff[-1].item())
     flops = gemm_flops(cfg, n_hit, T)
     ffn_ms = float(parts[2])
@@ -668,15 +681,24 @@ def bench_prefill(args, cfg_name, steps=None, warmup=None):
         "data": "synthetic",
         "config": {"workload": cfg.name, "E": E, "k": k, "H": H, "I": cfg.I, "T": T,
                    "weights": cfg.wfmt, "shared_expert": cfg.shared,
-                   "step": "moe_route + moe_resolve_slots + moe_expert_ffn + moe_combine"},
+                   "step": ("moe_route + moe_resolve_slots + moe_expert_ffn + moe_combine"
+                            if best == "pairs" else
+                            "moe_route + moe_resolve_slots + zero y + moe_expert_ffn_accum")},
         "ms_route": round(float(parts[0]), 4), "ms_resolve": round(float(parts[1]), 4),
         "ms_expert_ffn": round(ffn_ms, 4), "ms_combine": round(float(parts[3]), 4),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic(cfg.name, "prefill"),
-                     "kernel": "moe_expert_ffn (grouped gate/up + down GEMMs)",
+                     "traffic": measured_traffic(cfg.name, "prefill") if best == "pairs" else None,
+                     "kernel": ("moe_expert_ffn (grouped gate/up + down GEMMs)" if best == "pairs"
+                                else "zero y + moe_expert_ffn_accum (grouped gate/up + down "
+                                     "GEMMs, combine fused into the down epilogue)"),
                      "flops_per_launch": int(flops)},
     }
+    if len(res) > 1:
+        other = [m for m in res if m != best][0]
+        out["other_path"] = {"mode": other, "ms_per_step": round(res[other][0], 4),
+                             "ms_expert_ffn": round(float(res[other][1][2]), 4),
+                             "ms_combine": round(float(res[other][1][3]), 4)}
     if args.prefill_chunks:
         out["prefill_layer"] = []
         aux = torch.cuda.Stream()
@@ -739,6 +761,9 @@ def main():
     ap.add_argument("--layers", type=int, default=48)
     ap.add_argument("--cpu-tokens", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-mode", default="both", choices=["pairs", "accum", "both"],
+                    help="c5: pair outputs + moe_combine, the fused accumulate path, or both "
+                         "(the faster one is the line; the other is reported beside it)")
     ap.add_argument("--prefill-chunks", default="", metavar="C1,C2,...",
                     help="c5: also time moe_prefill_layer at these chunk sizes, with and "
                          "without a second stream")

@@ -157,6 +157,22 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const uint16_t* x, int32_t
                           float* pair_out, float* shared_out, void* ws, size_t ws_bytes,
                           void* stream);
 
+/* The expert FFN with the combine fused into it ([MD] "長いプロンプトを読む":
+ * prefill streams each expert over all of its tokens, and the GPU sums the
+ * expert results).  y [T][H] fp32 is ACCUMULATED: for every pair p = t*k + j
+ * in a slot's bucket, y[t] += topk_gate[p] * D_s h (h as for moe_expert_ffn),
+ * and y[t] += the shared expert's output (weight 1) when the layer has one.
+ * Pairs in no bucket (misses) add nothing.  With y zeroed first this is
+ * moe_expert_ffn followed by moe_combine, without the [T*k][H] pair outputs
+ * in memory.  The additions are device-scope float atomics, so y's
+ * summation order (and its last bits) can differ from run to run.  Same
+ * paths (GEMV or grouped GEMM), workspace and errors as moe_expert_ffn;
+ * topk_gate [T][k] as moe_route writes it. */
+moe_status moe_expert_ffn_accum(const moe_layer_desc* desc, const uint16_t* x, int32_t T,
+                                const int32_t* bucket_off, const int32_t* bucket_pair,
+                                const float* topk_gate, float* y, void* ws, size_t ws_bytes,
+                                void* stream);
+
 /* Combine ([MD] "1 トークン、三者の分担": the GPU sums the expert results).
  * y[t] = shared_out[t] + sum over j = 0..k-1 with slot_idx[t][j] >= 0 of
  * topk_gate[t][j] * pair_out[t*k+j], j ascending, fp32.  shared_out may be

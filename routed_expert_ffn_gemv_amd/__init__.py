@@ -27,7 +27,8 @@ EXPORTS = ("moe_status_string", "moe_version", "moe_workspace_size", "moe_route"
            "moe_slot_refresh_workspace_size", "moe_slot_refresh", "moe_host_miss_ffn",
            "moe_host_isa", "moe_verify_workspace_size", "moe_verify_accept",
            "moe_prefill_workspace_size", "moe_prefill_layer", "moe_layer_check",
-           "moe_set_wait_budget", "moe_set_trace", "moe_layer_noalloc")
+           "moe_set_wait_budget", "moe_set_trace", "moe_layer_noalloc",
+           "moe_expert_ffn_accum")
 MOE_REFRESH_MAX_SWAPS = 1024
 
 
@@ -87,6 +88,8 @@ def _load():
     lib.moe_resolve_slots.argtypes = [D, P, P, I32, P, P, P, P, P, P, SZ, P]
     lib.moe_expert_ffn.restype = I32
     lib.moe_expert_ffn.argtypes = [D, P, I32, P, P, P, P, P, SZ, P]
+    lib.moe_expert_ffn_accum.restype = I32
+    lib.moe_expert_ffn_accum.argtypes = [D, P, I32, P, P, P, P, P, SZ, P]
     lib.moe_combine.restype = I32
     lib.moe_combine.argtypes = [D, I32, P, P, P, P, P, P]
     lib.moe_layer.restype = I32
@@ -227,6 +230,14 @@ def moe_expert_ffn(desc, x, T, bucket_off, bucket_pair, pair_out, shared_out, ws
                               _ptr(pair_out), _ptr(shared_out), _ptr(ws),
                               ws.numel() if ws is not None else 0, _stream(stream)),
            "moe_expert_ffn")
+
+
+def moe_expert_ffn_accum(desc, x, T, bucket_off, bucket_pair, topk_gate, y, ws, stream=None):
+    """y [T][H] += the gate-weighted expert outputs and the shared expert's."""
+    _check(lib.moe_expert_ffn_accum(desc.ref, _ptr(x), int(T), _ptr(bucket_off),
+                                    _ptr(bucket_pair), _ptr(topk_gate), _ptr(y), _ptr(ws),
+                                    ws.numel() if ws is not None else 0, _stream(stream)),
+           "moe_expert_ffn_accum")
 
 
 def moe_combine(desc, T, slot_idx, topk_gate, pair_out, shared_out, y, stream=None):

@@ -215,10 +215,12 @@ moe_status run_resolve(const moe_layer_desc* d, const int32_t* idx, const float*
   return device_status(e);
 }
 
-// The expert FFN of one bucketed batch (the body of moe_expert_ffn).
+// The expert FFN of one bucketed batch (the body of moe_expert_ffn; with
+// y_acc set, of moe_expert_ffn_accum).
 moe_status run_ffn(const moe_layer_desc* d, const uint16_t* x, int T, const int32_t* bucket_off,
                    const int32_t* bucket_pair, float* pair_out, float* shared_out, void* ws,
-                   const WsLayout& w, hipStream_t st) {
+                   const WsLayout& w, hipStream_t st, float* y_acc = nullptr,
+                   const float* gate = nullptr) {
   FfnArgs a = ffn_args(d, x, T);
   a.act = active_at(ws, w);
   a.active_cap = w.cap;
@@ -227,6 +229,8 @@ moe_status run_ffn(const moe_layer_desc* d, const uint16_t* x, int T, const int3
   a.h_sh = a.h + size_t(T) * d->k * d->I;
   a.pair_out = pair_out;
   a.shared_out = shared_out;
+  a.y_acc = y_acc;
+  a.gate = gate;
   hipError_t e = launch_active_from_offsets(d->num_slots, bucket_off, a.act, st);
   if (e == hipSuccess) {
     if (int64_t(T) * d->k >= kFfnGemmMinPairs && ffn_gemm_ok(a.fmt, d->H, d->I) &&
@@ -406,6 +410,22 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const uint16_t* x, int32_t
   if ((s = check_ws(desc, T, ws, ws_bytes)) != MOE_OK) return s;
   return run_ffn(desc, x, T, bucket_off, bucket_pair, pair_out, shared_out, ws, layout(desc, T),
                  static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_expert_ffn_accum(const moe_layer_desc* desc, const uint16_t* x, int32_t T,
+                                const int32_t* bucket_off, const int32_t* bucket_pair,
+                                const float* topk_gate, float* y, void* ws, size_t ws_bytes,
+                                void* stream) {
+  moe_status s = check_desc(desc);
+  if (s != MOE_OK) return s;
+  if (T < 0) return MOE_ERR_INVALID;
+  if (T > kMaxT) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !aligned(x, 16) || !bucket_off || !bucket_pair || !topk_gate || !y || !aligned(y, 16))
+    return MOE_ERR_INVALID;
+  if ((s = check_ws(desc, T, ws, ws_bytes)) != MOE_OK) return s;
+  return run_ffn(desc, x, T, bucket_off, bucket_pair, nullptr, nullptr, ws, layout(desc, T),
+                 static_cast<hipStream_t>(stream), y, topk_gate);
 }
 
 moe_status moe_combine(const moe_layer_desc* desc, int32_t T, const int32_t* slot_idx,

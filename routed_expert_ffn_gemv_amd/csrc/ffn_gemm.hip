@@ -189,6 +189,8 @@ struct GemmArgs {
   int8_t* he;
   int8_t* hr;
   int P;
+  float* y_acc;             // accumulate mode: y [T][H] += gate * o (else null)
+  const float* gate;        // [T*k]
 };
 
 // Rows of the tile: token (A source row) and output row id.
@@ -567,7 +569,17 @@ __device__ __forceinline__ void qgemm_tile(const GemmArgs& a, const RowMap& rm, 
 #pragma unroll
             for (int c = 0; c < 4; ++c) o4[c] = ldexpf(o4[c], e);
           }
-          __builtin_nontemporal_store(o4, reinterpret_cast<f32x4*>(out + int64_t(orow[i * 32 + r]) * a.H + 4 * c4));
+          const int p = orow[i * 32 + r];
+          if (a.y_acc) {   // the combine, fused: y[t] += gate * o
+            const int t = rm.shared ? p : p / a.k;
+            const float g = rm.shared ? 1.f : a.gate[p];
+            float* yr = a.y_acc + int64_t(t) * a.H + nt * kBNt + 4 * c4;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              __hip_atomic_fetch_add(yr + c, g * o4[c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          } else {
+            __builtin_nontemporal_store(o4, reinterpret_cast<f32x4*>(out + int64_t(p) * a.H + 4 * c4));
+          }
         }
       }
     }
@@ -822,6 +834,8 @@ hipError_t launch_ffn_gemm(const FfnArgs& f, int S, const int32_t* bucket_off, v
   ga.h_sh = h + P * f.I;
   ga.pair_out = f.pair_out;
   ga.shared_out = f.shared_out;
+  ga.y_acc = f.y_acc;
+  ga.gate = f.gate;
   const int has_sh = f.sg.codes != nullptr ? 1 : 0;
   hipLaunchKernelGGL(gemm_schedule_kernel, dim3(1), dim3(1024), 0, st, f.act, f.T, has_sh, tiles,
                      n_tiles);

@@ -104,7 +104,8 @@ __global__ __launch_bounds__(256) void ffn_gateup_kernel(FfnArgs a, int units_pe
 }
 
 // down projection: o = D h for every pair of a bucket (and the shared
-// expert), written to pair_out / shared_out.
+// expert), written to pair_out / shared_out, or (accumulate mode) added
+// into y with the pair's gate.
 template <int FMT, int LPR>
 __global__ __launch_bounds__(256) void ffn_down_kernel(FfnArgs a, int units_per_expert, int np) {
   extern __shared__ uint32_t smem[];
@@ -157,8 +158,15 @@ __global__ __launch_bounds__(256) void ffn_down_kernel(FfnArgs a, int units_per_
           float o = group_sum<LPR>(acc[kVPP * v]);
           if (kSplit) o += group_sum<LPR>(acc[kVPP * v + 1]);
           if (r < a.H && lane_g == 0) {
-            float* out = un.shared ? a.shared_out : a.pair_out;
-            out[int64_t(items[v]) * a.H + r] = o;
+            if (a.y_acc) {   // the combine, fused: y[t] += gate * o
+              const int t = un.shared ? items[v] : items[v] / a.k;
+              const float g = un.shared ? 1.f : a.gate[items[v]];
+              __hip_atomic_fetch_add(a.y_acc + int64_t(t) * a.H + r, g * o, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+              float* out = un.shared ? a.shared_out : a.pair_out;
+              out[int64_t(items[v]) * a.H + r] = o;
+            }
           }
         }
       }

@@ -79,6 +79,11 @@ struct FfnArgs {
   float* h_sh;           // fp32 [T][I]
   float* pair_out;       // fp32 [T*k][H]
   float* shared_out;     // fp32 [T][H]
+  // accumulate mode (y_acc set): y_acc[t] += gate[t*k+j] * o for every hit
+  // pair and += the shared expert's output, with device-scope float atomic
+  // adds; pair_out and shared_out are then unused
+  float* y_acc;          // fp32 [T][H]
+  const float* gate;     // fp32 [T*k]
 };
 hipError_t launch_ffn_gemv(const FfnArgs& a, hipStream_t st);
 

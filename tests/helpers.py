@@ -103,6 +103,20 @@ class DeviceLayer:
                         o["y"])
         return o
 
+    def run_accum(self, o, base=None):
+        """moe_expert_ffn_accum on the buckets of a run_steps result: y =
+        base (zeros by default) + the gate-weighted expert outputs + the
+        shared expert's."""
+        import torch
+        import routed_expert_ffn_gemv_amd as moe
+        T, H = self.T, self.cfg.H
+        y = (torch.zeros((T, H), dtype=torch.float32, device=self.inp["x"].device)
+             if base is None else base.clone())
+        ws = moe.workspace(self.desc, T)
+        moe.moe_expert_ffn_accum(self.desc, self.inp["x"], T, o["bucket_off"], o["bucket_pair"],
+                                 o["gate"], y, ws)
+        return y
+
     def oracle(self, tokens=None, with_misses=False):
         return oracle.layer_from_synth(self.cfg, self.layer, self.inp["x_host"],
                                        slot_of=self.slot_of_host, num_slots=self.S,

@@ -56,10 +56,51 @@ def test_prefill_mid(name):
     assert rowwise_rel_err(host(o["y"]), ref["y"]) <= TOL
 
 
+ACCUM = ["q4_T600", "q2_T517", "gemm_q2_T1100", "gemm_q4_T900_noshared"]
+
+
+@pytest.mark.parametrize("name", ACCUM)
+def test_expert_ffn_accum(name):
+    """moe_expert_ffn_accum (the combine fused into the down projection, by
+    the GEMVs or the grouped GEMMs): y = base + shared + sum of gate * o
+    within tolerance of the oracle, on a nonzero base."""
+    import torch
+    cfg = MID[name]
+    say(f"[gpu] expert FFN, accumulate mode ({name}, {'GEMM' if _uses_gemm(cfg) else 'GEMV'})")
+    x, _ = oracle.margin_x(cfg, 0)
+    L = DeviceLayer(cfg, 0, x=x)
+    o = L.run_steps()
+    ref = L.oracle()
+    base = torch.from_numpy(np.random.default_rng(9).standard_normal((cfg.T, cfg.H))
+                            .astype(np.float32)).cuda()
+    y = L.run_accum(o, base)
+    err = rowwise_rel_err(host(y), host(base).astype(np.float64) + ref["y"])
+    say(f"  rel err {err:.2e}")
+    assert err <= TOL
+
+
+def test_expert_ffn_accum_partial_slots():
+    """Accumulate mode with a partial slot table: misses add nothing."""
+    cfg = PARTIAL_CFG
+    x, _ = oracle.margin_x(cfg, 0)
+    rank = synth.popularity_rank(cfg, 0)
+    resident = np.sort(np.argsort(rank)[:40])
+    slot_of = np.full(cfg.E, -1, np.int32)
+    slot_of[resident] = np.arange(len(resident))
+    from synth import device as sdev
+    pool = sdev.expert_pool(cfg, [0] * len(resident), resident.tolist())
+    L = DeviceLayer(cfg, 0, x=x, pool=pool, slot_of=slot_of, num_slots=len(resident))
+    o = L.run_steps()
+    ref = L.oracle()
+    assert len(ref["miss_expert"]) > 100 and _uses_gemm(cfg)
+    assert rowwise_rel_err(host(L.run_accum(o)), ref["y"]) <= TOL
+
+
 PARTIAL = {
     "gemv": small_cfg(E=64, k=6, H=256, I=128, T=450, wfmt="q4", bias="zipf", seed=44),
     "gemm": small_cfg(E=64, k=6, H=256, I=256, T=800, wfmt="q4", bias="zipf", seed=47),
 }
+PARTIAL_CFG = PARTIAL["gemm"]
 
 
 @pytest.mark.parametrize("name", list(PARTIAL))
@@ -118,8 +159,11 @@ def test_c5_prefill_full_size():
     assert len(tokens) == 1024
     ref = oracle.layer_from_synth(cfg, 0, x, tokens=tokens, route=r, threads=ORACLE_THREADS)
     err = rowwise_rel_err(host(o["y"])[tokens], ref["y"][tokens])
-    say(f"  sampled {len(tokens)} tokens: rel err {err:.2e}")
-    assert err <= TOL
+    y_acc = host(L.run_accum(o))
+    err_acc = rowwise_rel_err(y_acc[tokens], ref["y"][tokens])
+    say(f"  sampled {len(tokens)} tokens: rel err {err:.2e} (pairs + combine), "
+        f"{err_acc:.2e} (accumulate mode)")
+    assert err <= TOL and err_acc <= TOL
 
 
 RANGE = {
