@@ -282,7 +282,9 @@ struct Lds {
   int ncand[kTMax];          // per-token candidate counts
   alignas(16) uint32_t tmp[32];
   int cstart[kWaves + 1];   // this workgroup's waves' gate/up task ranges
-  int dstart[2];            // this workgroup's down unit range
+  int dstart[2];            // this workgroup's down unit range (contiguous split)
+  int dalign[2];            // the same, bucket-aligned split
+  int dzero;                // 1: some bucket got no workgroup in the aligned split
   int n_act;
   uint32_t calls;
   int failed;               // 1: this workgroup gave up a wait; 2: the workspace was poisoned
@@ -1511,6 +1513,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   }
   for (int e = tid; e < kEMax; e += kThreads) L.emask[e] = 0u;
   if (tid < kTMax) L.ncand[tid] = 0;
+  if (tid == 0) L.dzero = 0;
 #pragma unroll
   for (int r = 0; r < kEMax / kThreads; ++r)
     if (tid + r * kThreads < E) L.slot_of[tid + r * kThreads] = so[r];
@@ -1686,12 +1689,36 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
       if (is_c) L.cstart[tid] = v;
       else L.dstart[tid - (kWaves + 1)] = v;
     }
+    // Down units, bucket-aligned: bucket u gets the workgroups [s(u), s(u+1)),
+    // s(u) = floor(G * cum(u) / totD) with cum the cumulative cost, and its
+    // units spread evenly over them -- so a workgroup stages the activations
+    // of one bucket only (a second staging costs a poll round trip and a
+    // conversion, more than a unit).  When some bucket would get no
+    // workgroup, every workgroup keeps the contiguous split above.
+    {
+      const int u = tid - 64;
+      if (u >= 0 && u < n_db) {
+        auto cum_d = [&](int v) {
+          return nrb * (kCostD * v + (v <= n_act ? L.act_start[v] : L.act_start[n_act] + T));
+        };
+        const int s0 = int(int64_t(G) * cum_d(u) / totD);
+        const int s1 = int(int64_t(G) * cum_d(u + 1) / totD);
+        if (s1 == s0) {
+          L.dzero = 1;
+        } else if (b >= s0 && b < s1) {
+          const int w = s1 - s0, j = b - s0;
+          L.dalign[0] = u * nrb + j * nrb / w;
+          L.dalign[1] = u * nrb + (j + 1) * nrb / w;
+        }
+      }
+    }
     __syncthreads();
     c_first = L.cstart[wave];
     c_end = L.cstart[wave + 1];
     c_step = 1;
-    d_first = L.dstart[0];
-    d_end = L.dstart[1];
+    const bool aligned = L.dzero == 0;
+    d_first = aligned ? L.dalign[0] : L.dstart[0];
+    d_end = aligned ? L.dalign[1] : L.dstart[1];
     d_step = 1;
   }
   RowRegs<FMT, kNChD> rd;
