@@ -42,6 +42,29 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+_SLEEP_NS_PER_CYCLE = []
+
+
+def hold_queue(n_launches, per_launch_us=40.0):
+    """Queue a spin kernel on the current stream ahead of a timed region, long
+    enough for the host to enqueue the region's n_launches launches behind
+    it (per_launch_us is a generous bound on the host's cost per launch).
+    The region then runs back to back, and its first event is not stamped
+    while the GPU still waits for the first launch: without this, a short
+    region also times the host's marshalling of its first calls."""
+    import torch
+    if not _SLEEP_NS_PER_CYCLE:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        a.record()
+        torch.cuda._sleep(1 << 20)
+        b.record()
+        torch.cuda.synchronize()
+        _SLEEP_NS_PER_CYCLE.append(a.elapsed_time(b) * 1e6 / (1 << 20))
+    ns = (n_launches * per_launch_us + 2000.0) * 1e3
+    torch.cuda._sleep(int(ns / max(_SLEEP_NS_PER_CYCLE[0], 1e-3)))
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -233,6 +256,7 @@ def bench_decode(args, cfg_name, steps=None, warmup=None, cpu_calls=None):
         step(s, None)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    hold_queue(steps * calls_per_step)
     e0.record(stream)
     for i in range(steps):
         step(warmup + i, slot_rec[i])
@@ -293,7 +317,8 @@ def bench_decode(args, cfg_name, steps=None, warmup=None, cpu_calls=None):
 
 
 PHASES = [(0, "start"), (2, "tokens staged"), (3, "router/shared tasks (wave 0)"),
-          (4, "every logit seen (wave 0)"), (11, "every logit seen (all waves)"),
+          (21, "router/shared tasks (last wave)"), (4, "every logit seen (wave 0)"),
+          (11, "every logit seen (all waves)"),
           (16, "  routing: candidates listed"), (17, "  routing: second barrier"),
           (18, "  routing: ranks"), (19, "  routing: gates"), (20, "  routing: resolved"),
           (5, "routing done"), (6, "gate/up done (wave 0)"), (7, "gate/up done (last wave)"),
@@ -509,6 +534,7 @@ def bench_adaptive(args):
         round_(R + r)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    hold_queue(args.steps * L * 2)
     e0.record(stream)
     for r in range(args.steps):
         round_(R + args.warmup + r)
@@ -654,6 +680,7 @@ def bench_prefill(args, cfg_name, steps=None, warmup=None):
             step(mode)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        hold_queue(steps * 8)
         e0.record(stream)
         for _ in range(steps):
             step(mode)

@@ -258,9 +258,10 @@ void moe_set_wait_budget(uint64_t ns, int32_t hold);
  * wave's gate/up done, 12 down phase entered, 13 the first down unit's h
  * present, 8 first h staged, 9 down done, 10 end; word 1 is the XCD it ran
  * on, words 14 and 15 thread 0's poll rounds for that h and (one token)
- * for the logits; words 16-20 steps of one-token routing (candidates
- * listed, second barrier, ranks, gates, resolution) and 24-27 steps of the
- * first down unit's staging (two barriers, h converted, staging barrier).
+ * for the logits; words 16-20 steps of routing (candidates listed, second
+ * barrier (one token only), ranks, gates, resolution), word 21 the last
+ * wave's router/shared tasks done, and 24-27 steps of the first down
+ * unit's staging (two barriers, h converted, staging barrier).
  * Every launch overwrites the rows it writes.  Process-wide, read when a
  * call is issued. */
 void moe_set_trace(uint64_t* trace);

@@ -84,12 +84,14 @@ enum TraceSlot {
   kTrHPolled = 13,     // the first down unit's h all present (thread 0's poll)
   kTrHPolls = 14,      // thread 0's poll rounds for that h (a count, not a time)
   kTrLgPolls = 15,     // thread 0's poll rounds for the logits (a count)
-  // one-token routing, step by step
-  kTrRtCand = 16,      // candidates listed (before the second barrier)
+  // routing, step by step (17 is stamped for one token only)
+  kTrRtCand = 16,      // candidates listed (one token: before the second barrier;
+                       // several: the threshold selection done)
   kTrRtBar2 = 17,      // after the second barrier
-  kTrRtRank = 18,      // ranks taken, choices moved to their lanes
+  kTrRtRank = 18,      // ranks taken (several tokens: the per-wave fallback done)
   kTrRtGate = 19,      // gates made
   kTrRtResolved = 20,  // slots and miss list resolved
+  kTrTasksAAll = 21,   // the workgroup's last wave's router / shared-expert tasks done
   // first down unit
   kTrDBar1 = 24,       // after the barrier that ends the LDS use of gate/up
   kTrDBar2 = 25,       // after the barrier that publishes the h sources

@@ -289,6 +289,7 @@ struct Lds {
   uint32_t calls;
   int failed;               // 1: this workgroup gave up a wait; 2: the workspace was poisoned
   unsigned long long t_gu;  // trace: latest gate/up end over the waves
+  unsigned long long t_a;   // trace: latest router / shared-expert task end over the waves
 };
 
 // Phase stamp (thread 0 of the workgroup; nothing when tracing is off).
@@ -312,15 +313,66 @@ __device__ __forceinline__ bool keep_waiting(const LayerArgs& a, Lds& L, uint64_
 }
 
 // --------------------------------------------------------------- staging
+// Code pairs of a 2-bit code dword by class.  Pair s (codes s and s + 8)
+// is taken from the dword shifted right by 6 * (s / 3), masked to its two
+// fields at bits 2c and 16 + 2c, c = s % 3, and OR-ed into the mantissa of
+// bf16(128): the pair is 128 + q * 4^c, exact, from one shift per three
+// pairs and one AND-OR per pair.  The staged tokens carry the matching
+// factor: pair s of a token is x * 4^-c (exact), so a block dot product of
+// the pairs is sum q x + 128 * sum x', x' the staged values.
+__device__ __forceinline__ int q2_class(int s) { return s % 3; }
+// (a & m) | c as one v_and_or_b32.  Written out because with a literal mask
+// and a literal c the compiler splits it into an AND and an OR (a
+// three-operand VALU instruction takes no literal on this architecture);
+// here the mask sits in a scalar register and c in a vector register, both
+// set up once.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(c));
+  return r;
+}
+__device__ __forceinline__ uint32_t q2_pair_cls(uint32_t w, int s) {
+  return and_or(w >> (6 * (s / 3)), 0x00030003u << (2 * q2_class(s)), kMagic128x2);
+}
+// fp16 code pairs by class, for the class-staged h (fp16 1024 = 0x6400 has
+// ten mantissa bits of weight 1 .. 512).  2-bit codes, pair s (codes s and
+// s + 8): class c = s for s < 5 (fields at bits 2c, 16 + 2c), else s - 5
+// from the dword shifted right by 10; the pair is 1024 + q * 4^c.  4-bit
+// codes, pair s (codes s and s + 4): class c = s & 1 from the dword shifted
+// right by 8 * (s >> 1); the pair is 1024 + q * 16^c.  One shift per five
+// (two) pairs and one AND-OR per pair; h is staged as h * 4^-c (16^-c).
+template <int FMT>
+__device__ __forceinline__ int f16_class(int s) {
+  return FMT == MOE_W_Q2B32 ? (s < 5 ? s : s - 5) : (s & 1);
+}
+template <int FMT>
+__device__ __forceinline__ uint32_t f16_pair_cls(uint32_t w, int s) {
+  if constexpr (FMT == MOE_W_Q2B32)
+    return and_or(w >> (s < 5 ? 0 : 10), 0x00030003u << (2 * f16_class<FMT>(s)), 0x64006400u);
+  else
+    return and_or(w >> (8 * (s >> 1)), 0x000F000Fu << (4 * (s & 1)), 0x64006400u);
+}
+// A bf16 pair times 2^-e2 (both halves).  The fp32 products are exact, so
+// their top halves are the bf16 results (for results below the normal
+// range, truncated).
+__device__ __forceinline__ uint32_t bf16x2_scaled(uint32_t p, int e2) {
+  const float f = __uint_as_float(uint32_t(127 - e2) << 23);
+  const uint32_t lo = __float_as_uint(__uint_as_float(p << 16) * f);
+  const uint32_t hi = __float_as_uint(__uint_as_float(p & 0xFFFF0000u) * f);
+  return __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+}
+
 // Tokens into the expert format's LDS layout, with 32-byte loads per
-// thread (16 columns of one token) issued before any is used.  psum holds
-// each 16-column group's sum; block sums add two groups in a fixed order.
-// The caller synchronises before reading xs or psum.
+// thread (16 columns of one token) issued before any is used.  xsum gets
+// each 32-column block's sum of the token's values, xsum2 (2-bit codes)
+// -128 times the sum of the values as staged (x'); the two 16-column groups of a
+// block sit in lanes 2j and 2j + 1 and add in that order.  The caller
+// synchronises before reading xs or the sums.
 // mid() runs once, after the first batch's loads are issued and before they
 // are used.
 template <int FMT, typename Mid>
 __device__ __forceinline__ void stage_tokens(const uint16_t* __restrict__ x, int T, int H, uint32_t* xs,
-                                             float* psum, int vstride, Mid mid) {
+                                             float* xsum, float* xsum2, int vstride, Mid mid) {
   const int per_tok = H / 16;
   const int n_items = T * per_tok;
   constexpr int kR = 4;
@@ -333,77 +385,93 @@ __device__ __forceinline__ void stage_tokens(const uint16_t* __restrict__ x, int
         const u32x4* src = reinterpret_cast<const u32x4*>(x + int64_t(it) * 16);
         w[r][0] = src[0];
         w[r][1] = src[1];
+      } else {
+        w[r][0] = u32x4{0u, 0u, 0u, 0u};
+        w[r][1] = u32x4{0u, 0u, 0u, 0u};
       }
     }
     if (base == 0) mid();
 #pragma unroll
     for (int r = 0; r < kR; ++r) {
       const int it = base + r * kThreads + threadIdx.x;
-      if (it >= n_items) continue;
+      const bool on = it < n_items;   // the same for lanes 2j and 2j + 1
       const int t = it / per_tok, g16 = it % per_tok;
-      float s = 0.f;
+      float s = 0.f, s2 = 0.f;
 #pragma unroll
       for (int q = 0; q < 2; ++q)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           s += bf16_to_f32(w[r][q][e] & 0xFFFFu) + bf16_to_f32(w[r][q][e] >> 16);
-      psum[t * per_tok + g16] = s;
       if constexpr (FMT == MOE_W_F32) {
-        float* xf = reinterpret_cast<float*>(xs) + t * vstride + g16 * 16;
+        if (on) {
+          float* xf = reinterpret_cast<float*>(xs) + t * vstride + g16 * 16;
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
+          for (int q = 0; q < 2; ++q)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            xf[q * 8 + 2 * e] = bf16_to_f32(w[r][q][e] & 0xFFFFu);
-            xf[q * 8 + 2 * e + 1] = bf16_to_f32(w[r][q][e] >> 16);
-          }
+            for (int e = 0; e < 4; ++e) {
+              xf[q * 8 + 2 * e] = bf16_to_f32(w[r][q][e] & 0xFFFFu);
+              xf[q * 8 + 2 * e + 1] = bf16_to_f32(w[r][q][e] >> 16);
+            }
+        }
       } else if constexpr (FMT == MOE_W_Q2B32) {
-        // pairs (s, s+8), s < 8, of this 16-column group
-        uint32_t* d = xs + t * vstride + (g16 >> 2) * Fmt<FMT>::kCS + (g16 & 3) * 8;
+        // pairs (s, s+8), s < 8, of this 16-column group, pair s times 4^-(s % 3)
+        uint32_t pr[8];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          d[2 * m] = __builtin_amdgcn_perm(w[r][1][m], w[r][0][m], 0x05040100u);
-          d[2 * m + 1] = __builtin_amdgcn_perm(w[r][1][m], w[r][0][m], 0x07060302u);
+          pr[2 * m] = __builtin_amdgcn_perm(w[r][1][m], w[r][0][m], 0x05040100u);
+          pr[2 * m + 1] = __builtin_amdgcn_perm(w[r][1][m], w[r][0][m], 0x07060302u);
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          if (q2_class(q) != 0) pr[q] = bf16x2_scaled(pr[q], 2 * q2_class(q));
+          s2 += bf16_to_f32(pr[q] & 0xFFFFu) + bf16_to_f32(pr[q] >> 16);
+        }
+        if (on) {
+          uint32_t* d = xs + t * vstride + (g16 >> 2) * Fmt<FMT>::kCS + (g16 & 3) * 8;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) d[q] = pr[q];
         }
       } else {
         // two 8-column groups, pairs (s, s+4), s < 4
+        if (on) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          uint32_t* d = xs + t * vstride + (g16 >> 1) * Fmt<FMT>::kCS + ((g16 & 1) * 2 + q) * 4;
+          for (int q = 0; q < 2; ++q) {
+            uint32_t* d = xs + t * vstride + (g16 >> 1) * Fmt<FMT>::kCS + ((g16 & 1) * 2 + q) * 4;
 #pragma unroll
-          for (int m = 0; m < 2; ++m) {
-            d[2 * m] = __builtin_amdgcn_perm(w[r][q][2 + m], w[r][q][m], 0x05040100u);
-            d[2 * m + 1] = __builtin_amdgcn_perm(w[r][q][2 + m], w[r][q][m], 0x07060302u);
+            for (int m = 0; m < 2; ++m) {
+              d[2 * m] = __builtin_amdgcn_perm(w[r][q][2 + m], w[r][q][m], 0x05040100u);
+              d[2 * m + 1] = __builtin_amdgcn_perm(w[r][q][2 + m], w[r][q][m], 0x07060302u);
+            }
           }
         }
+      }
+      // block sums: group 2b (even lane) + group 2b + 1 (odd lane)
+      const float sp = dpp_f32<0xB1>(s), sp2 = dpp_f32<0xB1>(s2);   // quad_perm [1,0,3,2]
+      if (on && (g16 & 1) == 0) {
+        xsum[t * (H / 32) + (g16 >> 1)] = s + sp;
+        if constexpr (FMT == MOE_W_Q2B32) xsum2[t * (H / 32) + (g16 >> 1)] = -128.f * (s2 + sp2);
       }
     }
   }
 }
 
-// Block sums of the staged tokens (after a barrier that follows stage_tokens).
-__device__ __forceinline__ void token_block_sums(int T, int H, float* xsum, const float* psum) {
-  const int nb = H / 32, per_tok = H / 16;
-  for (int i = threadIdx.x; i < T * nb; i += kThreads) {
-    const int t = i / nb, b = i % nb;
-    xsum[t * nb + b] = psum[t * per_tok + 2 * b] + psum[t * per_tok + 2 * b + 1];
-  }
-}
-
-
 // Tagged fp32 vectors published by other workgroups (h), staged for the
 // down projection, 16 columns per item.  Quantised formats: fp16 in the pair
 // layout, each 32-column block scaled by a power of two that brings its
-// largest |h| into [0.5, 1) (bsc keeps the inverse, psum the sums of the
-// stored values), so no block overflows fp16 and each keeps 11 bits
-// relative to its largest value.  F32 format: plain fp32.
+// largest |h| into [128, 256) (bsc keeps the inverse), so no block
+// overflows fp16 and each keeps 11 bits relative to its largest value; pair
+// s is stored times 4^-c (2-bit codes) or 16^-c (4-bit codes), c its code
+// class, so even the smallest class factor leaves the block maximum a
+// normal fp16 number.  sd gets the block sums of h (the scaled values
+// times bsc), sd2 -1024 bsc times the block sums of the values as stored.
+// F32 format: plain fp32.
 // All loads of a batch are issued first; words that do not yet carry this
 // call's number are read again until they do (their producers never wait
-// on anything, so this ends).  Every thread calls it (the block maxima pass
-// between neighbouring lanes).
+// on anything, so this ends).  Every thread calls it (the block sums and
+// maxima pass between neighbouring lanes).
 template <int FMT>
 __device__ __forceinline__ void stage_h(const uint64_t* const* srcs, int n, int K, uint32_t* xd,
-                                        float* sd, float* psum, float* bsc, int vs,
+                                        float* sd, float* sd2, float* bsc, int vs,
                                         uint32_t epoch, const LayerArgs& a, Lds& L, uint64_t t0,
                                         bool trace_h) {
   const int per_vec = K / 16;
@@ -464,34 +532,49 @@ __device__ __forceinline__ void stage_h(const uint64_t* const* srcs, int n, int 
         for (int c = 0; c < 16; ++c) amax = fmaxf(amax, fabsf(v[c]));
         amax = fmaxf(amax, dpp_f32<0xB1>(amax));   // quad_perm [1,0,3,2]
         uint32_t ex = (__float_as_uint(amax) >> 23) & 0xFFu;
-        ex = ex > 253u ? 253u : ex;
-        // amax in [2^(ex-127), 2^(ex-126)): scale by 2^(126-ex); zero and
-        // subnormal maxima keep scale 1
-        const float sc = ex == 0u ? 1.f : __uint_as_float((253u - ex) << 23);
-        const float inv = ex == 0u ? 1.f : __uint_as_float((ex + 1u) << 23);
+        ex = ex < 8u ? 8u : (ex > 253u ? 253u : ex);
+        // amax in [2^(ex-127), 2^(ex-126)): scale by 2^(134-ex) (zero and
+        // tiny maxima take the smallest exponent, 8)
+        const float sc = __uint_as_float((261u - ex) << 23);
+        const float inv = __uint_as_float((ex - 7u) << 23);
+        // pair q: columns (q, q + 8) (2-bit codes) or (8g + e, 8g + e + 4)
+        // (4-bit codes, q = 4g + e); stored times 2^-cls
+        uint32_t hp[8];
+        float sum = 0.f, sum2 = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int lo = FMT == MOE_W_Q2B32 ? q : 8 * (q >> 2) + (q & 3);
+          const int hi = FMT == MOE_W_Q2B32 ? q + 8 : lo + 4;
+          const int cls = FMT == MOE_W_Q2B32 ? 2 * f16_class<FMT>(q) : 4 * f16_class<FMT>(q & 3);
+          const float scq = sc * __uint_as_float(uint32_t(127 - cls) << 23);
+          const _Float16 h0 = static_cast<_Float16>(v[lo] * scq);
+          const _Float16 h1 = static_cast<_Float16>(v[hi] * scq);
+          hp[q] = uint32_t(__builtin_bit_cast(uint16_t, h0)) |
+                  (uint32_t(__builtin_bit_cast(uint16_t, h1)) << 16);
+          const float p2 = static_cast<float>(h0) + static_cast<float>(h1);
+          sum2 += p2;
+          sum += p2 * __uint_as_float(uint32_t(127 + cls) << 23);
+        }
+        // block sums: group 2b (even lane) + group 2b + 1 (odd lane)
+        const float sp = dpp_f32<0xB1>(sum), sp2 = dpp_f32<0xB1>(sum2);
         if (it < n_items) {
           const int p = it / per_vec, g16 = it % per_vec;
-          uint32_t hv[16];
-          float sum = 0.f;
-#pragma unroll
-          for (int c = 0; c < 16; ++c) {
-            const _Float16 hh = static_cast<_Float16>(v[c] * sc);
-            hv[c] = __builtin_bit_cast(uint16_t, hh);
-            sum += static_cast<float>(hh);
+          if ((g16 & 1) == 0) {
+            bsc[p * (K / 32) + (g16 >> 1)] = inv;
+            sd[p * (K / 32) + (g16 >> 1)] = inv * (sum + sp);
+            sd2[p * (K / 32) + (g16 >> 1)] = -1024.f * inv * (sum2 + sp2);
           }
-          psum[p * per_vec + g16] = sum;
-          if ((g16 & 1) == 0) bsc[p * (K / 32) + (g16 >> 1)] = inv;
           uint32_t* dh = xd + p * vs;
           if constexpr (FMT == MOE_W_Q2B32) {
             const int off = (g16 >> 2) * Fmt<FMT>::kCS + (g16 & 3) * 8;
 #pragma unroll
-            for (int q = 0; q < 8; ++q) dh[off + q] = hv[q] | (hv[q + 8] << 16);
+            for (int q = 0; q < 8; ++q) dh[off + q] = hp[q];
           } else {
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
               const int off = (g16 >> 1) * Fmt<FMT>::kCS + ((g16 & 1) * 2 + q) * 4;
 #pragma unroll
-              for (int t = 0; t < 4; ++t) dh[off + t] = hv[8 * q + t] | (hv[8 * q + t + 4] << 16);
+              for (int t = 0; t < 4; ++t) dh[off + t] = hp[4 * q + t];
             }
           }
         }
@@ -499,14 +582,6 @@ __device__ __forceinline__ void stage_h(const uint64_t* const* srcs, int n, int 
     }
   }
   if (trace_h) stamp_now(a.trace, kTrHConv);
-  __syncthreads();
-  if (FMT != MOE_W_F32) {
-    const int nb = K / 32;
-    for (int i = threadIdx.x; i < n * nb; i += kThreads) {
-      const int v = i / nb, b = i % nb;
-      sd[v * nb + b] = psum[v * per_vec + 2 * b] + psum[v * per_vec + 2 * b + 1];
-    }
-  }
 }
 
 // --------------------------------------------------------------- row tiles
@@ -540,143 +615,35 @@ __device__ __forceinline__ void load_row(RowRegs<FMT, NCH>& R, const uint8_t* __
   }
 }
 
-// Block dot products of one 16-byte code chunk with one staged vector.
-// Q2: 64 codes = two 32-weight blocks, pairs (s, s+8) of each code dword;
-// Q4: 32 codes = one block, pairs (s, s+4).  Returns sum (128 + q) x per
-// block in p[0..1]; independent accumulators keep the dot2 chains short.
-template <int FMT>
-__device__ __forceinline__ void chunk_dot(u32x4 w, const uint32_t* xv, float* p) {
-  w = fresh(w);   // unpack per vector; keeping every unpacked pair costs more registers
-  const u32x4* x4 = reinterpret_cast<const u32x4*>(xv);
-#pragma unroll
-  for (int bb = 0; bb < (FMT == MOE_W_Q2B32 ? 2 : 1); ++bb) {
-    u32x4 xx[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) xx[q] = x4[4 * bb + q];
-    float a[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t pr = FMT == MOE_W_Q2B32 ? q2_pair(w[2 * bb + (q >> 1)], (q & 1) * 4 + e)
-                                                : q4_pair(w[q], e);
-        a[e] = dot2_bf16(pr, xx[q][e], a[e]);
-      }
-    p[bb] = (a[0] + a[1]) + (a[2] + a[3]);
-  }
-}
-
-// The same for two code chunks (gate and up rows) against one vector chunk.
-template <int FMT>
-__device__ __forceinline__ void chunk_dot2(u32x4 wg, u32x4 wu, const uint32_t* xv,
-                                           float* pg, float* pu) {
-  wg = fresh(wg);
-  wu = fresh(wu);
-  const u32x4* x4 = reinterpret_cast<const u32x4*>(xv);
-#pragma unroll
-  for (int bb = 0; bb < (FMT == MOE_W_Q2B32 ? 2 : 1); ++bb) {
-    u32x4 xx[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) xx[q] = x4[4 * bb + q];
-    float a[4] = {0.f, 0.f, 0.f, 0.f}, c[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int s2 = (q & 1) * 4 + e;
-        const uint32_t prg = FMT == MOE_W_Q2B32 ? q2_pair(wg[2 * bb + (q >> 1)], s2)
-                                                 : q4_pair(wg[q], e);
-        const uint32_t pru = FMT == MOE_W_Q2B32 ? q2_pair(wu[2 * bb + (q >> 1)], s2)
-                                                 : q4_pair(wu[q], e);
-        a[e] = dot2_bf16(prg, xx[q][e], a[e]);
-        c[e] = dot2_bf16(pru, xx[q][e], c[e]);
-      }
-    pg[bb] = (a[0] + a[1]) + (a[2] + a[3]);
-    pu[bb] = (c[0] + c[1]) + (c[2] + c[3]);
-  }
-}
-
-// This lane's part of one row . one staged vector (at xv_base + chunk
-// offsets, block sums at sv_base), over the lane's NCH chunks.
+// This lane's part of one fp32 row . one staged fp32 vector (at xv_base +
+// chunk offsets), over the lane's NCH chunks of 4 columns.
 template <int FMT, int NCH>
 __device__ __forceinline__ float row_vec_dot(const RowRegs<FMT, NCH>& R, int nch, int lane_g,
-                                             int lpr, const uint32_t* xv_base,
-                                             const float* sv_base) {
+                                             int lpr, const uint32_t* xv_base) {
+  static_assert(FMT == MOE_W_F32, "fp32 rows only");
   float acc = 0.f;
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
     if (j >= nch) continue;
     const int c = lane_g + j * lpr;
-    if constexpr (FMT == MOE_W_F32) {
-      const float4 wf = __builtin_bit_cast(float4, R.w[j]);
-      const float* xv = reinterpret_cast<const float*>(xv_base) + 4 * c;
-      acc = fmaf(wf.x, xv[0], fmaf(wf.y, xv[1], fmaf(wf.z, xv[2], fmaf(wf.w, xv[3], acc))));
-    } else if constexpr (FMT == MOE_W_Q2B32) {
-      float p[2];
-      chunk_dot<FMT>(R.w[j], xv_base + c * Fmt<FMT>::kCS, p);
-      const float d0 = f16_to_f32(uint16_t(R.sc[j] & 0xFFFFu));
-      const float d1 = f16_to_f32(uint16_t(R.sc[j] >> 16));
-      const float m0 = f16_to_f32(uint16_t(R.mn[j] & 0xFFFFu)) - 128.f * d0;
-      const float m1 = f16_to_f32(uint16_t(R.mn[j] >> 16)) - 128.f * d1;
-      acc += (d0 * p[0] + m0 * sv_base[2 * c]) + (d1 * p[1] + m1 * sv_base[2 * c + 1]);
-    } else {
-      float p[2];
-      chunk_dot<FMT>(R.w[j], xv_base + c * Fmt<FMT>::kCS, p);
-      const float d = f16_to_f32(uint16_t(R.sc[j]));
-      const float m = f16_to_f32(uint16_t(R.mn[j])) - 128.f * d;
-      acc += d * p[0] + m * sv_base[c];
-    }
+    const float4 wf = __builtin_bit_cast(float4, R.w[j]);
+    const float* xv = reinterpret_cast<const float*>(xv_base) + 4 * c;
+    acc = fmaf(wf.x, xv[0], fmaf(wf.y, xv[1], fmaf(wf.z, xv[2], fmaf(wf.w, xv[3], acc))));
   }
   return acc;
 }
 
-// Gate and up rows . one vector in one pass (one set of LDS reads for both).
-template <int FMT, int NCH>
-__device__ __forceinline__ void row_pair_vec_dot(const RowRegs<FMT, NCH>& RG,
-                                                 const RowRegs<FMT, NCH>& RU, int nch, int lane_g,
-                                                 int lpr, const uint32_t* xv_base,
-                                                 const float* sv_base, float& g, float& u) {
-  if constexpr (FMT == MOE_W_F32) {
-    g = row_vec_dot<FMT, NCH>(RG, nch, lane_g, lpr, xv_base, sv_base);
-    u = row_vec_dot<FMT, NCH>(RU, nch, lane_g, lpr, xv_base, sv_base);
-  } else {
-    g = 0.f;
-    u = 0.f;
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      if (j >= nch) continue;
-      const int c = lane_g + j * lpr;
-      const uint32_t* xv = xv_base + c * Fmt<FMT>::kCS;
-      float pg[2], pu[2];
-      chunk_dot2<FMT>(RG.w[j], RU.w[j], xv, pg, pu);
-      if constexpr (FMT == MOE_W_Q2B32) {
-        const float s0 = sv_base[2 * c], s1 = sv_base[2 * c + 1];
-        const float dg0 = f16_to_f32(uint16_t(RG.sc[j] & 0xFFFFu));
-        const float dg1 = f16_to_f32(uint16_t(RG.sc[j] >> 16));
-        const float du0 = f16_to_f32(uint16_t(RU.sc[j] & 0xFFFFu));
-        const float du1 = f16_to_f32(uint16_t(RU.sc[j] >> 16));
-        g += (dg0 * pg[0] + (f16_to_f32(uint16_t(RG.mn[j] & 0xFFFFu)) - 128.f * dg0) * s0) +
-             (dg1 * pg[1] + (f16_to_f32(uint16_t(RG.mn[j] >> 16)) - 128.f * dg1) * s1);
-        u += (du0 * pu[0] + (f16_to_f32(uint16_t(RU.mn[j] & 0xFFFFu)) - 128.f * du0) * s0) +
-             (du1 * pu[1] + (f16_to_f32(uint16_t(RU.mn[j] >> 16)) - 128.f * du1) * s1);
-      } else {
-        const float s0 = sv_base[c];
-        const float dg = f16_to_f32(uint16_t(RG.sc[j])), du = f16_to_f32(uint16_t(RU.sc[j]));
-        g += dg * pg[0] + (f16_to_f32(uint16_t(RG.mn[j])) - 128.f * dg) * s0;
-        u += du * pu[0] + (f16_to_f32(uint16_t(RU.mn[j])) - 128.f * du) * s0;
-      }
-    }
-  }
-}
-
 // Up to NG tokens at once: the code pairs of a block are unpacked once for
-// the group.  Block scale d and min m enter as d * sum (128 + q) x +
-// (m - 128 d) * sum x, with the block sums of the vectors staged beside them.
+// the group.  Block scale d and min m (w = d q + m):
+//  2-bit codes (class-staged x'): d * (sum (128 + q 4^c) x' - 128 sum x') + m * sum x;
+//  4-bit codes: d * sum (128 + q) x + (m - 128 d) * sum x,
+// with the block sums of the vectors (sum x, and sum x' for 2-bit codes)
+// staged beside them.
 template <int FMT>
 __device__ __forceinline__ void block_scales(uint32_t sc, uint32_t mn, int bb, float& d, float& m) {
   const uint32_t dsh = FMT == MOE_W_Q2B32 ? 16u * uint32_t(bb) : 0u;
   d = f16_to_f32(uint16_t((sc >> dsh) & 0xFFFFu));
-  m = f16_to_f32(uint16_t((mn >> dsh) & 0xFFFFu)) - 128.f * d;
+  m = f16_to_f32(uint16_t((mn >> dsh) & 0xFFFFu));
 }
 template <int FMT>
 __device__ __forceinline__ void unpack_block(u32x4 w, int bb, uint32_t (&pr)[16]) {
@@ -684,8 +651,8 @@ __device__ __forceinline__ void unpack_block(u32x4 w, int bb, uint32_t (&pr)[16]
   for (int q = 0; q < 4; ++q)
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      pr[q * 4 + e] = FMT == MOE_W_Q2B32 ? q2_pair(w[2 * bb + (q >> 1)], (q & 1) * 4 + e)
-                                         : q4_pair(w[q], e);
+      pr[q * 4 + e] = FMT == MOE_W_Q2B32 ? q2_pair_cls(w[2 * bb + (q >> 1)], (q & 1) * 4 + e)
+                                         : and_or(w[q] >> (4 * e), 0x000F000Fu, kMagic128x2);
 }
 // sum over one block of the code pairs . the vector's pairs (4 chains)
 __device__ __forceinline__ float block_dot(const uint32_t (&pr)[16], const u32x4* x4) {
@@ -699,12 +666,14 @@ __device__ __forceinline__ float block_dot(const uint32_t (&pr)[16], const u32x4
   return (a[0] + a[1]) + (a[2] + a[3]);
 }
 
-// Gate and up rows . the vectors xv[v] (block sums sv[v]) of tokens v < nv.
+// Gate and up rows . the vectors xv[v] (block sums sv[v]; -128 times the
+// block sums of the staged values sv2[v]) of tokens v < nv.
 template <int FMT, int NCH, int NG>
 __device__ __forceinline__ void row_pair_vecs_dot(const RowRegs<FMT, NCH>& RG,
                                                   const RowRegs<FMT, NCH>& RU, int nch, int lane_g,
                                                   int lpr, const uint32_t* const (&xv)[NG],
-                                                  const float* const (&sv)[NG], int nv,
+                                                  const float* const (&sv)[NG],
+                                                  const float* const (&sv2)[NG], int nv,
                                                   float (&g)[NG], float (&u)[NG]) {
 #pragma unroll
   for (int v = 0; v < NG; ++v) {
@@ -715,8 +684,8 @@ __device__ __forceinline__ void row_pair_vecs_dot(const RowRegs<FMT, NCH>& RG,
 #pragma unroll
     for (int v = 0; v < NG; ++v)
       if (v < nv) {
-        g[v] = row_vec_dot<FMT, NCH>(RG, nch, lane_g, lpr, xv[v], sv[v]);
-        u[v] = row_vec_dot<FMT, NCH>(RU, nch, lane_g, lpr, xv[v], sv[v]);
+        g[v] = row_vec_dot<FMT, NCH>(RG, nch, lane_g, lpr, xv[v]);
+        u[v] = row_vec_dot<FMT, NCH>(RU, nch, lane_g, lpr, xv[v]);
       }
   } else {
     constexpr int kBlk = FMT == MOE_W_Q2B32 ? 2 : 1;
@@ -731,6 +700,10 @@ __device__ __forceinline__ void row_pair_vecs_dot(const RowRegs<FMT, NCH>& RG,
         float dg, mg, du, mu;
         block_scales<FMT>(RG.sc[j], RG.mn[j], bb, dg, mg);
         block_scales<FMT>(RU.sc[j], RU.mn[j], bb, du, mu);
+        if constexpr (FMT == MOE_W_Q4B32) {
+          mg -= 128.f * dg;
+          mu -= 128.f * du;
+        }
         uint32_t pg[16], pu[16];
         unpack_block<FMT>(wg, bb, pg);
         unpack_block<FMT>(wu, bb, pu);
@@ -739,8 +712,14 @@ __device__ __forceinline__ void row_pair_vecs_dot(const RowRegs<FMT, NCH>& RG,
           if (v >= nv) continue;
           const u32x4* x4 = reinterpret_cast<const u32x4*>(xv[v] + c * Fmt<FMT>::kCS) + 4 * bb;
           const float sx = sv[v][kBlk * c + bb];
-          g[v] += dg * block_dot(pg, x4) + mg * sx;
-          u[v] += du * block_dot(pu, x4) + mu * sx;
+          if constexpr (FMT == MOE_W_Q2B32) {
+            const float sx2 = sv2[v][kBlk * c + bb];   // -128 sum x'
+            g[v] = fmaf(dg, block_dot(pg, x4), fmaf(dg, sx2, fmaf(mg, sx, g[v])));
+            u[v] = fmaf(du, block_dot(pu, x4), fmaf(du, sx2, fmaf(mu, sx, u[v])));
+          } else {
+            g[v] += dg * block_dot(pg, x4) + mg * sx;
+            u[v] += du * block_dot(pu, x4) + mu * sx;
+          }
         }
         __builtin_amdgcn_sched_barrier(0);   // one block's pairs live at a time
       }
@@ -757,17 +736,14 @@ __device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
                                 false);
 }
 
-// fp16 code pairs (1024 + q) of a block, for the fp16-staged h: OR-ing a
-// code below 1024 into the mantissa of fp16(1024) = 0x6400 gives 1024 + q.
 template <int FMT>
 __device__ __forceinline__ void unpack_block_f16(u32x4 w, int bb, uint32_t (&pr)[16]) {
 #pragma unroll
   for (int q = 0; q < 4; ++q)
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      pr[q * 4 + e] = FMT == MOE_W_Q2B32
-                          ? ((w[2 * bb + (q >> 1)] >> (2 * ((q & 1) * 4 + e))) & 0x00030003u) | 0x64006400u
-                          : ((w[q] >> (4 * e)) & 0x000F000Fu) | 0x64006400u;
+      pr[q * 4 + e] = FMT == MOE_W_Q2B32 ? f16_pair_cls<FMT>(w[2 * bb + (q >> 1)], (q & 1) * 4 + e)
+                                         : f16_pair_cls<FMT>(w[q], e);
 }
 __device__ __forceinline__ float block_dot_f16(const uint32_t (&pr)[16], const u32x4* x4) {
   float a[4] = {0.f, 0.f, 0.f, 0.f};
@@ -782,14 +758,16 @@ __device__ __forceinline__ float block_dot_f16(const uint32_t (&pr)[16], const u
 }
 
 // One row . h of tokens v0 .. v0 + nv - 1, staged by stage_h (token t's
-// vector at xd + t * vs, block sums at sd + t * ss, block scales at
-// bsc + t * ss).  Per block: 2^e * (d * sum (1024 + q) h' + (m - 1024 d) *
-// sum h'), with h' the scaled fp16 values.
+// vector at xd + t * vs, block scales 2^e at bsc + t * ss, and per block
+// 2^e * sum h and -1024 * 2^e * sum h' at sd + t * ss and sd2 + t * ss).
+// Per block: d * (2^e * sum (1024 + q 4^c) h' - 1024 * 2^e * sum h') +
+// m * 2^e * sum h, with h the block-scaled fp16 values and h' = h * 4^-c as
+// staged.
 template <int FMT, int NCH, int NG>
 __device__ __forceinline__ void row_vecs_dot_f16(const RowRegs<FMT, NCH>& R, int nch, int lane_g,
                                                  int lpr, const uint32_t* xd, const float* sd,
-                                                 const float* bsc, int vs, int ss, int v0, int nv,
-                                                 float (&o)[NG]) {
+                                                 const float* sd2, const float* bsc, int vs,
+                                                 int ss, int v0, int nv, float (&o)[NG]) {
 #pragma unroll
   for (int v = 0; v < NG; ++v) o[v] = 0.f;
   constexpr int kBlk = FMT == MOE_W_Q2B32 ? 2 : 1;
@@ -802,7 +780,7 @@ __device__ __forceinline__ void row_vecs_dot_f16(const RowRegs<FMT, NCH>& R, int
     for (int bb = 0; bb < kBlk; ++bb) {
       const uint32_t dsh = FMT == MOE_W_Q2B32 ? 16u * uint32_t(bb) : 0u;
       const float d = f16_to_f32(uint16_t((R.sc[j] >> dsh) & 0xFFFFu));
-      const float m = f16_to_f32(uint16_t((R.mn[j] >> dsh) & 0xFFFFu)) - 1024.f * d;
+      const float m = f16_to_f32(uint16_t((R.mn[j] >> dsh) & 0xFFFFu));
       uint32_t pr[16];
       unpack_block_f16<FMT>(w, bb, pr);
 #pragma unroll
@@ -810,7 +788,8 @@ __device__ __forceinline__ void row_vecs_dot_f16(const RowRegs<FMT, NCH>& R, int
         if (v >= nv) continue;
         const int t = v0 + v, blk = kBlk * c + bb;
         const u32x4* h4 = reinterpret_cast<const u32x4*>(xd + t * vs + c * Fmt<FMT>::kCS) + 4 * bb;
-        o[v] += bsc[t * ss + blk] * (d * block_dot_f16(pr, h4) + m * sd[t * ss + blk]);
+        const float p = fmaf(bsc[t * ss + blk], block_dot_f16(pr, h4), sd2[t * ss + blk]);
+        o[v] = fmaf(d, p, fmaf(m, sd[t * ss + blk], o[v]));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -847,8 +826,8 @@ __device__ __forceinline__ void gateup_compute(const RowRegs<FMT, nch_gu<FMT>()>
                                                const LayerArgs& a,
                                                int i, int n, const int* vid, const int* ids,
                                                int t0, uint64_t* out, const uint32_t* xs,
-                                               const float* xsum, int vstride, int lane_g,
-                                               uint32_t epoch) {
+                                               const float* xsum, const float* xsum2, int vstride,
+                                               int lane_g, uint32_t epoch) {
   constexpr int kLprGU = Lanes<FMT>::kGU;
   const int K = a.H, sstride = K / 32;
   const int nch = chunks_of<FMT>(K) / kLprGU;
@@ -856,14 +835,16 @@ __device__ __forceinline__ void gateup_compute(const RowRegs<FMT, nch_gu<FMT>()>
     const int nv = min(NG, n - v0);
     const uint32_t* xv[NG];
     const float* sv[NG];
+    const float* sv2[NG];
 #pragma unroll
     for (int v = 0; v < NG; ++v) {
       const int id = v < nv ? (vid ? vid[v0 + v] : t0 + v0 + v) : 0;
       xv[v] = xs + id * vstride;
       sv[v] = xsum + id * sstride;
+      sv2[v] = xsum2 + id * sstride;
     }
     float g[NG], u[NG];
-    row_pair_vecs_dot<FMT, nch_gu<FMT>(), NG>(rg, ru, nch, lane_g, kLprGU, xv, sv, nv, g, u);
+    row_pair_vecs_dot<FMT, nch_gu<FMT>(), NG>(rg, ru, nch, lane_g, kLprGU, xv, sv, sv2, nv, g, u);
 #pragma unroll
     for (int v = 0; v < NG; ++v) {
       if (v >= nv) continue;
@@ -966,10 +947,22 @@ __device__ __forceinline__ void router_compute(const RouterRegs<FMT>& R, const L
       for (int t = 0; t < TB; ++t) {
         if (t < nt) {
           const uint32_t* xv = xs + t * vstride + lane_g * Fmt<FMT>::kCS;
-          float s4[4] = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (FMT == MOE_W_Q2B32) {
+            // pair s of each group is staged times 4^-(s % 3): sums per
+            // class (and group parity, for shorter chains)
+            float s6[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int j = 0; j < kG * kS; ++j) s4[j & 3] = dot2_bf16(pr[j], xv[j], s4[j & 3]);
-          acc[t] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+            for (int j = 0; j < kG * kS; ++j) {
+              const int a6 = 2 * q2_class(j % kS) + (j / kS) % 2;
+              s6[a6] = dot2_bf16(pr[j], xv[j], s6[a6]);
+            }
+            acc[t] = fmaf(16.f, s6[4] + s6[5], fmaf(4.f, s6[2] + s6[3], s6[0] + s6[1]));
+          } else {
+            float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < kG * kS; ++j) s4[j & 3] = dot2_bf16(pr[j], xv[j], s4[j & 3]);
+            acc[t] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+          }
         }
       }
     } else {
@@ -1458,11 +1451,11 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   const int T = ka.T, k = ka.k, P = T * k, E = ka.E;
   const int K = ka.H;
   const int vstride = FMT == MOE_W_F32 ? K : (K / Fmt<FMT>::kWPC) * Fmt<FMT>::kCS;
-  // LDS: tokens | block sums | group sums | logits
+  // LDS: tokens | block sums of the values | of the staged values | logits
   uint32_t* xs = smem;
   float* xsum = reinterpret_cast<float*>(xs + T * vstride);
-  float* psum = xsum + T * (K / 32);
-  float* lg = psum + T * (K / 16);
+  float* xsum2 = xsum + T * (K / 32);
+  float* lg = xsum2 + T * (K / 32);
 
   // ---- A: loads first (call counter and error word, slot table, first task's rows)
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();   // start of this workgroup's waits
@@ -1503,7 +1496,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   // The first router task zeroes its share of y while the tokens load: the
   // stores land before the task publishes its logits, and the wait for the
   // header lets the row and token loads stay in flight.
-  stage_tokens<FMT>(ka.x, T, K, xs, psum, vstride, [&]() {
+  stage_tokens<FMT>(ka.x, T, K, xs, xsum, xsum2, vstride, [&]() {
     if (task0 < n_router && __builtin_amdgcn_readfirstlane(uint32_t(hdr >> 32)) == 0u)
       zero_y_share(ka, task0, n_router, lane);
   });
@@ -1513,7 +1506,11 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   }
   for (int e = tid; e < kEMax; e += kThreads) L.emask[e] = 0u;
   if (tid < kTMax) L.ncand[tid] = 0;
-  if (tid == 0) L.dzero = 0;
+  if (tid == 0) {
+    L.dzero = 0;
+    L.t_gu = 0ull;
+    L.t_a = 0ull;
+  }
 #pragma unroll
   for (int r = 0; r < kEMax / kThreads; ++r)
     if (tid + r * kThreads < E) L.slot_of[tid + r * kThreads] = so[r];
@@ -1521,9 +1518,6 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   if (L.failed == 2) return;   // every thread: nothing is written
   const LayerArgs& a = sa;
   stamp_now(a.trace, kTrStaged);
-  if (tid == 0) L.t_gu = 0ull;
-  token_block_sums(T, K, xsum, psum);
-  __syncthreads();
   const uint32_t epoch = L.calls + 1u;   // this call's number
   if (a.debug_hold && b == 0 && tid == 0) {
     // test hook: wait for a word nothing writes until the budget is spent
@@ -1542,11 +1536,13 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
       const int i = (s % n_srb) * kRowsGU + lane / kLprGU;
       if (task != task0) gateup_load<FMT>(rg, ru, a, a.sg, a.su, 0, i, lane_gu);
       gateup_compute<FMT, kNG>(rg, ru, a, i, min(kTG, T - t0), nullptr, nullptr, t0, region_h_sh(a), xs,
-                          xsum, vstride, lane_gu, epoch);
+                               xsum, xsum2, vstride, lane_gu, epoch);
     }
   }
 
   stamp_now(a.trace, kTrTasksA);
+  if (a.trace && lane == 0)
+    atomicMax(&L.t_a, static_cast<unsigned long long>(__builtin_amdgcn_s_memrealtime()));
   // this workgroup has read the counter (workgroup 0 checks before it
   // advances the counter)
   if (tid == 0) st_dev(region_arrive(a) + b, tag_word(0.f, epoch));
@@ -1590,6 +1586,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   stamp_now(a.trace, kTrLogitsAll);
   const bool thresh = k <= kTopkListMax;
   if (thresh) topk_threshold<TB>(lg, T, E, k, L);
+  stamp_now(a.trace, kTrRtCand);
   // tokens the threshold selection did not take: one wave each
   for (int t = wave; t < T; t += kWaves) {
     if (thresh && L.ncand[t] <= kThreads / TB) continue;
@@ -1603,6 +1600,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     }
   }
   __syncthreads();
+  stamp_now(a.trace, kTrRtRank);
   for (int t = wave; t < T; t += kWaves) {
     // gates: softmax over the k chosen logits (choice 0 is the largest)
     const int my_e = lane < k ? L.idx[t * k + lane] : 0;
@@ -1620,10 +1618,13 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     }
   }
   __syncthreads();
+  stamp_now(a.trace, kTrRtGate);
   resolve_multi(a, L, P, b == 0);   // T >= 2 here
   __syncthreads();
+  stamp_now(a.trace, kTrRtResolved);
   }
   stamp_now(a.trace, kTrRouted);
+  if (a.trace) stamp(a.trace, kTrTasksAAll, L.t_a);
   const int n_act = L.n_act;
   if (b == 0 && a.usage && tid < P)
     __hip_atomic_fetch_add(gmem_w(a.usage + L.idx[tid]), 1u, __ATOMIC_RELAXED,
@@ -1789,7 +1790,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
       const int st = L.act_start[u];
       const int n = L.act_start[u + 1] - st;
       gateup_compute<FMT, kNGC>(g, up, a, i, n, L.tok + st, L.bpair + st, 0, region_h(a), xs,
-                                xsum, vstride, lane_gu, epoch);
+                                xsum, xsum2, vstride, lane_gu, epoch);
     };
     // At most one task (one token, the usual case): no loop, so no load is
     // issued on one path and not on another, which would make the waits
@@ -1825,8 +1826,8 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   {
     uint32_t* xd = smem;                                    // reuses the token area
     float* sd = reinterpret_cast<float*>(xd + kTMax * vs_d);
-    float* pd = sd + kTMax * ss_d;
-    float* bsc = pd + kTMax * (Kd / 16);
+    float* sd2 = sd + kTMax * ss_d;
+    float* bsc = sd2 + kTMax * ss_d;
     // The first unit's rows load here, not during gate/up: there they would
     // queue ahead of other waves' gate/up rows in the CU's address unit,
     // which would then finish later.
@@ -1851,7 +1852,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
                              : region_h(a) + int64_t(L.bpair[st + tid]) * Kd;
         __syncthreads();
         if (staged < 0) stamp_now(a.trace, kTrDBar2);
-        stage_h<FMT>(srcs, n, Kd, xd, sd, pd, bsc, vs_d, epoch, a, L, t0, staged < 0);
+        stage_h<FMT>(srcs, n, Kd, xd, sd, sd2, bsc, vs_d, epoch, a, L, t0, staged < 0);
         __syncthreads();
         if (staged < 0 && a.trace) {
           stamp(a.trace, kTrHBar, __builtin_amdgcn_s_memrealtime());
@@ -1864,13 +1865,12 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
         const int nv = min(kNG, n - v0);
         float o[kNG];
         if constexpr (FMT != MOE_W_F32) {
-          row_vecs_dot_f16<FMT, kNChD, kNG>(rd, nch_d, lane_gd, kLprD, xd, sd, bsc, vs_d, ss_d, v0,
-                                            nv, o);
+          row_vecs_dot_f16<FMT, kNChD, kNG>(rd, nch_d, lane_gd, kLprD, xd, sd, sd2, bsc, vs_d,
+                                            ss_d, v0, nv, o);
         } else {
 #pragma unroll
           for (int v = 0; v < kNG; ++v)
-            o[v] = v < nv ? row_vec_dot<FMT, kNChD>(rd, nch_d, lane_gd, kLprD,
-                                                     xd + (v0 + v) * vs_d, sd + (v0 + v) * ss_d)
+            o[v] = v < nv ? row_vec_dot<FMT, kNChD>(rd, nch_d, lane_gd, kLprD, xd + (v0 + v) * vs_d)
                           : 0.f;
         }
 #pragma unroll
@@ -1952,11 +1952,10 @@ size_t vec_bytes(int fmt, int K) {
 }  // namespace
 
 size_t layer_fused_lds(int fmt, int T, int E, int H, int I) {
-  // A-C: tokens, block sums, group sums, logits
-  const size_t a = size_t(T) * (vec_bytes(fmt, H) + (H / 32) * 4 + (H / 16) * 4) +
-                   size_t(T) * E * 4;
-  // D: a vector per token, block sums, group sums, block scales (16 tokens)
-  const size_t d = size_t(kTMax) * (vec_bytes(fmt, I) + (I / 32) * 4 + (I / 16) * 4 + (I / 32) * 4);
+  // A-C: tokens, two sets of block sums, logits
+  const size_t a = size_t(T) * (vec_bytes(fmt, H) + 2 * (H / 32) * 4) + size_t(T) * E * 4;
+  // D: a vector per token, two sets of block sums, block scales (16 tokens)
+  const size_t d = size_t(kTMax) * (vec_bytes(fmt, I) + 3 * (I / 32) * 4);
   return a > d ? a : d;
 }
 
