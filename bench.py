@@ -231,6 +231,7 @@ def bench_decode(args, cfg_name, steps=None, warmup=None, cpu_calls=None):
     idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     gate = torch.empty((T, k), dtype=torch.float32, device=dev)
     calls_per_step = 1 if cfg.layers == 1 else L
+    moe.moe_set_deterministic(bool(args.fixed_order))
     # one slot table per timed call: the distinct experts those calls read
     slot_rec = torch.empty((max(steps, 1), calls_per_step, T, k), dtype=torch.int32, device=dev)
     slot_tmp = torch.empty((T, k), dtype=torch.int32, device=dev)
@@ -287,7 +288,8 @@ def bench_decode(args, cfg_name, steps=None, warmup=None, cpu_calls=None):
         "config": {"workload": cfg.name, "E": cfg.E, "k": cfg.k, "H": cfg.H, "I": cfg.I,
                    "T": T, "layers": L, "weights": cfg.wfmt, "shared_expert": cfg.shared,
                    "slots": cfg.slots, "step": "one moe_layer call" if cfg.layers == 1
-                   else f"{L} moe_layer calls (one per layer)"},
+                   else f"{L} moe_layer calls (one per layer)",
+                   "sums": "fixed order" if args.fixed_order else "float atomics"},
         "hbm_gbs": round(gbs, 1),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
@@ -796,6 +798,8 @@ def main():
                          "without a second stream")
     ap.add_argument("--host-tier", action="store_true",
                     help="c4: also time the host tier on one step's misses")
+    ap.add_argument("--fixed-order", action="store_true",
+                    help="decode workloads: fixed-order sums into y (moe_set_deterministic)")
     ap.add_argument("--phase-trace", type=int, default=0, metavar="N",
                     help="decode workloads: after the timed steps, N more cold calls with the "
                          "fused launch's phase stamps on (medians reported)")

@@ -266,6 +266,19 @@ void moe_set_wait_budget(uint64_t ns, int32_t hold);
  * call is issued. */
 void moe_set_trace(uint64_t* trace);
 
+/* Order of the sums into y of later fused moe_layer launches (and of
+ * moe_layer_noalloc).  on == 0 (the default): every down-projection unit
+ * adds its gate-weighted rows into y with float atomics, whose order varies
+ * from run to run, so y may differ in its last bits between identical calls
+ * (the combine's definition, [MD] section "1 トークン、三者の分担", fixes
+ * the value, not the order; [MD] "代償" accepts last-bit differences).
+ * on != 0: the units publish their rows to the hand-off region instead, and
+ * y[t][r] is summed over the hit choices in choice order j = 0 .. k-1, then
+ * the shared expert, by one thread: y is bit-identical between identical
+ * calls, whatever the grid size or timing.  Costs one more poll round trip
+ * per launch.  Process-wide, read when a call is issued. */
+void moe_set_deterministic(int32_t on);
+
 /* ---- Adaptive slot table ([MD] section "粗から細へ" and its placement
  * figure: each card fills its expert slots by a usage ranking, and an
  * adaptive tier swaps at most 96 experts every 4 rounds toward the experts

@@ -28,7 +28,7 @@ EXPORTS = ("moe_status_string", "moe_version", "moe_workspace_size", "moe_route"
            "moe_host_isa", "moe_verify_workspace_size", "moe_verify_accept",
            "moe_prefill_workspace_size", "moe_prefill_layer", "moe_layer_check",
            "moe_set_wait_budget", "moe_set_trace", "moe_layer_noalloc",
-           "moe_expert_ffn_accum")
+           "moe_expert_ffn_accum", "moe_set_deterministic")
 MOE_REFRESH_MAX_SWAPS = 1024
 
 
@@ -102,6 +102,8 @@ def _load():
     lib.moe_set_wait_budget.argtypes = [ctypes.c_uint64, I32]
     lib.moe_set_trace.restype = None
     lib.moe_set_trace.argtypes = [P]
+    lib.moe_set_deterministic.restype = None
+    lib.moe_set_deterministic.argtypes = [I32]
     SP = ctypes.POINTER(moe_slot_pool)
     lib.moe_slot_refresh_workspace_size.restype = I32
     lib.moe_slot_refresh_workspace_size.argtypes = [SP, ctypes.POINTER(SZ)]
@@ -277,6 +279,12 @@ def moe_set_trace(trace):
     """Phase stamps of later fused moe_layer launches into trace (a uint64-
     sized int64 device tensor of [1024][32] words), or None to stop."""
     lib.moe_set_trace(_ptr(trace))
+
+
+def moe_set_deterministic(on=True):
+    """Fixed-order sums into y for later fused moe_layer launches (True), or
+    the float-atomic sums (False, the default)."""
+    lib.moe_set_deterministic(1 if on else 0)
 
 
 class SlotPool:

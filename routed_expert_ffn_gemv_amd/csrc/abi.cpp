@@ -31,6 +31,7 @@ constexpr uint64_t kDefaultWaitNs = 100000000ull;
 std::atomic<uint64_t> g_wait_ns{0};
 std::atomic<int32_t> g_hold{0};
 std::atomic<uint64_t*> g_trace{nullptr};   // phase stamps of the fused launch (diagnostics)
+std::atomic<int32_t> g_det{0};             // fused launch: y summed in a fixed order
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -107,7 +108,7 @@ WsLayout layout(const moe_layer_desc* d, int64_t T) {
   w.cap = int(P < d->num_slots ? P : d->num_slots);
   size_t o = 0;
   w.layer = o;
-  o += up(layer_region_bytes(d->E, d->k, d->I));
+  o += up(layer_region_bytes(d->E, d->k, d->H, d->I));
   w.logits = o;
   o += up(size_t(T) * d->E * 4);
   w.active = o;
@@ -337,6 +338,7 @@ LayerArgs layer_args(const moe_layer_desc* desc, const uint16_t* x, int T, float
   if (L.wait_ticks == 0) L.wait_ticks = 1;
   L.debug_hold = g_hold.load(std::memory_order_relaxed);
   L.trace = g_trace.load(std::memory_order_relaxed);
+  L.det = g_det.load(std::memory_order_relaxed) ? 1 : 0;
   return L;
 }
 
@@ -498,7 +500,7 @@ moe_status moe_layer_noalloc(const moe_layer_desc* desc, const uint16_t* x, int3
       !miss_off)
     return MOE_ERR_INVALID;
   if (!fused_shape(desc, T) ||
-      layer_region_bytes(desc->E, desc->k, desc->I) > size_t(MOE_LAYER_SCRATCH_BYTES))
+      layer_region_bytes(desc->E, desc->k, desc->H, desc->I) > size_t(MOE_LAYER_SCRATCH_BYTES))
     return MOE_ERR_UNSUPPORTED;
   const LayerArgs L =
       layer_args(desc, x, T, y, topk_idx, topk_gate, slot_idx, miss, miss_off, nullptr);
@@ -531,6 +533,8 @@ void moe_set_wait_budget(uint64_t ns, int32_t hold) {
 }
 
 void moe_set_trace(uint64_t* trace) { g_trace.store(trace, std::memory_order_relaxed); }
+
+void moe_set_deterministic(int32_t on) { g_det.store(on ? 1 : 0, std::memory_order_relaxed); }
 
 moe_status moe_slot_refresh_workspace_size(const moe_slot_pool* pool, size_t* bytes) {
   const moe_status s = check_pool(pool);

@@ -20,15 +20,18 @@ namespace moe {
 //   logits [16][E]     tagged router logits
 //   h      [hrows][I]  tagged SwiGLU activations: pairs first, then the
 //                      shared expert's rows (one per token)
+//   part   [hrows][H]  tagged down-projection rows, the same row order
+//                      (pair rows already times their gate; the fixed-order
+//                      sum of y reads them)
 constexpr int kLayerMaxGrid = 1024;
 constexpr int kLayerMaxPairs = 256;
 __host__ __device__ inline int layer_h_rows(int k) {
   const int p = MOE_LAYER_MAX_T * k;
   return (p < kLayerMaxPairs ? p : kLayerMaxPairs) + MOE_LAYER_MAX_T;
 }
-inline size_t layer_region_bytes(int E, int k, int I) {
+inline size_t layer_region_bytes(int E, int k, int H, int I) {
   return 256 + size_t(kLayerMaxGrid) * 8 + size_t(MOE_LAYER_MAX_T) * E * 8 +
-         size_t(layer_h_rows(k)) * I * 8;
+         size_t(layer_h_rows(k)) * (size_t(I) + H) * 8;
 }
 
 // Data planes of one expert matrix pool (sizes are common to all six).
@@ -63,6 +66,7 @@ struct LayerArgs {
   uint64_t wait_ticks;     // budget of every wait, in ticks of the 100 MHz real-time counter
   int debug_hold;          // test hook: workgroup 0 first waits on a word nothing writes
   uint64_t* trace;         // phase stamps [grid][kTraceSlots] (null: off)
+  int det;                 // 1: y summed in a fixed order (no float atomics)
 };
 
 // Phase stamps of the fused launch (real-time counter ticks, 100 MHz), one

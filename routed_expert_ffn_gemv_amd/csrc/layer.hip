@@ -137,6 +137,11 @@ __device__ __forceinline__ uint64_t* region_h(const LayerArgs& a) {
 __device__ __forceinline__ uint64_t* region_h_sh(const LayerArgs& a) {
   return region_h(a) + int64_t(layer_h_rows(a.k) - kTMax) * a.I;
 }
+// down-projection rows for the fixed-order sum: pair p at row p, the shared
+// expert's row of token t at row layer_h_rows(k) - 16 + t
+__device__ __forceinline__ uint64_t* region_part(const LayerArgs& a) {
+  return region_h(a) + int64_t(layer_h_rows(a.k)) * a.I;
+}
 
 // Tagged words: value bits low, call number high.
 __device__ __forceinline__ uint64_t tag_word(float v, uint32_t epoch) {
@@ -280,6 +285,7 @@ struct Lds {
   alignas(16) uint64_t rkey[kThreads + 8];   // segment maxima, then candidates (top-k)
   uint64_t tau[kTMax];       // per-token thresholds
   int ncand[kTMax];          // per-token candidate counts
+  uint64_t hmask[kTMax];     // per token: the choices j that hit a resident slot (bit j)
   alignas(16) uint32_t tmp[32];
   int cstart[kWaves + 1];   // this workgroup's waves' gate/up task ranges
   int dstart[2];            // this workgroup's down unit range (contiguous split)
@@ -1196,6 +1202,7 @@ __device__ __forceinline__ void resolve_one(const LayerArgs& a, Lds& L, int e, f
   if (lane == 0) {
     L.act_start[n_hit] = n_hit;
     L.n_act = n_hit;
+    L.hmask[0] = hit_mask;
   }
 }
 
@@ -1377,7 +1384,10 @@ __device__ __forceinline__ void resolve_multi(const LayerArgs& a, Lds& L, int P,
   const int t = valid ? tid / k : 0;
   const int s = valid ? slot_of_choice(a, L, e) : -1;
   const bool hit = s >= 0;
-  if (hit) atomicOr(&L.emask[e], 1u << t);
+  if (hit) {
+    atomicOr(&L.emask[e], 1u << t);
+    atomicOr(reinterpret_cast<unsigned long long*>(&L.hmask[t]), 1ull << (tid - t * k));
+  }
   const uint64_t mm = __ballot(valid && !hit);
   if (lane == 0) L.tmp[wave] = uint32_t(__popcll(mm));
   __syncthreads();
@@ -1497,7 +1507,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   // stores land before the task publishes its logits, and the wait for the
   // header lets the row and token loads stay in flight.
   stage_tokens<FMT>(ka.x, T, K, xs, xsum, xsum2, vstride, [&]() {
-    if (task0 < n_router && __builtin_amdgcn_readfirstlane(uint32_t(hdr >> 32)) == 0u)
+    if (task0 < n_router && !ka.det && __builtin_amdgcn_readfirstlane(uint32_t(hdr >> 32)) == 0u)
       zero_y_share(ka, task0, n_router, lane);
   });
   if (tid == 0) {
@@ -1505,7 +1515,10 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     L.failed = uint32_t(hdr >> 32) != 0u ? 2 : 0;   // a failed call left the workspace poisoned
   }
   for (int e = tid; e < kEMax; e += kThreads) L.emask[e] = 0u;
-  if (tid < kTMax) L.ncand[tid] = 0;
+  if (tid < kTMax) {
+    L.ncand[tid] = 0;
+    L.hmask[tid] = 0ull;
+  }
   if (tid == 0) {
     L.dzero = 0;
     L.t_gu = 0ull;
@@ -1528,7 +1541,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     if (task < n_router) {
       if (task != task0) {
         router_load<FMT>(rr, a, task, task % n_rg, n_router, lane);
-        zero_y_share(a, task, n_router, lane);   // after the workspace check, before the logits
+        if (!a.det) zero_y_share(a, task, n_router, lane);   // after the workspace check, before the logits
       }
       router_compute<FMT, kTG>(rr, a, task % n_rg, (task / n_rg) * kTG, xs, vstride, lane, epoch);
     } else {
@@ -1879,8 +1892,14 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
           const float os = group_sum<kLprD>(o[v]);
           if (r < a.H && lane_gd == 0) {
             const int t = shared ? v0 + v : L.tok[st + v0 + v];
-            const float g = shared ? 1.f : L.gate[L.bpair[st + v0 + v]];
-            fadd_dev(a.y + int64_t(t) * a.H + r, g * os);
+            const int pr = shared ? 0 : L.bpair[st + v0 + v];
+            const float g = shared ? 1.f : L.gate[pr];
+            if (a.det) {
+              const int row = shared ? layer_h_rows(a.k) - kTMax + t : pr;
+              st_dev(region_part(a) + int64_t(row) * a.H + r, tag_word(g * os, epoch));
+            } else {
+              fadd_dev(a.y + int64_t(t) * a.H + r, g * os);
+            }
           }
         }
       }
@@ -1888,6 +1907,48 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     }
   }
   stamp_now(a.trace, kTrDown);
+  if (a.det) {
+    // Fixed-order sums: this workgroup's share of y, each element by one
+    // thread: the hit choices j = 0 .. k-1 in order, then the shared expert
+    // (index k), their rows read once every unit has published them (16
+    // words in flight per thread; words not yet of this call are read again).
+    const int TH = T * a.H, per = (TH + G - 1) / G;
+    const int i0 = b * per, i1 = min(i0 + per, TH);
+    const uint64_t* part = region_part(a);
+    const int sh_row = layer_h_rows(k) - kTMax;
+    for (int i = i0 + tid; i < i1; i += kThreads) {
+      const int t = i / a.H, r = i - t * a.H;
+      const uint64_t m = L.hmask[t];
+      float acc = 0.f;
+      for (int j0 = 0; j0 <= k; j0 += 16) {
+        uint64_t w[16];
+        const uint64_t* src[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int j = j0 + q;
+          const bool want = j < k ? ((m >> j) & 1ull) != 0ull : (j == k && a.has_sh != 0);
+          src[q] = want ? part + int64_t(j < k ? t * k + j : sh_row + t) * a.H + r : nullptr;
+          if (src[q]) w[q] = ld_dev(src[q]);
+        }
+        auto all_here = [&]() {
+          bool ok = true;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) ok = ok && (!src[q] || tag_ok(w[q], epoch));
+          return ok;
+        };
+        while (!all_here() && keep_waiting(a, L, t0)) {
+          __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+          for (int q = 0; q < 16; ++q)
+            if (src[q] && !tag_ok(w[q], epoch)) w[q] = ld_dev(src[q]);
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          if (src[q]) acc += tag_val(w[q]);
+      }
+      *gmem_w(a.y + i) = acc;
+    }
+  }
   // Workgroup 0 advances the call counter once every workgroup has read it
   // (a failed call leaves it: the workspace is poisoned anyway).
   if (b == 0) {

@@ -221,6 +221,62 @@ def test_all_miss_table():
     assert rowwise_rel_err(host(o["y"]), ref["y"]) <= TOL   # shared expert only
 
 
+def _tiered_small():
+    """A partial slot table (24 of 64 experts resident): (cfg, layer kwargs)."""
+    cfg = small_cfg(E=64, k=6, H=1024, I=256, T=5, bias="zipf", seed=87)
+    rng = np.random.default_rng(3)
+    resident = np.sort(rng.choice(cfg.E, 24, replace=False))
+    slot_of = np.full(cfg.E, -1, np.int32)
+    slot_of[resident] = np.arange(len(resident))[::-1]
+    from synth import device as sdev
+    pool = sdev.expert_pool(cfg, [0] * len(resident),
+                            [int(resident[len(resident) - 1 - s]) for s in range(len(resident))])
+    return cfg, dict(pool=pool, slot_of=slot_of, num_slots=len(resident))
+
+
+DET_CASES = ["q2_T1", "q2_T9", "q4_T16", "q2_T16_no_shared", "tiered_misses", "c2", "c3"]
+
+
+@pytest.mark.parametrize("name", DET_CASES)
+def test_fused_deterministic_sums(name):
+    """moe_set_deterministic: every element of y is summed by one thread in
+    choice order (hits only), then the shared expert.  Two calls on one
+    workspace give bit-identical y, every element written (y starts as
+    NaN), within tolerance of the oracle; the atomic-sum mode agrees within
+    tolerance."""
+    import torch
+    import routed_expert_ffn_gemv_amd as moe
+    kw = {}
+    if name == "tiered_misses":
+        cfg, kw = _tiered_small()
+    elif name in ("c2", "c3"):
+        cfg = synth.CONFIGS[name]
+    else:
+        cfg = FUSED[name]
+    say(f"[gpu] fixed-order sums {name}: E={cfg.E} k={cfg.k} H={cfg.H} I={cfg.I} T={cfg.T}")
+    x, _ = oracle.margin_x(cfg, 0)
+    L = DeviceLayer(cfg, 0, x=x, **kw)
+    ws = moe.workspace(L.desc, L.T)
+    moe.moe_set_deterministic(True)
+    try:
+        o1 = L.run_layer(ws)
+        o2 = L.run_layer(ws)
+    finally:
+        moe.moe_set_deterministic(False)
+    o3 = L.run_layer(ws)
+    moe.moe_layer_check(ws)
+    ref = L.oracle()
+    for o in (o1, o2, o3):
+        check_routing(o, ref, cfg.k)
+    y1, y2 = host(o1["y"]), host(o2["y"])
+    assert np.isfinite(y1).all()
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    err = rowwise_rel_err(y1, ref["y"])
+    say(f"  rel err {err:.2e} (atomic sums: {rowwise_rel_err(host(o3['y']), ref['y']):.2e})")
+    assert err <= TOL
+    assert rowwise_rel_err(host(o3["y"]), ref["y"]) <= TOL
+
+
 def test_c2_decode_layer():
     """The decode layer at full size, the launch bench.py times (moe_layer, T=1)."""
     cfg = synth.CONFIGS["c2"]

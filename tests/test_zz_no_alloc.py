@@ -49,6 +49,31 @@ def test_noalloc_matches_moe_layer():
         assert err_w <= TOL and err <= TOL
 
 
+def test_noalloc_fixed_order_matches_moe_layer_bit_for_bit():
+    """With fixed-order sums (moe_set_deterministic) y no longer depends on
+    the order of the float additions: noalloc and moe_layer give the same y
+    bit for bit, again on two calls in a row, the second smaller."""
+    import torch
+    import routed_expert_ffn_gemv_amd as moe
+    moe.moe_set_deterministic(True)
+    try:
+        for cfg, layer in ((synth.CONFIGS["c3"], 7), (synth.CONFIGS["c2"], 3)):
+            say(f"[gpu] noalloc, fixed-order sums: {cfg.name} layer {layer}, T={cfg.T}")
+            x, _ = oracle.margin_x(cfg, layer)
+            L = DeviceLayer(cfg, layer, x=x)
+            o = _noalloc(L)
+            moe.moe_layer_check(None)
+            w = L.run_layer()
+            torch.cuda.synchronize()
+            yo, yw = host(o["y"]), host(w["y"])
+            assert np.isfinite(yo).all()
+            assert np.array_equal(yo.view(np.uint32), yw.view(np.uint32))
+            for key in ("idx", "gate", "slot_idx", "miss_off"):
+                np.testing.assert_array_equal(host(o[key]), host(w[key]))
+    finally:
+        moe.moe_set_deterministic(False)
+
+
 def test_noalloc_rejects_unfused_shapes():
     """A shape moe_layer runs as separate steps (T * k > 256) needs a
     workspace: MOE_ERR_UNSUPPORTED, nothing launched."""
