@@ -1444,7 +1444,7 @@ __device__ __forceinline__ void resolve_multi(const LayerArgs& a, Lds& L, int P,
 // --------------------------------------------------------------- kernel
 // TB: the largest token count the instance serves (1, 4 or 16), so per-token
 // loops are unrolled no further than needed.
-template <int FMT, int TB>
+template <int FMT, int TB, bool DET>
 __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   constexpr int kLprGU = Lanes<FMT>::kGU, kRowsGU = Lanes<FMT>::kRowsGU;
   constexpr int kLprD = Lanes<FMT>::kD, kRowsD = Lanes<FMT>::kRowsD;
@@ -1507,7 +1507,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   // stores land before the task publishes its logits, and the wait for the
   // header lets the row and token loads stay in flight.
   stage_tokens<FMT>(ka.x, T, K, xs, xsum, xsum2, vstride, [&]() {
-    if (task0 < n_router && !ka.det && __builtin_amdgcn_readfirstlane(uint32_t(hdr >> 32)) == 0u)
+    if (task0 < n_router && !DET && __builtin_amdgcn_readfirstlane(uint32_t(hdr >> 32)) == 0u)
       zero_y_share(ka, task0, n_router, lane);
   });
   if (tid == 0) {
@@ -1541,7 +1541,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     if (task < n_router) {
       if (task != task0) {
         router_load<FMT>(rr, a, task, task % n_rg, n_router, lane);
-        if (!a.det) zero_y_share(a, task, n_router, lane);   // after the workspace check, before the logits
+        if (!DET) zero_y_share(a, task, n_router, lane);   // after the workspace check, before the logits
       }
       router_compute<FMT, kTG>(rr, a, task % n_rg, (task / n_rg) * kTG, xs, vstride, lane, epoch);
     } else {
@@ -1894,7 +1894,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
             const int t = shared ? v0 + v : L.tok[st + v0 + v];
             const int pr = shared ? 0 : L.bpair[st + v0 + v];
             const float g = shared ? 1.f : L.gate[pr];
-            if (a.det) {
+            if constexpr (DET) {
               const int row = shared ? layer_h_rows(a.k) - kTMax + t : pr;
               st_dev(region_part(a) + int64_t(row) * a.H + r, tag_word(g * os, epoch));
             } else {
@@ -1907,7 +1907,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     }
   }
   stamp_now(a.trace, kTrDown);
-  if (a.det) {
+  if constexpr (DET) {
     // Fixed-order sums: this workgroup's share of y, each element by one
     // thread: the hit choices j = 0 .. k-1 in order, then the shared expert
     // (index k), their rows read once every unit has published them (16
@@ -1970,18 +1970,18 @@ struct Occ {
   int grid = 0;
 };
 
-template <int FMT, int TB>
-hipError_t launch_fmt(const LayerArgs& a, size_t lds, hipStream_t st, int* grid_out) {
+template <int FMT, int TB, bool DET>
+hipError_t launch_det(const LayerArgs& a, size_t lds, hipStream_t st, int* grid_out) {
   static thread_local Occ c;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (c.lds != lds || c.device != dev) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_layer_kernel<FMT, TB>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_layer_kernel<FMT, TB, DET>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return e;
     int per_cu = 0, cus = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, moe_layer_kernel<FMT, TB>, kThreads,
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, moe_layer_kernel<FMT, TB, DET>, kThreads,
                                                      lds);
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -1993,8 +1993,16 @@ hipError_t launch_fmt(const LayerArgs& a, size_t lds, hipStream_t st, int* grid_
     c.grid = cus;   // one workgroup of 8 waves per CU
   }
   if (grid_out) *grid_out = c.grid;
-  hipLaunchKernelGGL((moe_layer_kernel<FMT, TB>), dim3(c.grid), dim3(kThreads), lds, st, a);
+  hipLaunchKernelGGL((moe_layer_kernel<FMT, TB, DET>), dim3(c.grid), dim3(kThreads), lds, st, a);
   return hipGetLastError();
+}
+
+// The fixed-order sums are a separate instance: the atomic-sum instance
+// carries none of their code.
+template <int FMT, int TB>
+hipError_t launch_fmt(const LayerArgs& a, size_t lds, hipStream_t st, int* grid_out) {
+  return a.det ? launch_det<FMT, TB, true>(a, lds, st, grid_out)
+               : launch_det<FMT, TB, false>(a, lds, st, grid_out);
 }
 
 template <int FMT>
