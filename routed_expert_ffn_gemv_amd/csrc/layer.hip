@@ -287,7 +287,6 @@ struct Lds {
   int ncand[kTMax];          // per-token candidate counts
   uint64_t hmask[kTMax];     // per token: the choices j that hit a resident slot (bit j)
   alignas(16) uint32_t tmp[32];
-  int cstart[kWaves + 1];   // this workgroup's waves' gate/up task ranges
   int dstart[2];            // this workgroup's down unit range (contiguous split)
   int dalign[2];            // the same, bucket-aligned split
   int dzero;                // 1: some bucket got no workgroup in the aligned split
@@ -1654,35 +1653,35 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   const int tpe = a.I / kRowsGU;
   const int n_tasks = n_act * tpe;
   const int lane_gd = lane % kLprD;
-  // Who does what.  One token: gate/up tasks (bucket, row block) dealt to
-  // the waves in turn and down units (bucket, row block) to the workgroups
-  // in turn -- every bucket has one token, so their costs are equal.  More
-  // tokens: buckets differ in size, so each wave takes a contiguous range
-  // of tasks and each workgroup a contiguous range of units with equal sums
-  // of cost (a fixed part plus the bucket's tokens).  Thread u finds the
-  // range bounds that fall inside bucket u's span of cumulative cost.
-  int c_first = b + wave * G, c_end = n_tasks, c_step = kWaves * G;
+  // Who does what.  Gate/up tasks (bucket, row block) are dealt to the waves
+  // in turn, consecutive tasks to consecutive workgroups, so each bucket's
+  // tasks spread over the whole grid (for several tokens this measured
+  // faster than contiguous ranges of equal cost: c3 39.4 -> 38.7 us, c4
+  // 76.1 -> 75.3 us).  Down units (bucket, row block): one token -- every
+  // bucket costs the same -- dealt to the workgroups in turn; several
+  // tokens, by cost (a fixed part plus the bucket's tokens), in the
+  // bucket-aligned split below, else a contiguous range of equal cost per
+  // workgroup, whose bounds thread u finds inside bucket u's span of
+  // cumulative cost.
+  const int c_first = b + wave * G, c_end = n_tasks, c_step = kWaves * G;
   int d_first = b, d_end = n_units, d_step = G;
   if constexpr (TB > 1) {
-    constexpr int kCostC = 2, kCostD = 1;
+    constexpr int kCostD = 1;
     const int n_db = n_act + (a.has_sh ? 1 : 0);
     // (costs stay below 2^20; a bound's exact quotient a * tot / W comes from
     // double arithmetic: the product is exact and no quotient lies within a
     // rounding error of an integer it does not equal)
-    const int totC = tpe * (kCostC * n_act + L.act_start[n_act]);
     const int totD = nrb * (kCostD * n_db + L.act_start[n_act] + (a.has_sh ? T : 0));
     auto bound = [](int i, int tot, int parts) {
       return int(floor(double(i) * double(tot) / double(parts)));
     };
-    // One thread per range bound (kWaves + 1 task bounds, 2 unit bounds):
-    // a binary search for the bucket whose span of cumulative cost holds the
-    // bound's target, then the first task / unit of that bucket at or past it.
-    if (tid <= kWaves + 2) {
-      const bool is_c = tid <= kWaves;
-      const int n = is_c ? n_act : n_db;
-      const int rows = is_c ? tpe : nrb, fixed = is_c ? kCostC : kCostD;
-      const int bt = is_c ? bound(b * kWaves + tid, totC, G * kWaves)
-                          : bound(b + tid - (kWaves + 1), totD, G);
+    // One thread per range bound (2 unit bounds): a binary search for the
+    // bucket whose span of cumulative cost holds the bound's target, then
+    // the first unit of that bucket at or past it.
+    if (tid < 2) {
+      const int n = n_db;
+      const int rows = nrb, fixed = kCostD;
+      const int bt = bound(b + tid, totD, G);
       auto tokens_before = [&](int u) {   // tokens of buckets < u (the shared one last)
         return u <= n_act ? L.act_start[u] : L.act_start[n_act] + T;
       };
@@ -1695,13 +1694,12 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
       }
       int v;
       if (lo == n) {
-        v = is_c ? n_tasks : n_units;
+        v = n_units;
       } else {
         const int cost = fixed + (lo < n_act ? L.act_start[lo + 1] - L.act_start[lo] : T);
         v = lo * rows + (bt - cum(lo) + cost - 1) / cost;
       }
-      if (is_c) L.cstart[tid] = v;
-      else L.dstart[tid - (kWaves + 1)] = v;
+      L.dstart[tid] = v;
     }
     // Down units, bucket-aligned: bucket u gets the workgroups [s(u), s(u+1)),
     // s(u) = floor(G * cum(u) / totD) with cum the cumulative cost, and its
@@ -1727,9 +1725,6 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
       }
     }
     __syncthreads();
-    c_first = L.cstart[wave];
-    c_end = L.cstart[wave + 1];
-    c_step = 1;
     const bool aligned = L.dzero == 0;
     d_first = aligned ? L.dalign[0] : L.dstart[0];
     d_end = aligned ? L.dalign[1] : L.dstart[1];
