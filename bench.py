@@ -318,14 +318,12 @@ def bench_decode(args, cfg_name, steps=None, warmup=None, cpu_calls=None):
     return out
 
 
-PHASES = [(0, "start"), (2, "tokens staged"), (22, "  router (wave 0): logits computed"),
-          (23, "  router (wave 0): its stores landed"), (3, "router/shared tasks (wave 0)"),
+PHASES = [(0, "start"), (2, "tokens staged"), (3, "router/shared tasks (wave 0)"),
           (21, "router/shared tasks (last wave)"), (4, "every logit seen (wave 0)"),
           (11, "every logit seen (all waves)"),
           (16, "  routing: candidates listed"), (17, "  routing: second barrier"),
           (18, "  routing: ranks"), (19, "  routing: gates"), (20, "  routing: resolved"),
-          (5, "routing done"), (28, "  gate/up rows arrived (wave 0, one token)"),
-          (6, "gate/up done (wave 0)"), (7, "gate/up done (last wave)"),
+          (5, "routing done"), (6, "gate/up done (wave 0)"), (7, "gate/up done (last wave)"),
           (12, "down phase entered"), (24, "  down: LDS free (barrier)"),
           (25, "  down: h sources set (barrier)"), (13, "first unit's h present"),
           (26, "  down: h converted (thread 0)"), (27, "  down: staging barrier"),

@@ -260,11 +260,8 @@ void moe_set_wait_budget(uint64_t ns, int32_t hold);
  * on, words 14 and 15 thread 0's poll rounds for that h and (one token)
  * for the logits; words 16-20 steps of routing (candidates listed, second
  * barrier (one token only), ranks, gates, resolution), word 21 the last
- * wave's router/shared tasks done, 22 and 23 wave 0's router task before
- * and after the wait for its stores, 24-27 steps of the first down unit's
- * staging (two barriers, h converted, staging barrier), and 28 (one token)
- * wave 0's gate/up rows arrived (with tracing on, the wave waits for them
- * before it stamps).
+ * wave's router/shared tasks done, and 24-27 steps of the first down
+ * unit's staging (two barriers, h converted, staging barrier).
  * Every launch overwrites the rows it writes.  Process-wide, read when a
  * call is issued. */
 void moe_set_trace(uint64_t* trace);

@@ -96,14 +96,11 @@ enum TraceSlot {
   kTrRtGate = 19,      // gates made
   kTrRtResolved = 20,  // slots and miss list resolved
   kTrTasksAAll = 21,   // the workgroup's last wave's router / shared-expert tasks done
-  kTrRtComputed = 22,  // wave 0's router task: logits computed (before the wait for its stores)
-  kTrRtStored = 23,    // wave 0's router task: its stores landed (logits publish next)
   // first down unit
   kTrDBar1 = 24,       // after the barrier that ends the LDS use of gate/up
   kTrDBar2 = 25,       // after the barrier that publishes the h sources
   kTrHConv = 26,       // h converted and stored in LDS (thread 0)
   kTrHBar = 27,        // after the staging barrier
-  kTrRowsGU = 28,      // wave 0's gate/up rows arrived (one token; the trace waits for them)
   kTraceSlots = 32
 };
 

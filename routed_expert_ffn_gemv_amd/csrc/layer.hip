@@ -1001,9 +1001,7 @@ __device__ __forceinline__ void router_compute(const RouterRegs<FMT>& R, const L
   if (lpr >= 64)
 #pragma unroll
     for (int t = 0; t < TB; ++t) acc[t] += __shfl_xor(acc[t], 32, 64);
-  stamp_now(a.trace, kTrRtComputed);
   wait_mem();
-  stamp_now(a.trace, kTrRtStored);
   if (e < a.E && lane_g == 0) {
 #pragma unroll
     for (int t = 0; t < TB; ++t)
@@ -1806,10 +1804,6 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     // issued on one path and not on another, which would make the waits
     // for the rows also wait for the prefetch.
     if (TB == 1 && task + c_step >= c_end) {
-      if (a.trace) {   // diagnostics only: wait for the rows, then stamp
-        wait_mem();
-        stamp_now(a.trace, kTrRowsGU);
-      }
       if (task < c_end) compute_task(task, rg, ru);
       task = c_end;
     }
