@@ -262,8 +262,10 @@ void moe_set_wait_budget(uint64_t ns, int32_t hold);
  * barrier (one token only), ranks, gates, resolution), word 21 the last
  * wave's router/shared tasks done, and 24-27 steps of the first down
  * unit's staging (two barriers, h converted, staging barrier).
- * Every launch overwrites the rows it writes.  Process-wide, read when a
- * call is issued. */
+ * Every launch overwrites the rows it writes.  Traced calls run a separate
+ * instance of the fused kernel (the untraced one carries no stamps); calls
+ * with fixed-order sums (moe_set_deterministic) are not traced.
+ * Process-wide, read when a call is issued. */
 void moe_set_trace(uint64_t* trace);
 
 /* Order of the sums into y of later fused moe_layer launches (and of

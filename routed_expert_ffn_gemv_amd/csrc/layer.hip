@@ -478,7 +478,7 @@ template <int FMT>
 __device__ __forceinline__ void stage_h(const uint64_t* const* srcs, int n, int K, uint32_t* xd,
                                         float* sd, float* sd2, float* bsc, int vs,
                                         uint32_t epoch, const LayerArgs& a, Lds& L, uint64_t t0,
-                                        bool trace_h) {
+                                        uint64_t* trc) {
   const int per_vec = K / 16;
   const int n_items = n * per_vec;
   constexpr int kIt = 2;   // items per thread and batch
@@ -512,9 +512,9 @@ __device__ __forceinline__ void stage_h(const uint64_t* const* srcs, int n, int 
           if (src[r] && !tag_ok(wv[r][c], epoch)) wv[r][c] = ld_dev(src[r] + c);
       ++rounds;
     }
-    if (base == 0 && trace_h) {
-      stamp_now(a.trace, kTrHPolled);
-      stamp(a.trace, kTrHPolls, uint64_t(rounds));
+    if (base == 0 && trc) {
+      stamp_now(trc, kTrHPolled);
+      stamp(trc, kTrHPolls, uint64_t(rounds));
     }
 #pragma unroll
     for (int r = 0; r < kIt; ++r) {
@@ -586,7 +586,7 @@ __device__ __forceinline__ void stage_h(const uint64_t* const* srcs, int n, int 
       }
     }
   }
-  if (trace_h) stamp_now(a.trace, kTrHConv);
+  if (trc) stamp_now(trc, kTrHConv);
 }
 
 // --------------------------------------------------------------- row tiles
@@ -1230,7 +1230,8 @@ __device__ __forceinline__ void wave_lds_sync() {
 // per-wave selection instead.  lg receives the logits.  Only wave 0 of a
 // writer workgroup stores the outputs.
 __device__ __forceinline__ void route_token(const LayerArgs& a, float* lg, int E, int k, Lds& L,
-                                            uint32_t epoch, bool writer, uint64_t t0) {
+                                            uint32_t epoch, bool writer, uint64_t t0,
+                                            uint64_t* trc) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int kR = kEMax / kThreads;
   uint64_t w[kR];
@@ -1250,9 +1251,9 @@ __device__ __forceinline__ void route_token(const LayerArgs& a, float* lg, int E
         w[r] = ld_dev(region_lg(a) + tid + r * kThreads);
     ++rounds;
   }
-  if (a.trace) {
-    stamp_now(a.trace, kTrLogits);
-    stamp(a.trace, kTrLgPolls, uint64_t(rounds));
+  if (trc) {
+    stamp_now(trc, kTrLogits);
+    stamp(trc, kTrLgPolls, uint64_t(rounds));
   }
   uint64_t key[kR];   // 0: no expert
   uint32_t m = 0u;    // largest logit bits of the thread
@@ -1275,7 +1276,7 @@ __device__ __forceinline__ void route_token(const LayerArgs& a, float* lg, int E
   if ((tid & 15) == 0) L.tmp[tid >> 4] = m;
   if (tid < 64) L.rkey[tid] = 0ull;   // the candidate list's empty slots
   __syncthreads();
-  stamp_now(a.trace, kTrLogitsAll);
+  stamp_now(trc, kTrLogitsAll);
   const bool thresh = k <= kTopkListMax;
   if (thresh) {
     const uint32_t my = L.tmp[lane & 31];
@@ -1309,9 +1310,9 @@ __device__ __forceinline__ void route_token(const LayerArgs& a, float* lg, int E
       }
     }
   }
-  stamp_now(a.trace, kTrRtCand);
+  stamp_now(trc, kTrRtCand);
   __syncthreads();
-  stamp_now(a.trace, kTrRtBar2);
+  stamp_now(trc, kTrRtBar2);
   // The count, this lane's candidate and the first eight candidates are
   // read together; list slots past the count hold key 0 (zeroed before the
   // first barrier), which is below every key.
@@ -1339,7 +1340,7 @@ __device__ __forceinline__ void route_token(const LayerArgs& a, float* lg, int E
     const uint32_t lo = uint32_t(__builtin_amdgcn_ds_permute(to, int(uint32_t(ck))));
     my_e = int(~lo);
     my_v = key_value(hi);
-    stamp_now(a.trace, kTrRtRank);
+    stamp_now(trc, kTrRtRank);
   } else if (E <= 512) {
     wave_topk<8>(lg, E, k, lane, &my_e, &my_v);
   } else {
@@ -1353,7 +1354,7 @@ __device__ __forceinline__ void route_token(const LayerArgs& a, float* lg, int E
   const float vmax = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_v), 0));
   const float ex = lane < k ? __expf(my_v - vmax) : 0.f;
   const float g = ex * __frcp_rn(wave_sum_f32(ex));
-  stamp_now(a.trace, kTrRtGate);
+  stamp_now(trc, kTrRtGate);
   const bool out = writer && wave == 0;
   if (lane < k) {
     L.idx[lane] = my_e;
@@ -1365,7 +1366,7 @@ __device__ __forceinline__ void route_token(const LayerArgs& a, float* lg, int E
   }
   resolve_one(a, L, my_e, g, lane, out);
   wave_lds_sync();
-  stamp_now(a.trace, kTrRtResolved);
+  stamp_now(trc, kTrRtResolved);
 }
 
 // Resolution of the P = T*k pairs of T >= 2 tokens (thread p = pair p).
@@ -1443,7 +1444,7 @@ __device__ __forceinline__ void resolve_multi(const LayerArgs& a, Lds& L, int P,
 // --------------------------------------------------------------- kernel
 // TB: the largest token count the instance serves (1, 4 or 16), so per-token
 // loops are unrolled no further than needed.
-template <int FMT, int TB, bool DET>
+template <int FMT, int TB, bool DET, bool TR>
 __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   constexpr int kLprGU = Lanes<FMT>::kGU, kRowsGU = Lanes<FMT>::kRowsGU;
   constexpr int kLprD = Lanes<FMT>::kD, kRowsD = Lanes<FMT>::kRowsD;
@@ -1457,6 +1458,10 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   const int G = gridDim.x, b = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   if (tid == 0) sa = ka;
+  // Phase stamps only in the traced instance: with tracing off the kernel
+  // carries none of their code (a few stamps measured 0.3-0.8 us per call
+  // even when not taken).
+  uint64_t* const trc = TR ? ka.trace : nullptr;
   const int T = ka.T, k = ka.k, P = T * k, E = ka.E;
   const int K = ka.H;
   const int vstride = FMT == MOE_W_F32 ? K : (K / Fmt<FMT>::kWPC) * Fmt<FMT>::kCS;
@@ -1468,11 +1473,11 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
 
   // ---- A: loads first (call counter and error word, slot table, first task's rows)
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();   // start of this workgroup's waits
-  if (ka.trace) {
+  if (trc) {
     uint32_t xcc;
     asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
-    stamp(ka.trace, kTrStart, t0);
-    stamp(ka.trace, kTrXcd, xcc & 0xFu);
+    stamp(trc, kTrStart, t0);
+    stamp(trc, kTrXcd, xcc & 0xFu);
   }
   // every wave reads the header (its router task zeroes y only on a sound workspace)
   const uint64_t hdr = lane == 0 ? ld_dev(reinterpret_cast<const uint64_t*>(ka.region)) : 0ull;
@@ -1529,7 +1534,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   __syncthreads();
   if (L.failed == 2) return;   // every thread: nothing is written
   const LayerArgs& a = sa;
-  stamp_now(a.trace, kTrStaged);
+  stamp_now(trc, kTrStaged);
   const uint32_t epoch = L.calls + 1u;   // this call's number
   if (a.debug_hold && b == 0 && tid == 0) {
     // test hook: wait for a word nothing writes until the budget is spent
@@ -1552,8 +1557,8 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     }
   }
 
-  stamp_now(a.trace, kTrTasksA);
-  if (a.trace && lane == 0)
+  stamp_now(trc, kTrTasksA);
+  if (trc && lane == 0)
     atomicMax(&L.t_a, static_cast<unsigned long long>(__builtin_amdgcn_s_memrealtime()));
   // this workgroup has read the counter (workgroup 0 checks before it
   // advances the counter)
@@ -1561,7 +1566,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
 
   // ---- B: every logit of this call, then routing
   if constexpr (TB == 1) {
-    route_token(a, lg, E, k, L, epoch, b == 0, t0);
+    route_token(a, lg, E, k, L, epoch, b == 0, t0, trc);
   } else {
     const int n_lg = T * E;
     constexpr int kR = TB * kEMax / kThreads > 16 ? 16 : TB * kEMax / kThreads;
@@ -1593,12 +1598,12 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
         if (i < n_lg) lg[i] = tag_val(w[r]);
       }
     }
-  stamp_now(a.trace, kTrLogits);
+  stamp_now(trc, kTrLogits);
   __syncthreads();
-  stamp_now(a.trace, kTrLogitsAll);
+  stamp_now(trc, kTrLogitsAll);
   const bool thresh = k <= kTopkListMax;
   if (thresh) topk_threshold<TB>(lg, T, E, k, L);
-  stamp_now(a.trace, kTrRtCand);
+  stamp_now(trc, kTrRtCand);
   // tokens the threshold selection did not take: one wave each
   for (int t = wave; t < T; t += kWaves) {
     if (thresh && L.ncand[t] <= kThreads / TB) continue;
@@ -1612,7 +1617,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     }
   }
   __syncthreads();
-  stamp_now(a.trace, kTrRtRank);
+  stamp_now(trc, kTrRtRank);
   for (int t = wave; t < T; t += kWaves) {
     // gates: softmax over the k chosen logits (choice 0 is the largest)
     const int my_e = lane < k ? L.idx[t * k + lane] : 0;
@@ -1630,13 +1635,13 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     }
   }
   __syncthreads();
-  stamp_now(a.trace, kTrRtGate);
+  stamp_now(trc, kTrRtGate);
   resolve_multi(a, L, P, b == 0);   // T >= 2 here
   __syncthreads();
-  stamp_now(a.trace, kTrRtResolved);
+  stamp_now(trc, kTrRtResolved);
   }
-  stamp_now(a.trace, kTrRouted);
-  if (a.trace) stamp(a.trace, kTrTasksAAll, L.t_a);
+  stamp_now(trc, kTrRouted);
+  if (trc) stamp(trc, kTrTasksAAll, L.t_a);
   const int n_act = L.n_act;
   if (b == 0 && a.usage && tid < P)
     __hip_atomic_fetch_add(gmem_w(a.usage + L.idx[tid]), 1u, __ATOMIC_RELAXED,
@@ -1824,13 +1829,13 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     }
   }
 
-  if (a.trace) {   // this wave's gate/up end
+  if (trc) {   // this wave's gate/up end
     const uint64_t t = __builtin_amdgcn_s_memrealtime();
     if (lane == 0) atomicMax(&L.t_gu, static_cast<unsigned long long>(t));
-    if (wave == 0) stamp(a.trace, kTrGateUp0, t);
+    if (wave == 0) stamp(trc, kTrGateUp0, t);
   }
   // ---- D: down units (expert or shared, block of rows), y += gate * D h
-  stamp_now(a.trace, kTrDStart);
+  stamp_now(trc, kTrDStart);
   {
     uint32_t* xd = smem;                                    // reuses the token area
     float* sd = reinterpret_cast<float*>(xd + kTMax * vs_d);
@@ -1854,18 +1859,19 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
       const int r = rb * kRowsD + wave * (64 / kLprD) + lane / kLprD;
       if (u != staged) {
         __syncthreads();   // gate/up tasks and the previous unit are done with the LDS
-        if (staged < 0) stamp_now(a.trace, kTrDBar1);
+        if (staged < 0) stamp_now(trc, kTrDBar1);
         if (tid < n)
           srcs[tid] = shared ? region_h_sh(a) + int64_t(tid) * Kd
                              : region_h(a) + int64_t(L.bpair[st + tid]) * Kd;
         __syncthreads();
-        if (staged < 0) stamp_now(a.trace, kTrDBar2);
-        stage_h<FMT>(srcs, n, Kd, xd, sd, sd2, bsc, vs_d, epoch, a, L, t0, staged < 0);
+        if (staged < 0) stamp_now(trc, kTrDBar2);
+        stage_h<FMT>(srcs, n, Kd, xd, sd, sd2, bsc, vs_d, epoch, a, L, t0,
+                     staged < 0 ? trc : nullptr);
         __syncthreads();
-        if (staged < 0 && a.trace) {
-          stamp(a.trace, kTrHBar, __builtin_amdgcn_s_memrealtime());
-          stamp(a.trace, kTrStagedH, __builtin_amdgcn_s_memrealtime());
-          stamp(a.trace, kTrGateUpAll, L.t_gu);
+        if (staged < 0 && trc) {
+          stamp(trc, kTrHBar, __builtin_amdgcn_s_memrealtime());
+          stamp(trc, kTrStagedH, __builtin_amdgcn_s_memrealtime());
+          stamp(trc, kTrGateUpAll, L.t_gu);
         }
         staged = u;
       }
@@ -1901,7 +1907,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
       rd = nd;
     }
   }
-  stamp_now(a.trace, kTrDown);
+  stamp_now(trc, kTrDown);
   if constexpr (DET) {
     // Fixed-order sums: this workgroup's share of y, each element by one
     // thread: the hit choices j = 0 .. k-1 in order, then the shared expert
@@ -1955,7 +1961,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     __syncthreads();
     if (tid == 0 && !L.failed) st_dev(region_calls(a), epoch);
   }
-  stamp_now(a.trace, kTrEnd);
+  stamp_now(trc, kTrEnd);
   asm volatile("" ::"v"(pf));   // the prefetch's value counts as used
 }
 
@@ -1965,18 +1971,18 @@ struct Occ {
   int grid = 0;
 };
 
-template <int FMT, int TB, bool DET>
+template <int FMT, int TB, bool DET, bool TR>
 hipError_t launch_det(const LayerArgs& a, size_t lds, hipStream_t st, int* grid_out) {
   static thread_local Occ c;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (c.lds != lds || c.device != dev) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_layer_kernel<FMT, TB, DET>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_layer_kernel<FMT, TB, DET, TR>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return e;
     int per_cu = 0, cus = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, moe_layer_kernel<FMT, TB, DET>, kThreads,
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, moe_layer_kernel<FMT, TB, DET, TR>, kThreads,
                                                      lds);
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -1988,16 +1994,18 @@ hipError_t launch_det(const LayerArgs& a, size_t lds, hipStream_t st, int* grid_
     c.grid = cus;   // one workgroup of 8 waves per CU
   }
   if (grid_out) *grid_out = c.grid;
-  hipLaunchKernelGGL((moe_layer_kernel<FMT, TB, DET>), dim3(c.grid), dim3(kThreads), lds, st, a);
+  hipLaunchKernelGGL((moe_layer_kernel<FMT, TB, DET, TR>), dim3(c.grid), dim3(kThreads), lds, st, a);
   return hipGetLastError();
 }
 
-// The fixed-order sums are a separate instance: the atomic-sum instance
-// carries none of their code.
+// The fixed-order sums and the phase stamps are separate instances: the
+// plain instance carries none of their code.  (The fixed-order instance is
+// not traced.)
 template <int FMT, int TB>
 hipError_t launch_fmt(const LayerArgs& a, size_t lds, hipStream_t st, int* grid_out) {
-  return a.det ? launch_det<FMT, TB, true>(a, lds, st, grid_out)
-               : launch_det<FMT, TB, false>(a, lds, st, grid_out);
+  if (a.det) return launch_det<FMT, TB, true, false>(a, lds, st, grid_out);
+  return a.trace ? launch_det<FMT, TB, false, true>(a, lds, st, grid_out)
+                 : launch_det<FMT, TB, false, false>(a, lds, st, grid_out);
 }
 
 template <int FMT>
