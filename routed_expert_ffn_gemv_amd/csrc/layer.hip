@@ -1229,9 +1229,10 @@ __device__ __forceinline__ void wave_lds_sync() {
 // More than 64 candidates (many equal logits) or k > kTopkListMax: the
 // per-wave selection instead.  lg receives the logits.  Only wave 0 of a
 // writer workgroup stores the outputs.
+template <typename OnChoices>
 __device__ __forceinline__ void route_token(const LayerArgs& a, float* lg, int E, int k, Lds& L,
                                             uint32_t epoch, bool writer, uint64_t t0,
-                                            uint64_t* trc) {
+                                            uint64_t* trc, OnChoices on_choices) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int kR = kEMax / kThreads;
   uint64_t w[kR];
@@ -1351,6 +1352,7 @@ __device__ __forceinline__ void route_token(const LayerArgs& a, float* lg, int E
     my_e = 0;
     my_v = 0.f;
   }
+  on_choices(my_e);   // lane r < k holds choice r
   const float vmax = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_v), 0));
   const float ex = lane < k ? __expf(my_v - vmax) : 0.f;
   const float g = ex * __frcp_rn(wave_sum_f32(ex));
@@ -1566,7 +1568,22 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
 
   // ---- B: every logit of this call, then routing
   if constexpr (TB == 1) {
-    route_token(a, lg, E, k, L, epoch, b == 0, t0, trc);
+    // The wave's gate/up task needs only its expert's slot, known once the
+    // choices are: its rows load from there, before the gates and the
+    // resolution (which build the same bucket list: hits in choice order).
+    const int tpe1 = a.I / kRowsGU, c1 = b + wave * G;
+    route_token(a, lg, E, k, L, epoch, b == 0, t0, trc, [&](int my_e) {
+      const int s = lane < k ? slot_of_choice(a, L, my_e) : -1;
+      const uint64_t hm = __ballot(s >= 0);
+      const int u = c1 / tpe1;
+      if (u < __popcll(hm)) {
+        const int hpos = __builtin_amdgcn_mbcnt_hi(uint32_t(hm >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo(uint32_t(hm), 0u));
+        const uint64_t at = __ballot(s >= 0 && hpos == u);
+        const int slot = __builtin_amdgcn_readlane(s, __builtin_ctzll(at));
+        gateup_load<FMT>(rg, ru, a, a.g, a.u, slot, (c1 % tpe1) * kRowsGU + lane / kLprGU, lane_gu);
+      }
+    });
   } else {
     const int n_lg = T * E;
     constexpr int kR = TB * kEMax / kThreads > 16 ? 16 : TB * kEMax / kThreads;
@@ -1792,7 +1809,8 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     };
     int task = c_first;
     RowRegs<FMT, nch_gu<FMT>()> ng, nu;
-    if (task < c_end) load_task(task, rg, ru);
+    // (one token: the first task's rows were issued during routing)
+    if (TB > 1 && task < c_end) load_task(task, rg, ru);
     if (kAhead == 2 && task + c_step < c_end) load_task(task + c_step, ng, nu);
     // one token: the first down unit's lines head for the L2 meanwhile
     if constexpr (TB == 1) pf = prefetch_down(d_first < d_end ? d_first : -1);
