@@ -112,14 +112,14 @@ KERNEL_SOURCES = {
 TRAFFIC = {
     # workload: {"sha256": ..., "bytes": fetched + written per launch}
     # c2: the moe_layer kernel (profiles/c2_decode_layer_hbm_traffic.md)
-    "c2_decode_layer_q2": {"sha256": "8f3197ae83bfe4df03f57af0e8e7f3bdd37392c5167d4667d62c58304cc1481c",
-                           "bytes": 23038862},
+    "c2_decode_layer_q2": {"sha256": "9e9566846c7428ac5672163544ff2743acc6c183cdd8c888f03e7d9f12c267ff",
+                           "bytes": 23079431},
     # c3: the moe_layer kernel (profiles/c3_verify_stack_hbm_traffic.md)
-    "c3_verify_stack_q2": {"sha256": "8f3197ae83bfe4df03f57af0e8e7f3bdd37392c5167d4667d62c58304cc1481c",
-                           "bytes": 70271106},
+    "c3_verify_stack_q2": {"sha256": "9e9566846c7428ac5672163544ff2743acc6c183cdd8c888f03e7d9f12c267ff",
+                           "bytes": 70151618},
     # c4: the moe_layer kernel (profiles/c4_slot_tiering_hbm_traffic.md)
-    "c4_slot_tiering_q2": {"sha256": "8f3197ae83bfe4df03f57af0e8e7f3bdd37392c5167d4667d62c58304cc1481c",
-                           "bytes": 121610675},
+    "c4_slot_tiering_q2": {"sha256": "9e9566846c7428ac5672163544ff2743acc6c183cdd8c888f03e7d9f12c267ff",
+                           "bytes": 121597985},
     # c5: the kernels of one moe_expert_ffn call (active list, schedule, x16,
     # gate/up and down GEMMs; profiles/c5_prefill_hbm_traffic.md)
     "c5_prefill_q4": {"sha256": "60e44c72388bf65f02e182f4083d57b020dc015a61f0d171f19085e8a1ed5810",
