@@ -96,11 +96,14 @@ enum TraceSlot {
   kTrRtGate = 19,      // gates made
   kTrRtResolved = 20,  // slots and miss list resolved
   kTrTasksAAll = 21,   // the workgroup's last wave's router / shared-expert tasks done
+  kTrTkSeg = 22,       // several tokens: segment maxima published (first top-k barrier)
+  kTrTkTau = 23,       // several tokens: thresholds found (second barrier)
   // first down unit
   kTrDBar1 = 24,       // after the barrier that ends the LDS use of gate/up
   kTrDBar2 = 25,       // after the barrier that publishes the h sources
   kTrHConv = 26,       // h converted and stored in LDS (thread 0)
   kTrHBar = 27,        // after the staging barrier
+  kTrTkCand = 28,      // several tokens: candidates listed (third barrier)
   kTraceSlots = 32
 };
 

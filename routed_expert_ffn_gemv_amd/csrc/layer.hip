@@ -1049,7 +1049,8 @@ __device__ __forceinline__ uint64_t key_max_dpp(uint64_t v) {
 // A token with more than CAP candidates (many equal logits) is left to the
 // caller.  Called by every thread; k <= kTopkListMax.
 template <int TB, int KPT>   // KPT: keys per thread, E <= KPT * kThreads / TB
-__device__ __forceinline__ void topk_threshold_k(const float* lg, int T, int E, int k, Lds& L) {
+__device__ __forceinline__ void topk_threshold_k(const float* lg, int T, int E, int k, Lds& L,
+                                                 uint64_t* trc) {
   constexpr int GS = kThreads / TB, SL = GS / 32, CAP = kThreads / TB;
   const int tid = threadIdx.x, t = tid / GS, j = tid % GS;
   const bool on = t < T;
@@ -1070,6 +1071,7 @@ __device__ __forceinline__ void topk_threshold_k(const float* lg, int T, int E, 
   if constexpr (SL >= 16) m = key_max_dpp<0x140>(m);  // row_mirror
   if (on && j % SL == 0) L.rkey[t * 32 + j / SL] = m;
   __syncthreads();
+  stamp_now(trc, kTrTkSeg);
   {
     const int tt = tid / 32, sg = tid % 32;
     if (tt < T) {
@@ -1088,6 +1090,7 @@ __device__ __forceinline__ void topk_threshold_k(const float* lg, int T, int E, 
     }
   }
   __syncthreads();
+  stamp_now(trc, kTrTkTau);
   if (on) {
     const uint64_t tau = L.tau[t];
     int c = 0;
@@ -1104,6 +1107,7 @@ __device__ __forceinline__ void topk_threshold_k(const float* lg, int T, int E, 
     }
   }
   __syncthreads();
+  stamp_now(trc, kTrTkCand);
   if (on) {
     const int n = L.ncand[t];
     if (n <= CAP) {
@@ -1131,12 +1135,13 @@ __device__ __forceinline__ void topk_threshold_k(const float* lg, int T, int E, 
 }
 
 template <int TB>
-__device__ __forceinline__ void topk_threshold(const float* lg, int T, int E, int k, Lds& L) {
+__device__ __forceinline__ void topk_threshold(const float* lg, int T, int E, int k, Lds& L,
+                                               uint64_t* trc) {
   constexpr int GS = kThreads / TB, KMAX = kEMax / GS;
   if (KMAX >= 2 && E <= GS * (KMAX / 2))
-    topk_threshold_k<TB, (KMAX >= 2 ? KMAX / 2 : 1)>(lg, T, E, k, L);
+    topk_threshold_k<TB, (KMAX >= 2 ? KMAX / 2 : 1)>(lg, T, E, k, L, trc);
   else
-    topk_threshold_k<TB, KMAX>(lg, T, E, k, L);
+    topk_threshold_k<TB, KMAX>(lg, T, E, k, L, trc);
 }
 
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
@@ -1378,6 +1383,125 @@ __device__ __forceinline__ void route_token(const LayerArgs& a, float* lg, int E
   resolve_one(a, L, my_e, g, lane, out);
   wave_lds_sync();
   stamp_now(trc, kTrRtResolved);
+}
+
+// Routing of up to four tokens (E <= 512, k <= kTopkListMax) in three
+// barriers: the one-token scheme with two waves per token.  Token t owns
+// the 128 threads of waves 2t and 2t + 1; thread j of them holds experts
+// 4j .. 4j + 3, and each of the 32 segments of 16 experts (four
+// neighbouring threads) publishes the logit bits of its largest key.
+// After the first barrier each of the token's waves finds tau -- the
+// smallest of those 32 values with fewer than k larger ones, so that at
+// least k keys reach it and the k best all do -- and lists its keys that
+// reach tau through one LDS add per wave.  After the second barrier the
+// token's first wave ranks the candidates (keys are unique), moves choice r
+// to lane r, makes the gates and writes the choices.  A token with more
+// than 64 candidates (many equal logits) takes the exact per-wave
+// selection instead.  L.idx and L.gate receive the choices and gates as
+// from topk_threshold and the gate step; writer: also the outputs.
+__device__ __forceinline__ void route_few(const LayerArgs& a, const float* lg, int T, int E, int k,
+                                          Lds& L, bool writer, uint64_t* trc) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t = tid >> 7, j = tid & 127;
+  const bool on = t < T;
+  uint32_t* seg = reinterpret_cast<uint32_t*>(L.idx);   // [t][32], until the choices
+  uint64_t key[4];   // 0: no expert
+  uint32_t m = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = 4 * j + i;
+    key[i] = 0ull;
+    if (on && e < E) {
+      const uint32_t ob = ordered_bits(lg[t * E + e]);
+      key[i] = (uint64_t(ob) << 32) | uint64_t(~uint32_t(e));
+      m = max(m, ob);
+    }
+  }
+  m = max(m, dpp_u32<0xB1>(m));   // quad_perm [1,0,3,2]
+  m = max(m, dpp_u32<0x4E>(m));   // quad_perm [2,3,0,1]
+  if (on && (j & 3) == 0) seg[t * 32 + (j >> 2)] = m;
+  if (tid < 4 * 64) L.rkey[tid] = 0ull;   // the candidate lists' empty slots
+  __syncthreads();
+  stamp_now(trc, kTrTkSeg);
+  if (on) {
+    const uint32_t my = seg[t * 32 + (lane & 31)];
+    const u32x4* half = reinterpret_cast<const u32x4*>(seg + t * 32) + 4 * (lane >> 5);
+    int gt = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 o = half[q];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) gt += o[c] > my ? 1 : 0;
+    }
+    gt += __shfl_xor(gt, 32, 64);
+    const uint32_t tau = ~wave_max_u32(gt <= k - 1 ? ~my : 0u);
+    uint64_t cm[4];
+    int cnt = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      cm[r] = __ballot(key[r] != 0ull && uint32_t(key[r] >> 32) >= tau);
+      cnt += __popcll(cm[r]);
+    }
+    if (cnt > 0) {
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&L.ncand[t], cnt);
+      base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pos = base + lanes_below(cm[r]);
+        if (((cm[r] >> lane) & 1ull) && pos < 64) L.rkey[t * 64 + pos] = key[r];
+        base += __popcll(cm[r]);
+      }
+    }
+  }
+  __syncthreads();
+  stamp_now(trc, kTrTkTau);
+  if (on && (wave & 1) == 0) {
+    const int n = L.ncand[t];
+    int my_e = 0;
+    float my_v = 0.f;
+    if (n <= 64) {
+      const uint64_t* list = L.rkey + t * 64;
+      const uint64_t ck = list[lane];
+      int r = 0;
+      for (int j0 = 0; j0 < n; j0 += 8) {   // candidates j0 .. j0 + 7 above ck
+        u32x4 q[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) q[h] = reinterpret_cast<const u32x4*>(list + j0)[h];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          r += ((uint64_t(q[h][1]) << 32) | q[h][0]) > ck ? 1 : 0;
+          r += ((uint64_t(q[h][3]) << 32) | q[h][2]) > ck ? 1 : 0;
+        }
+      }
+      // choice r moves to lane r (k <= 16 < 63, the lane that takes the rest)
+      const int to = 4 * ((lane < n && r < k) ? r : 63);
+      const uint32_t hi = uint32_t(__builtin_amdgcn_ds_permute(to, int(uint32_t(ck >> 32))));
+      const uint32_t lo = uint32_t(__builtin_amdgcn_ds_permute(to, int(uint32_t(ck))));
+      my_e = int(~lo);
+      my_v = key_value(hi);
+    } else {
+      wave_topk<8>(lg + t * E, E, k, lane, &my_e, &my_v);
+    }
+    // gates: softmax over the k chosen logits (choice 0 is the largest)
+    if (lane >= k) {
+      my_e = 0;
+      my_v = 0.f;
+    }
+    const float vmax = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_v), 0));
+    const float ex = lane < k ? expf(my_v - vmax) : 0.f;
+    const float z = wave_sum_f32(ex);
+    const float g = ex / z;
+    if (lane < k) {
+      L.idx[t * k + lane] = my_e;
+      L.gate[t * k + lane] = g;
+      if (writer) {
+        *gmem_w(a.idx + t * k + lane) = my_e;
+        *gmem_w(a.gate + t * k + lane) = g;
+      }
+    }
+  }
+  __syncthreads();
 }
 
 // Resolution of the P = T*k pairs of T >= 2 tokens (thread p = pair p).
@@ -1636,8 +1760,12 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   stamp_now(trc, kTrLogits);
   __syncthreads();
   stamp_now(trc, kTrLogitsAll);
+  if (TB == 4 && E <= 512 && k <= kTopkListMax) {
+    route_few(a, lg, T, E, k, L, b == 0, trc);
+    stamp_now(trc, kTrRtGate);
+  } else {
   const bool thresh = k <= kTopkListMax;
-  if (thresh) topk_threshold<TB>(lg, T, E, k, L);
+  if (thresh) topk_threshold<TB>(lg, T, E, k, L, trc);
   stamp_now(trc, kTrRtCand);
   // tokens the threshold selection did not take: one wave each
   for (int t = wave; t < T; t += kWaves) {
@@ -1671,6 +1799,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   }
   __syncthreads();
   stamp_now(trc, kTrRtGate);
+  }
   resolve_multi(a, L, P, b == 0);   // T >= 2 here
   __syncthreads();
   stamp_now(trc, kTrRtResolved);
