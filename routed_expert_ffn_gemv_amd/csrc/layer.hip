@@ -48,6 +48,7 @@
 // access still stays in bounds), and later calls on the workspace return at
 // once until the caller zeroes it again (moe_layer_check reports it).
 #include <mutex>
+#include <type_traits>
 
 #include "gemv_core.h"
 #include "kernels.h"
@@ -1156,8 +1157,8 @@ template <int CTRL, int ROWS>
 __device__ __forceinline__ uint32_t dpp_shift(uint32_t v) {
   return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, ROWS, 0xF, true));
 }
-__device__ __forceinline__ uint32_t block_scan_u32(uint32_t v, uint32_t* wtot, uint32_t* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Inclusive sum over the lanes of the wave up to this one.
+__device__ __forceinline__ uint32_t wave_scan_u32(uint32_t v) {
   uint32_t x = v;
   x += dpp_shift<0x111, 0xF>(x);   // row_shr:1
   x += dpp_shift<0x112, 0xF>(x);   // row_shr:2
@@ -1165,6 +1166,11 @@ __device__ __forceinline__ uint32_t block_scan_u32(uint32_t v, uint32_t* wtot, u
   x += dpp_shift<0x118, 0xF>(x);   // row_shr:8
   x += dpp_shift<0x142, 0xA>(x);   // row_bcast:15 into rows 1 and 3
   x += dpp_shift<0x143, 0xC>(x);   // row_bcast:31 into rows 2 and 3
+  return x;
+}
+__device__ __forceinline__ uint32_t block_scan_u32(uint32_t v, uint32_t* wtot, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t x = wave_scan_u32(v);
   if (lane == 63) wtot[wave] = x;
   __syncthreads();
   uint32_t before = 0, all = 0;
@@ -1576,6 +1582,65 @@ __device__ __forceinline__ void resolve_multi(const LayerArgs& a, Lds& L, int P,
   }
 }
 
+// Resolution of the P = T*k <= 64 pairs of up to four tokens (lane p =
+// pair p) by every wave for itself, with no barrier: the waves write the
+// same values to the same places of the tables, and the LDS operations of
+// one wave complete in order.  Misses keep pair order.  One bucket per hit
+// expert, the buckets in the order of their first pairs, each bucket's
+// pairs in token order: the tokens that chose an expert gather in
+// L.emask[e] by OR (bits that any number of waves may set), a pair opens
+// its bucket when its token is the lowest there, and a scan of the opened
+// buckets' sizes over the wave places them.  L.emask must be zero on entry.
+__device__ __forceinline__ void resolve_few(const LayerArgs& a, Lds& L, int P, bool writer) {
+  const int lane = threadIdx.x & 63;
+  const int k = a.k;
+  const bool valid = lane < P;
+  const int e = valid ? L.idx[lane] : 0;
+  const int t = valid ? lane / k : 0;
+  const int s = valid ? slot_of_choice(a, L, e) : -1;
+  const bool hit = s >= 0;
+  if (hit) atomicOr(&L.emask[e], 1u << t);
+  const uint64_t hm = __ballot(hit), mm = __ballot(valid && !hit);
+  wave_lds_sync();
+  const uint32_t tm = hit ? (L.emask[e] & 0xFFFFu) : 0u;   // this wave's ORs cover every pair
+  const bool first = hit && __builtin_ctz(tm) == t;
+  const uint32_t size = first ? uint32_t(__popc(tm)) : 0u;
+  const uint32_t x = wave_scan_u32(size) - size;   // the bucket's first place
+  const uint64_t fm = __ballot(first);
+  const int n_act = __popcll(fm), n_hit = __popcll(hm);
+  if (first) {
+    const int bi = lanes_below(fm);
+    L.act_slot[bi] = s;
+    L.act_start[bi] = int(x);
+    L.emask[e] = tm | (x << 16);
+  }
+  if (lane == 0) {
+    L.act_start[n_act] = n_hit;
+    L.n_act = n_act;
+  }
+  if (lane < P / k) L.hmask[lane] = (hm >> (lane * k)) & ((1ull << k) - 1ull);
+  wave_lds_sync();
+  if (hit) {
+    const int pos = int(L.emask[e] >> 16) + __popc(tm & ((1u << t) - 1u));
+    L.bpair[pos] = lane;
+    L.tok[pos] = t;
+  }
+  if (writer) {
+    const int mpos = lanes_below(mm);
+    if (valid && a.slot_idx) *gmem_w(a.slot_idx + lane) = s;
+    if (valid && !hit) {
+      moe_miss m;
+      m.expert = e;
+      m.token = t;
+      m.gate = L.gate[lane];
+      store_miss(a.miss + mpos, m);
+    }
+    if (valid && lane % k == 0) *gmem_w(a.miss_off + t) = mpos;
+    if (lane == 0) *gmem_w(a.miss_off + a.T) = __popcll(mm);
+  }
+  wave_lds_sync();
+}
+
 // --------------------------------------------------------------- kernel
 // TB: the largest token count the instance serves (1, 4 or 16), so per-token
 // loops are unrolled no further than needed.
@@ -1645,6 +1710,12 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   const int lane_gu = lane % kLprGU;
   RouterRegs<FMT> rr;
   RowRegs<FMT, nch_gu<FMT>()> rg, ru;
+  // Verify batches: the second gate/up task's rows, issued during routing
+  // (an empty type elsewhere, so that other instances carry none of it).
+  struct NoRegs {};
+  using EarlyRegs = std::conditional_t<TB == 4, RowRegs<FMT, nch_gu<FMT>()>, NoRegs>;
+  EarlyRegs eg, eu;
+  bool gu_early = false;   // the first gate/up tasks were issued during routing
   if (task0 < n_router)
     router_load<FMT>(rr, ka, task0, task0 % n_rg, n_router, lane);
   else if (task0 < n_a)
@@ -1763,6 +1834,21 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   if (TB == 4 && E <= 512 && k <= kTopkListMax) {
     route_few(a, lg, T, E, k, L, b == 0, trc);
     stamp_now(trc, kTrRtGate);
+    resolve_few(a, L, P, b == 0 && wave == 0);
+    stamp_now(trc, kTrRtResolved);
+    // This wave's first two gate/up tasks load now, ahead of the work split
+    // and its barrier: the wave's own tables are complete.
+    const int tpe1 = a.I / kRowsGU, nt1 = L.n_act * tpe1, c1 = b + wave * G;
+    if (c1 < nt1)
+      gateup_load<FMT, kRoutedNT>(rg, ru, a, a.g, a.u, L.act_slot[c1 / tpe1],
+                                  (c1 % tpe1) * kRowsGU + lane / kLprGU, lane_gu);
+    const int c2 = c1 + kWaves * G;
+    if constexpr (TB == 4) {
+      if (c2 < nt1)
+        gateup_load<FMT, kRoutedNT>(eg, eu, a, a.g, a.u, L.act_slot[c2 / tpe1],
+                                    (c2 % tpe1) * kRowsGU + lane / kLprGU, lane_gu);
+    }
+    gu_early = true;
   } else {
   const bool thresh = k <= kTopkListMax;
   if (thresh) topk_threshold<TB>(lg, T, E, k, L, trc);
@@ -1799,10 +1885,10 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   }
   __syncthreads();
   stamp_now(trc, kTrRtGate);
-  }
   resolve_multi(a, L, P, b == 0);   // T >= 2 here
   __syncthreads();
   stamp_now(trc, kTrRtResolved);
+  }
   }
   stamp_now(trc, kTrRouted);
   if (trc) stamp(trc, kTrTasksAAll, L.t_a);
@@ -1960,9 +2046,16 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     };
     int task = c_first;
     RowRegs<FMT, nch_gu<FMT>()> ng, nu;
-    // (one token: the first task's rows were issued during routing)
-    if (TB > 1 && task < c_end) load_task(task, rg, ru);
-    if (kAhead == 2 && task + c_step < c_end) load_task(task + c_step, ng, nu);
+    // (one token, and up to four with the wave-local resolution: the first
+    // tasks' rows were issued during routing)
+    if constexpr (TB == 4) {
+      if (gu_early) {
+        ng = eg;
+        nu = eu;
+      }
+    }
+    if (TB > 1 && !gu_early && task < c_end) load_task(task, rg, ru);
+    if (kAhead == 2 && !gu_early && task + c_step < c_end) load_task(task + c_step, ng, nu);
     // one token: the first down unit's lines head for the L2 meanwhile
     if constexpr (TB == 1) pf = prefetch_down(d_first < d_end ? d_first : -1);
     auto compute_task = [&](int t, const RowRegs<FMT, nch_gu<FMT>()>& g,
