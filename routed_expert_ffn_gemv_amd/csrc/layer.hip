@@ -670,15 +670,16 @@ __device__ __forceinline__ void unpack_block(u32x4 w, int bb, uint32_t (&pr)[16]
                                          : and_or(w[q] >> (4 * e), 0x000F000Fu, kMagic128x2);
 }
 // sum over one block of the code pairs . the vector's pairs (4 chains)
-__device__ __forceinline__ float block_dot(const uint32_t (&pr)[16], const u32x4* x4) {
-  float a[4] = {0.f, 0.f, 0.f, 0.f};
+// c + the block's 16 pairs . x, as one chain of dot2 instructions (a
+// dependent dot2 issues right behind the one it waits for).
+__device__ __forceinline__ float block_dot(const uint32_t (&pr)[16], const u32x4* x4, float c) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const u32x4 xx = x4[q];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) a[e] = dot2_bf16(pr[q * 4 + e], xx[e], a[e]);
+    for (int e = 0; e < 4; ++e) c = dot2_bf16(pr[q * 4 + e], xx[e], c);
   }
-  return (a[0] + a[1]) + (a[2] + a[3]);
+  return c;
 }
 
 // Gate and up rows . the vectors xv[v] (block sums sv[v]; -128 times the
@@ -729,11 +730,11 @@ __device__ __forceinline__ void row_pair_vecs_dot(const RowRegs<FMT, NCH>& RG,
           const float sx = sv[v][kBlk * c + bb];
           if constexpr (FMT == MOE_W_Q2B32) {
             const float sx2 = sv2[v][kBlk * c + bb];   // -128 sum x'
-            g[v] = fmaf(dg, block_dot(pg, x4), fmaf(dg, sx2, fmaf(mg, sx, g[v])));
-            u[v] = fmaf(du, block_dot(pu, x4), fmaf(du, sx2, fmaf(mu, sx, u[v])));
+            g[v] = fmaf(dg, block_dot(pg, x4, sx2), fmaf(mg, sx, g[v]));
+            u[v] = fmaf(du, block_dot(pu, x4, sx2), fmaf(mu, sx, u[v]));
           } else {
-            g[v] += dg * block_dot(pg, x4) + mg * sx;
-            u[v] += du * block_dot(pu, x4) + mu * sx;
+            g[v] += dg * block_dot(pg, x4, 0.f) + mg * sx;
+            u[v] += du * block_dot(pu, x4, 0.f) + mu * sx;
           }
         }
         __builtin_amdgcn_sched_barrier(0);   // one block's pairs live at a time
@@ -761,15 +762,14 @@ __device__ __forceinline__ void unpack_block_f16(u32x4 w, int bb, uint32_t (&pr)
                                          : f16_pair_cls<FMT>(w[q], e);
 }
 __device__ __forceinline__ float block_dot_f16(const uint32_t (&pr)[16], const u32x4* x4) {
-  float a[4] = {0.f, 0.f, 0.f, 0.f};
+  float c = 0.f;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const u32x4 xx = x4[q];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      a[e] = dot2_f16(pr[q * 4 + e], xx[e], a[e]);
+    for (int e = 0; e < 4; ++e) c = dot2_f16(pr[q * 4 + e], xx[e], c);
   }
-  return (a[0] + a[1]) + (a[2] + a[3]);
+  return c;
 }
 
 // One row . h of tokens v0 .. v0 + nv - 1, staged by stage_h (token t's
