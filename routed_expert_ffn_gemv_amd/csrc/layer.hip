@@ -1150,14 +1150,14 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u));
 }
 
-// Exclusive scan of one value per thread over the workgroup: a DPP scan in
-// each wave (row shifts, then the row broadcasts), wave totals through LDS.
-// *total receives the sum.  Called by every thread; one barrier.
+// v of the lane CTRL names (a DPP row shift or broadcast), 0 where none or
+// outside the rows ROWS.
 template <int CTRL, int ROWS>
 __device__ __forceinline__ uint32_t dpp_shift(uint32_t v) {
   return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, ROWS, 0xF, true));
 }
-// Inclusive sum over the lanes of the wave up to this one.
+// Inclusive sum over the lanes of the wave up to this one: row shifts, then
+// the row broadcasts.
 __device__ __forceinline__ uint32_t wave_scan_u32(uint32_t v) {
   uint32_t x = v;
   x += dpp_shift<0x111, 0xF>(x);   // row_shr:1
@@ -1167,21 +1167,6 @@ __device__ __forceinline__ uint32_t wave_scan_u32(uint32_t v) {
   x += dpp_shift<0x142, 0xA>(x);   // row_bcast:15 into rows 1 and 3
   x += dpp_shift<0x143, 0xC>(x);   // row_bcast:31 into rows 2 and 3
   return x;
-}
-__device__ __forceinline__ uint32_t block_scan_u32(uint32_t v, uint32_t* wtot, uint32_t* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t x = wave_scan_u32(v);
-  if (lane == 63) wtot[wave] = x;
-  __syncthreads();
-  uint32_t before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const uint32_t c = wtot[w];
-    before += w < wave ? c : 0u;
-    all += c;
-  }
-  *total = all;
-  return before + x - v;
 }
 
 // Resolution of one token's k choices by the wave that chose them (lane j
@@ -1510,78 +1495,6 @@ __device__ __forceinline__ void route_few(const LayerArgs& a, const float* lg, i
   __syncthreads();
 }
 
-// Resolution of the P = T*k pairs of T >= 2 tokens (thread p = pair p).
-// Misses keep pair order (a ballot scan).  Hits are bucketed by expert, the
-// buckets in ascending expert order, each bucket's pairs in token order (a
-// token chooses an expert at most once): every expert gathers the mask of
-// the tokens that chose it, and one scan over the experts of (bucket
-// exists, bucket size) places the buckets and their pairs.  L.emask must be
-// zero on entry; three barriers.
-__device__ __forceinline__ void resolve_multi(const LayerArgs& a, Lds& L, int P, bool writer) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int k = a.k, E = a.E;
-  const bool valid = tid < P;
-  const int e = valid ? L.idx[tid] : 0;
-  const int t = valid ? tid / k : 0;
-  const int s = valid ? slot_of_choice(a, L, e) : -1;
-  const bool hit = s >= 0;
-  if (hit) {
-    atomicOr(&L.emask[e], 1u << t);
-    atomicOr(reinterpret_cast<unsigned long long*>(&L.hmask[t]), 1ull << (tid - t * k));
-  }
-  const uint64_t mm = __ballot(valid && !hit);
-  if (lane == 0) L.tmp[wave] = uint32_t(__popcll(mm));
-  __syncthreads();
-  int mpos = lanes_below(mm), n_miss = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const int c = int(L.tmp[w]);
-    mpos += w < wave ? c : 0;
-    n_miss += c;
-  }
-  if (writer) {
-    if (valid && a.slot_idx) *gmem_w(a.slot_idx + tid) = s;
-    if (valid && !hit) {
-      moe_miss m;
-      m.expert = e;
-      m.token = t;
-      m.gate = L.gate[tid];
-      store_miss(a.miss + mpos, m);
-    }
-    if (valid && tid % k == 0) *gmem_w(a.miss_off + t) = mpos;
-    if (tid == 0) *gmem_w(a.miss_off + a.T) = n_miss;
-  }
-  // experts 2*tid and 2*tid + 1 (E <= 2 * kThreads)
-  const int e0 = 2 * tid;
-  const uint32_t m0 = e0 < E ? L.emask[e0] : 0u, m1 = e0 + 1 < E ? L.emask[e0 + 1] : 0u;
-  const uint32_t v0 = m0 ? (1u << 16) | uint32_t(__popc(m0)) : 0u;
-  const uint32_t v1 = m1 ? (1u << 16) | uint32_t(__popc(m1)) : 0u;
-  uint32_t total;
-  const uint32_t x0 = block_scan_u32(v0 + v1, L.tmp + 8, &total);
-  const uint32_t x1 = x0 + v0;
-  if (m0) {
-    L.act_slot[x0 >> 16] = slot_of_choice(a, L, e0);
-    L.act_start[x0 >> 16] = int(x0 & 0xFFFFu);
-    L.emask[e0] = m0 | (x0 << 16);
-  }
-  if (m1) {
-    L.act_slot[x1 >> 16] = slot_of_choice(a, L, e0 + 1);
-    L.act_start[x1 >> 16] = int(x1 & 0xFFFFu);
-    L.emask[e0 + 1] = m1 | (x1 << 16);
-  }
-  if (tid == 0) {
-    L.act_start[total >> 16] = int(total & 0xFFFFu);
-    L.n_act = int(total >> 16);
-  }
-  __syncthreads();
-  if (hit) {
-    const uint32_t w = L.emask[e];
-    const int pos = int(w >> 16) + __popc(w & ((1u << t) - 1u));
-    L.bpair[pos] = tid;
-    L.tok[pos] = t;
-  }
-}
-
 // Resolution of the P = T*k <= 64 pairs of up to four tokens (lane p =
 // pair p) by every wave for itself, with no barrier: the waves write the
 // same values to the same places of the tables, and the LDS operations of
@@ -1637,6 +1550,87 @@ __device__ __forceinline__ void resolve_few(const LayerArgs& a, Lds& L, int P, b
     }
     if (valid && lane % k == 0) *gmem_w(a.miss_off + t) = mpos;
     if (lane == 0) *gmem_w(a.miss_off + a.T) = __popcll(mm);
+  }
+  wave_lds_sync();
+}
+
+// The same for up to kPMax pairs: lane l holds pairs 4l .. 4l + 3, so that
+// pair order is lane order and then i.  Per lane counts of opened buckets,
+// misses and bucket sizes are scanned over the wave in one packed word.
+// L.emask and L.hmask must be zero on entry.
+__device__ __forceinline__ void resolve_wave(const LayerArgs& a, Lds& L, int P, bool writer) {
+  constexpr int kPL = kPMax / 64;   // pairs per lane
+  const int lane = threadIdx.x & 63;
+  const int k = a.k;
+  int e[kPL], t[kPL], s[kPL];
+#pragma unroll
+  for (int i = 0; i < kPL; ++i) {
+    const int p = kPL * lane + i;
+    const bool valid = p < P;
+    e[i] = valid ? L.idx[p] : 0;
+    t[i] = valid ? p / k : 0;
+    s[i] = valid ? slot_of_choice(a, L, e[i]) : -2;   // -2: no pair, -1: a miss
+    if (s[i] >= 0) {
+      atomicOr(&L.emask[e[i]], 1u << t[i]);
+      atomicOr(reinterpret_cast<unsigned long long*>(&L.hmask[t[i]]), 1ull << (p - t[i] * k));
+    }
+  }
+  wave_lds_sync();
+  uint32_t tm[kPL], cnt = 0u;   // opened buckets | misses << 10 | hits in opened buckets << 20
+#pragma unroll
+  for (int i = 0; i < kPL; ++i) {
+    tm[i] = s[i] >= 0 ? (L.emask[e[i]] & 0xFFFFu) : 0u;   // this wave's ORs cover every pair
+    const bool first = s[i] >= 0 && __builtin_ctz(tm[i]) == t[i];
+    cnt += first ? 1u + (uint32_t(__popc(tm[i])) << 20) : 0u;
+    cnt += s[i] == -1 ? 1u << 10 : 0u;
+  }
+  const uint32_t incl = wave_scan_u32(cnt);
+  const uint32_t all = uint32_t(__builtin_amdgcn_readlane(int(incl), 63));
+  uint32_t before = incl - cnt;
+  const int n_act = int(all & 0x3FFu), n_miss = int((all >> 10) & 0x3FFu);
+  const int n_hit = int(all >> 20);
+#pragma unroll
+  for (int i = 0; i < kPL; ++i) {
+    if (s[i] >= 0 && __builtin_ctz(tm[i]) == t[i]) {
+      const int bi = int(before & 0x3FFu);
+      const uint32_t x = before >> 20;
+      L.act_slot[bi] = s[i];
+      L.act_start[bi] = int(x);
+      L.emask[e[i]] = tm[i] | (x << 16);
+      before += 1u + (uint32_t(__popc(tm[i])) << 20);
+    }
+  }
+  if (lane == 0) {
+    L.act_start[n_act] = n_hit;
+    L.n_act = n_act;
+  }
+  wave_lds_sync();
+#pragma unroll
+  for (int i = 0; i < kPL; ++i) {
+    if (s[i] >= 0) {
+      const int pos = int(L.emask[e[i]] >> 16) + __popc(tm[i] & ((1u << t[i]) - 1u));
+      L.bpair[pos] = kPL * lane + i;
+      L.tok[pos] = t[i];
+    }
+  }
+  if (writer) {
+    int mpos = int((before >> 10) & 0x3FFu);   // misses before this lane's pairs
+#pragma unroll
+    for (int i = 0; i < kPL; ++i) {
+      const int p = kPL * lane + i;
+      if (s[i] == -2) continue;
+      if (a.slot_idx) *gmem_w(a.slot_idx + p) = s[i];
+      if (p % k == 0) *gmem_w(a.miss_off + t[i]) = mpos;
+      if (s[i] == -1) {
+        moe_miss m;
+        m.expert = e[i];
+        m.token = t[i];
+        m.gate = L.gate[p];
+        store_miss(a.miss + mpos, m);
+        ++mpos;
+      }
+    }
+    if (lane == 0) *gmem_w(a.miss_off + a.T) = n_miss;
   }
   wave_lds_sync();
 }
@@ -1710,12 +1704,11 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   const int lane_gu = lane % kLprGU;
   RouterRegs<FMT> rr;
   RowRegs<FMT, nch_gu<FMT>()> rg, ru;
-  // Verify batches: the second gate/up task's rows, issued during routing
-  // (an empty type elsewhere, so that other instances carry none of it).
+  // Several tokens: the second gate/up task's rows, issued during routing
+  // (an empty type for one token, so that its instance carries none of it).
   struct NoRegs {};
-  using EarlyRegs = std::conditional_t<TB == 4, RowRegs<FMT, nch_gu<FMT>()>, NoRegs>;
+  using EarlyRegs = std::conditional_t<(TB > 1), RowRegs<FMT, nch_gu<FMT>()>, NoRegs>;
   EarlyRegs eg, eu;
-  bool gu_early = false;   // the first gate/up tasks were issued during routing
   if (task0 < n_router)
     router_load<FMT>(rr, ka, task0, task0 % n_rg, n_router, lane);
   else if (task0 < n_a)
@@ -1835,20 +1828,6 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     route_few(a, lg, T, E, k, L, b == 0, trc);
     stamp_now(trc, kTrRtGate);
     resolve_few(a, L, P, b == 0 && wave == 0);
-    stamp_now(trc, kTrRtResolved);
-    // This wave's first two gate/up tasks load now, ahead of the work split
-    // and its barrier: the wave's own tables are complete.
-    const int tpe1 = a.I / kRowsGU, nt1 = L.n_act * tpe1, c1 = b + wave * G;
-    if (c1 < nt1)
-      gateup_load<FMT, kRoutedNT>(rg, ru, a, a.g, a.u, L.act_slot[c1 / tpe1],
-                                  (c1 % tpe1) * kRowsGU + lane / kLprGU, lane_gu);
-    const int c2 = c1 + kWaves * G;
-    if constexpr (TB == 4) {
-      if (c2 < nt1)
-        gateup_load<FMT, kRoutedNT>(eg, eu, a, a.g, a.u, L.act_slot[c2 / tpe1],
-                                    (c2 % tpe1) * kRowsGU + lane / kLprGU, lane_gu);
-    }
-    gu_early = true;
   } else {
   const bool thresh = k <= kTopkListMax;
   if (thresh) topk_threshold<TB>(lg, T, E, k, L, trc);
@@ -1885,10 +1864,19 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   }
   __syncthreads();
   stamp_now(trc, kTrRtGate);
-  resolve_multi(a, L, P, b == 0);   // T >= 2 here
-  __syncthreads();
-  stamp_now(trc, kTrRtResolved);
+  resolve_wave(a, L, P, b == 0 && wave == 0);
   }
+  stamp_now(trc, kTrRtResolved);
+  // This wave's first two gate/up tasks load now, ahead of the work split
+  // and its barrier: the wave's own tables are complete.
+  const int tpe1 = a.I / kRowsGU, nt1 = L.n_act * tpe1, c1 = b + wave * G;
+  if (c1 < nt1)
+    gateup_load<FMT, kRoutedNT>(rg, ru, a, a.g, a.u, L.act_slot[c1 / tpe1],
+                                (c1 % tpe1) * kRowsGU + lane / kLprGU, lane_gu);
+  const int c2 = c1 + kWaves * G;
+  if (c2 < nt1)
+    gateup_load<FMT, kRoutedNT>(eg, eu, a, a.g, a.u, L.act_slot[c2 / tpe1],
+                                (c2 % tpe1) * kRowsGU + lane / kLprGU, lane_gu);
   }
   stamp_now(trc, kTrRouted);
   if (trc) stamp(trc, kTrTasksAAll, L.t_a);
@@ -2045,17 +2033,13 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
                                   (t % tpe) * kRowsGU + lane / kLprGU, lane_gu);
     };
     int task = c_first;
+    // (the first task's rows, and with several tokens the second's, were
+    // issued during routing)
     RowRegs<FMT, nch_gu<FMT>()> ng, nu;
-    // (one token, and up to four with the wave-local resolution: the first
-    // tasks' rows were issued during routing)
-    if constexpr (TB == 4) {
-      if (gu_early) {
-        ng = eg;
-        nu = eu;
-      }
+    if constexpr (TB > 1) {
+      ng = eg;
+      nu = eu;
     }
-    if (TB > 1 && !gu_early && task < c_end) load_task(task, rg, ru);
-    if (kAhead == 2 && !gu_early && task + c_step < c_end) load_task(task + c_step, ng, nu);
     // one token: the first down unit's lines head for the L2 meanwhile
     if constexpr (TB == 1) pf = prefetch_down(d_first < d_end ? d_first : -1);
     auto compute_task = [&](int t, const RowRegs<FMT, nch_gu<FMT>()>& g,

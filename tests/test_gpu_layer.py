@@ -55,6 +55,10 @@ FUSED = {
     "q2_T1_E1024": small_cfg(E=1024, k=16, H=1024, I=256, T=1, bias="zipf", seed=88),
     "q4_T1_E300_k20": small_cfg(E=300, k=20, H=1024, I=256, T=1, wfmt="q4", seed=89),
     "q2_T3": small_cfg(E=64, k=8, H=1024, I=256, T=3, bias="zipf", seed=82),
+    # up to four tokens outside the fast routing path (E > 512; k > 16, so
+    # that the pairs outnumber a wave's lanes)
+    "q2_T2_E600_k12": small_cfg(E=600, k=12, H=1024, I=256, T=2, bias="zipf", seed=90),
+    "q4_T4_E300_k20": small_cfg(E=300, k=20, H=1024, I=256, T=4, wfmt="q4", seed=91),
     "q2_T9": small_cfg(E=96, k=6, H=1024, I=256, T=9, bias="zipf", seed=83),
     "q4_T16": small_cfg(E=64, k=10, H=1024, I=256, T=16, wfmt="q4", bias="zipf", seed=84),
     "q2_T16_no_shared": small_cfg(E=48, k=10, H=1024, I=256, T=16, shared=False, seed=85),
