@@ -112,14 +112,14 @@ KERNEL_SOURCES = {
 TRAFFIC = {
     # workload: {"sha256": ..., "bytes": fetched + written per launch}
     # c2: the moe_layer kernel (profiles/c2_decode_layer_hbm_traffic.md)
-    "c2_decode_layer_q2": {"sha256": "9e9566846c7428ac5672163544ff2743acc6c183cdd8c888f03e7d9f12c267ff",
-                           "bytes": 23079431},
+    "c2_decode_layer_q2": {"sha256": "84c8b7eecc1a9020f215317f1c6ae1c0c5105c2eb264e237489cf695a60003f4",
+                           "bytes": 23063696},
     # c3: the moe_layer kernel (profiles/c3_verify_stack_hbm_traffic.md)
-    "c3_verify_stack_q2": {"sha256": "9e9566846c7428ac5672163544ff2743acc6c183cdd8c888f03e7d9f12c267ff",
-                           "bytes": 70151618},
+    "c3_verify_stack_q2": {"sha256": "84c8b7eecc1a9020f215317f1c6ae1c0c5105c2eb264e237489cf695a60003f4",
+                           "bytes": 70038205},
     # c4: the moe_layer kernel (profiles/c4_slot_tiering_hbm_traffic.md)
-    "c4_slot_tiering_q2": {"sha256": "9e9566846c7428ac5672163544ff2743acc6c183cdd8c888f03e7d9f12c267ff",
-                           "bytes": 121597985},
+    "c4_slot_tiering_q2": {"sha256": "84c8b7eecc1a9020f215317f1c6ae1c0c5105c2eb264e237489cf695a60003f4",
+                           "bytes": 121582544},
     # c5: the kernels of one moe_expert_ffn call (active list, schedule, x16,
     # gate/up and down GEMMs; profiles/c5_prefill_hbm_traffic.md)
     "c5_prefill_q4": {"sha256": "60e44c72388bf65f02e182f4083d57b020dc015a61f0d171f19085e8a1ed5810",
@@ -321,6 +321,8 @@ def bench_decode(args, cfg_name, steps=None, warmup=None, cpu_calls=None):
 PHASES = [(0, "start"), (2, "tokens staged"), (3, "router/shared tasks (wave 0)"),
           (21, "router/shared tasks (last wave)"), (4, "every logit seen (wave 0)"),
           (11, "every logit seen (all waves)"),
+          (22, "  top-k: segment maxima"), (23, "  top-k: thresholds"),
+          (28, "  top-k: candidates listed"),
           (16, "  routing: candidates listed"), (17, "  routing: second barrier"),
           (18, "  routing: ranks"), (19, "  routing: gates"), (20, "  routing: resolved"),
           (5, "routing done"), (6, "gate/up done (wave 0)"), (7, "gate/up done (last wave)"),
