@@ -646,36 +646,34 @@ def bench_prefill(args, cfg_name, steps=None, warmup=None):
     torch.cuda.synchronize()
     log(f"[bench] setup {time.time() - t0:.1f}s")
     stream = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
     x = inp["x"]
     steps = args.steps if steps is None else steps
     warmup = args.warmup if warmup is None else warmup
 
-    def step(mode, times=None):
+    def step(mode, ev=None):
         """One prefill step.  pairs: moe_expert_ffn writes every pair's output
         and moe_combine sums them; accum: y is zeroed and
-        moe_expert_ffn_accum adds the gate-weighted outputs into it."""
-        if times is not None:
+        moe_expert_ffn_accum adds the gate-weighted outputs into it.  ev: five
+        events recorded on the stream around the four calls (no host wait)."""
+        if ev is not None:
             ev[0].record(stream)
         moe.moe_route(desc, x, T, idx, gate, ws, stream)
-        if times is not None:
+        if ev is not None:
             ev[1].record(stream)
         moe.moe_resolve_slots(desc, idx, gate, T, slot_idx, boff, bpair, miss, moff, ws, stream)
-        if times is not None:
+        if ev is not None:
             ev[2].record(stream)
         if mode == "pairs":
             moe.moe_expert_ffn(desc, x, T, boff, bpair, pair_out, shared_out, ws, stream)
         else:
             y.zero_()
             moe.moe_expert_ffn_accum(desc, x, T, boff, bpair, gate, y, ws, stream)
-        if times is not None:
+        if ev is not None:
             ev[3].record(stream)
         if mode == "pairs":
             moe.moe_combine(desc, T, slot_idx, gate, pair_out, shared_out, y, stream)
-        if times is not None:
+        if ev is not None:
             ev[4].record(stream)
-            torch.cuda.synchronize()
-            times.append([ev[i].elapsed_time(ev[i + 1]) for i in range(4)])
 
     modes = ["pairs", "accum"] if args.prefill_mode == "both" else [args.prefill_mode]
     res = {}
@@ -683,17 +681,18 @@ def bench_prefill(args, cfg_name, steps=None, warmup=None):
         for _ in range(warmup):
             step(mode)
         torch.cuda.synchronize()
+        # the parts of every timed step, from events recorded on the stream
+        # inside the timed region (averages over its steps)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         hold_queue(steps * 8)
         e0.record(stream)
-        for _ in range(steps):
-            step(mode)
+        for i in range(steps):
+            step(mode, evs[i])
         e1.record(stream)
         torch.cuda.synchronize()
-        parts = []
-        for _ in range(3):
-            step(mode, parts)
-        res[mode] = (e0.elapsed_time(e1) / steps, np.median(np.array(parts), axis=0))
+        parts = np.array([[ev[j].elapsed_time(ev[j + 1]) for j in range(4)] for ev in evs])
+        res[mode] = (e0.elapsed_time(e1) / steps, parts.mean(axis=0))
         log(f"[bench] prefill ({mode}): {res[mode][0]:.4f} ms per step, parts {res[mode][1]}")
     best = min(res, key=lambda m: res[m][0])
     ms, parts = res[best]
