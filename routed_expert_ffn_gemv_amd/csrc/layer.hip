@@ -1892,7 +1892,12 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   const int nch_d = chunks_of<FMT>(Kd) / kLprD;
   const int64_t row_bytes_d = int64_t(Kd) * fmt_bits(FMT) / 8;
   const int nrb = (a.H + kRowsD - 1) / kRowsD;
-  const int n_units = (n_act + (a.has_sh ? 1 : 0)) * nrb;
+  // The shared expert's down work is split into token groups of at most
+  // kShG tokens, each a bucket of its own: one unit of all 16 tokens of a
+  // batch would cost more than a workgroup's whole share of the phase.
+  constexpr int kShG = 4;
+  const int n_shg = a.has_sh ? (TB > kShG ? (T + kShG - 1) / kShG : 1) : 0;
+  const int n_units = (n_act + n_shg) * nrb;
   const int tpe = a.I / kRowsGU;
   const int n_tasks = n_act * tpe;
   const int lane_gd = lane % kLprD;
@@ -1910,7 +1915,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   int d_first = b, d_end = n_units, d_step = G;
   if constexpr (TB > 1) {
     constexpr int kCostD = 1;
-    const int n_db = n_act + (a.has_sh ? 1 : 0);
+    const int n_db = n_act + n_shg;
     // (costs stay below 2^20; a bound's exact quotient a * tot / W comes from
     // double arithmetic: the product is exact and no quotient lies within a
     // rounding error of an integer it does not equal)
@@ -1925,8 +1930,8 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
       const int n = n_db;
       const int rows = nrb, fixed = kCostD;
       const int bt = bound(b + tid, totD, G);
-      auto tokens_before = [&](int u) {   // tokens of buckets < u (the shared one last)
-        return u <= n_act ? L.act_start[u] : L.act_start[n_act] + T;
+      auto tokens_before = [&](int u) {   // tokens of buckets < u (the shared groups last)
+        return u <= n_act ? L.act_start[u] : L.act_start[n_act] + min(T, (u - n_act) * kShG);
       };
       auto cum = [&](int u) { return rows * (fixed * u + tokens_before(u)); };
       int lo = 0, hi = n;   // the largest u <= n with cum(u) <= bt
@@ -1939,7 +1944,8 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
       if (lo == n) {
         v = n_units;
       } else {
-        const int cost = fixed + (lo < n_act ? L.act_start[lo + 1] - L.act_start[lo] : T);
+        const int cost =
+            fixed + (lo < n_act ? L.act_start[lo + 1] - L.act_start[lo] : min(kShG, T - (lo - n_act) * kShG));
         v = lo * rows + (bt - cum(lo) + cost - 1) / cost;
       }
       L.dstart[tid] = v;
@@ -1954,7 +1960,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
       const int u = tid - 64;
       if (u >= 0 && u < n_db) {
         auto cum_d = [&](int v) {
-          return nrb * (kCostD * v + (v <= n_act ? L.act_start[v] : L.act_start[n_act] + T));
+          return nrb * (kCostD * v + (v <= n_act ? L.act_start[v] : L.act_start[n_act] + min(T, (v - n_act) * kShG)));
         };
         const int s0 = int(int64_t(G) * cum_d(u) / totD);
         const int s1 = int(int64_t(G) * cum_d(u + 1) / totD);
@@ -2100,14 +2106,15 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
       if (unit + d_step < d_end) load_down(unit + d_step, nd);
       const int u = unit / nrb, rb = unit % nrb;
       const bool shared = u >= n_act;
-      const int st = shared ? 0 : L.act_start[u];
-      const int n = shared ? T : L.act_start[u + 1] - st;
+      // (a shared group's first token, else the bucket's first position)
+      const int st = shared ? (TB > kShG ? (u - n_act) * kShG : 0) : L.act_start[u];
+      const int n = shared ? (TB > kShG ? min(kShG, T - st) : T) : L.act_start[u + 1] - st;
       const int r = rb * kRowsD + wave * (64 / kLprD) + lane / kLprD;
       if (u != staged) {
         __syncthreads();   // gate/up tasks and the previous unit are done with the LDS
         if (staged < 0) stamp_now(trc, kTrDBar1);
         if (tid < n)
-          srcs[tid] = shared ? region_h_sh(a) + int64_t(tid) * Kd
+          srcs[tid] = shared ? region_h_sh(a) + int64_t(st + tid) * Kd
                              : region_h(a) + int64_t(L.bpair[st + tid]) * Kd;
         __syncthreads();
         if (staged < 0) stamp_now(trc, kTrDBar2);
@@ -2138,7 +2145,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
           if (v >= nv) continue;
           const float os = group_sum<kLprD>(o[v]);
           if (r < a.H && lane_gd == 0) {
-            const int t = shared ? v0 + v : L.tok[st + v0 + v];
+            const int t = shared ? st + v0 + v : L.tok[st + v0 + v];
             const int pr = shared ? 0 : L.bpair[st + v0 + v];
             const float g = shared ? 1.f : L.gate[pr];
             if constexpr (DET) {
