@@ -809,7 +809,7 @@ def main():
                          "known-size kernel that scales the HBM byte counters of a profile")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
     if args.copy_probe:
         copy_probe(args.copy_probe)
