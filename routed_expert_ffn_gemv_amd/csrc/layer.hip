@@ -290,7 +290,8 @@ struct Lds {
   alignas(16) uint32_t tmp[32];
   int dstart[2];            // this workgroup's down unit range (contiguous split)
   int dalign[2];            // the same, bucket-aligned split
-  int dzero;                // 1: some bucket got no workgroup in the aligned split
+  int dzero;                // 1: no bound fits the aligned split (more buckets than workgroups)
+  int dhist[kTMax + 1];     // down buckets by tokens
   int n_act;
   uint32_t calls;
   int failed;               // 1: this workgroup gave up a wait; 2: the workspace was poisoned
@@ -1730,8 +1731,11 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
     L.ncand[tid] = 0;
     L.hmask[tid] = 0ull;
   }
+  if (tid <= kTMax) L.dhist[tid] = 0;
   if (tid == 0) {
     L.dzero = 0;
+    L.dalign[0] = 0;
+    L.dalign[1] = 0;
     L.t_gu = 0ull;
     L.t_a = 0ull;
   }
@@ -1916,6 +1920,10 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
   if constexpr (TB > 1) {
     constexpr int kCostD = 1;
     const int n_db = n_act + n_shg;
+    auto tokens_of = [&](int u) {   // tokens of down bucket u (the shared groups last)
+      return u < n_act ? L.act_start[u + 1] - L.act_start[u]
+                       : (TB > kShG ? min(kShG, T - (u - n_act) * kShG) : T);
+    };
     // (costs stay below 2^20; a bound's exact quotient a * tot / W comes from
     // double arithmetic: the product is exact and no quotient lies within a
     // rounding error of an integer it does not equal)
@@ -1950,26 +1958,73 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(LayerArgs ka) {
       }
       L.dstart[tid] = v;
     }
-    // Down units, bucket-aligned: bucket u gets the workgroups [s(u), s(u+1)),
-    // s(u) = floor(G * cum(u) / totD) with cum the cumulative cost, and its
-    // units spread evenly over them -- so a workgroup stages the activations
-    // of one bucket only (a second staging costs a poll round trip and a
-    // conversion, more than a unit).  When some bucket would get no
-    // workgroup, every workgroup keeps the contiguous split above.
-    {
-      const int u = tid - 64;
-      if (u >= 0 && u < n_db) {
-        auto cum_d = [&](int v) {
-          return nrb * (kCostD * v + (v <= n_act ? L.act_start[v] : L.act_start[n_act] + min(T, (v - n_act) * kShG)));
-        };
-        const int s0 = int(int64_t(G) * cum_d(u) / totD);
-        const int s1 = int(int64_t(G) * cum_d(u + 1) / totD);
-        if (s1 == s0) {
-          L.dzero = 1;
-        } else if (b >= s0 && b < s1) {
-          const int w = s1 - s0, j = b - s0;
-          L.dalign[0] = u * nrb + j * nrb / w;
-          L.dalign[1] = u * nrb + (j + 1) * nrb / w;
+    // Down units, bucket-aligned, by a min-max split: the smallest cost
+    // bound C such that every bucket's units fit on its own run of
+    // workgroups, each with at most C of cost, where bucket u (cost c per
+    // unit) takes w(u) = ceil(nrb / min(nrb, floor(C / c))) workgroups and
+    // its units spread evenly over them -- so a workgroup stages the
+    // activations of one bucket only (a second staging costs a poll round
+    // trip and a conversion, more than a unit).  The runs follow the bucket
+    // order; workgroups past the last run take no down unit.  With more
+    // buckets than workgroups no bound fits, and every workgroup keeps the
+    // contiguous split above.  Wave 1 alone: a histogram of the bucket sizes
+    // (one wave's LDS operations complete in order), then each lane tries a
+    // bound, 64 consecutive bounds per round from a lower limit; at C =
+    // nrb * (largest cost) every bucket takes one workgroup, so the search
+    // ends there at the latest.
+    if (wave == 1) {
+      for (int u = lane; u < n_db; u += 64) atomicAdd(&L.dhist[tokens_of(u)], 1);
+      int nmax = TB;
+      while (nmax > 1 && L.dhist[nmax] == 0) --nmax;
+      // floor(p / q) for small positive integers: the exact quotient's
+      // fraction lies at least 0.5 / q away from an integer, far beyond the
+      // reciprocal's rounding error
+      auto fdiv = [](int p, int q) {
+        return int((float(p) + 0.5f) * __builtin_amdgcn_rcpf(float(q)));
+      };
+      // workgroups a bucket of cost c takes under bound C (0 if a unit does
+      // not fit)
+      auto wgs = [&](int C, int c) {
+        const int m = min(nrb, fdiv(C, c));
+        return m == 0 ? 0 : fdiv(nrb - 1, m) + 1;
+      };
+      int cs = -1;
+      if (n_db <= G) {
+        for (int c0 = max(kCostD + nmax, (totD + G - 1) / G);; c0 += 64) {
+          const int C = c0 + lane;
+          int need = 0;
+          for (int n = 1; n <= nmax; ++n) {
+            const int h = L.dhist[n];
+            if (h == 0) continue;
+            const int w = wgs(C, kCostD + n);
+            need += w == 0 ? G + 1 : h * w;
+          }
+          const uint64_t ok = __ballot(need <= G);
+          if (ok != 0ull) {
+            cs = c0 + __builtin_ctzll(ok);
+            break;
+          }
+        }
+      }
+      if (cs < 0) {
+        if (lane == 0) L.dzero = 1;
+      } else {
+        int before = 0;   // workgroups taken by the buckets of earlier groups of 64
+        for (int u0 = 0; u0 < n_db; u0 += 64) {
+          const int u = u0 + lane;
+          const int w = u < n_db ? wgs(cs, kCostD + tokens_of(u)) : 0;
+          int incl = w;   // inclusive prefix sum over the wave
+          for (int d = 1; d < 64; d <<= 1) {
+            const int o = __shfl_up(incl, d);
+            if (lane >= d) incl += o;
+          }
+          const int s0 = before + incl - w;
+          if (b >= s0 && b < s0 + w) {
+            const int j = b - s0;
+            L.dalign[0] = u * nrb + j * nrb / w;
+            L.dalign[1] = u * nrb + (j + 1) * nrb / w;
+          }
+          before += __shfl(incl, 63);
         }
       }
     }
