@@ -183,6 +183,39 @@ def test_tied_logits(name, path):
     assert rowwise_rel_err(host(o["y"]), ref["y"]) <= TOL
 
 
+@pytest.mark.parametrize("shared", [True, False])
+def test_fused_every_choice_its_own_expert(shared):
+    """16 tokens, k = 16, every token on 16 experts of its own: 256 buckets of
+    one token.  With the shared expert's four token groups that is more down
+    buckets than a 256-workgroup grid holds (the contiguous split), without
+    it exactly one workgroup per bucket."""
+    import torch
+    E, k, T, H = 512, 16, 16, 1024
+    cfg = small_cfg(E=E, k=k, H=H, I=256, T=T, shared=shared, seed=47)
+    say(f"[gpu] every choice its own expert: E={E} k={k} T={T} shared={shared}")
+    # token t: a one-hot row at coordinate t; expert e: weight 1 + (e % 16) / 16
+    # (exact in bf16) at coordinate e // 16, so token t's logits are those 16
+    # distinct values on experts 16 t .. 16 t + 15 and zero elsewhere
+    one = synth.bf16_bits(np.array([1.0]))[0]
+    x = np.zeros((T, H), np.uint16)
+    x[np.arange(T), np.arange(T)] = one
+    W = np.zeros((E, H), np.uint16)
+    e = np.arange(E)
+    W[e, e // 16] = synth.bf16_bits(1.0 + (e % 16) / 16.0)
+    L = DeviceLayer(cfg, 0, x=x)
+    L.inp["router_w"].copy_(torch.from_numpy(W.view(np.int16)))
+    o = L.run_layer()
+    logits = oracle.router(x, W, cfg.router_fmt, None)
+    idx, gate = oracle.topk(logits, k)
+    assert len(np.unique(idx)) == T * k
+    slot_idx, me, mt, mg, moff = oracle.resolve(idx, gate, E)
+    route = {"logits": logits, "idx": idx, "gate": gate, "slot_idx": slot_idx,
+             "miss_expert": me, "miss_token": mt, "miss_gate": mg, "miss_off": moff}
+    ref = oracle.layer_from_synth(cfg, 0, x, route=route)
+    check_routing(o, ref, k)
+    assert rowwise_rel_err(host(o["y"]), ref["y"]) <= TOL
+
+
 def test_tiered_small_with_misses():
     """A partial slot table: misses listed bit-exactly; y holds hits only and
     y + sum over misses of gate * FFN equals the all-resident layer."""
