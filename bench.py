@@ -112,14 +112,14 @@ KERNEL_SOURCES = {
 TRAFFIC = {
     # workload: {"sha256": ..., "bytes": fetched + written per launch}
     # c2: the moe_layer kernel (profiles/c2_decode_layer_hbm_traffic.md)
-    "c2_decode_layer_q2": {"sha256": "a4068e93284f0cd422bbe45b511ec2cfe63ff478f262d25cbea61178a7a77a5a",
-                           "bytes": 23057273},
+    "c2_decode_layer_q2": {"sha256": "414b3dd770c9eb0f8add72ac88e3a3adf9ba262d609e90a6f800f95b8d7e2690",
+                           "bytes": 23067323},
     # c3: the moe_layer kernel (profiles/c3_verify_stack_hbm_traffic.md)
-    "c3_verify_stack_q2": {"sha256": "a4068e93284f0cd422bbe45b511ec2cfe63ff478f262d25cbea61178a7a77a5a",
-                           "bytes": 69868134},
+    "c3_verify_stack_q2": {"sha256": "414b3dd770c9eb0f8add72ac88e3a3adf9ba262d609e90a6f800f95b8d7e2690",
+                           "bytes": 69957373},
     # c4: the moe_layer kernel (profiles/c4_slot_tiering_hbm_traffic.md)
-    "c4_slot_tiering_q2": {"sha256": "a4068e93284f0cd422bbe45b511ec2cfe63ff478f262d25cbea61178a7a77a5a",
-                           "bytes": 123094233},
+    "c4_slot_tiering_q2": {"sha256": "414b3dd770c9eb0f8add72ac88e3a3adf9ba262d609e90a6f800f95b8d7e2690",
+                           "bytes": 122847317},
     # c5: the kernels of one moe_expert_ffn call (active list, schedule, x16,
     # gate/up and down GEMMs; profiles/c5_prefill_hbm_traffic.md)
     "c5_prefill_q4": {"sha256": "60e44c72388bf65f02e182f4083d57b020dc015a61f0d171f19085e8a1ed5810",
